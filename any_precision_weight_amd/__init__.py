@@ -1,0 +1,257 @@
+"""Python binding of libapmoe (ctypes), the any-precision MoE expert layer for
+MI355X (gfx950).
+
+Argument marshalling only: every step runs in the HIP kernels of
+``libapmoe.so``.  Tensors are torch device tensors (PyTorch provides device
+memory and streams); they are passed to the C ABI as raw pointers.  There is
+no fallback: if the library is missing, importing the functions raises.
+
+Function names and argument order follow ``include/apmoe.h``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libapmoe.so")
+
+OK, INVALID_ARG, UNSUPPORTED, NOT_RESIDENT, HIP_ERROR, OUT_OF_MEMORY = range(6)
+GATE_UP, DOWN = 0, 1
+F16, F32 = 0, 1
+MIN_BITS, MAX_BITS, PLANES = 3, 8, 8
+
+EXPORTED = [
+    "apmoe_status_string", "apmoe_last_error", "apmoe_version", "apmoe_create", "apmoe_destroy",
+    "apmoe_block_bytes", "apmoe_table_create", "apmoe_table_destroy", "apmoe_table_set_block",
+    "apmoe_table_set_bits", "apmoe_table_set_plane", "apmoe_table_validate", "apmoe_table_committed_bits",
+    "apmoe_table_commit", "apmoe_lut_build", "apmoe_pack_planes", "apmoe_route", "apmoe_gemm", "apmoe_act",
+    "apmoe_combine", "apmoe_moe_workspace", "apmoe_moe_forward",
+]
+
+
+class ApmoeError(RuntimeError):
+    def __init__(self, status: int, fn: str, detail: str):
+        self.status = status
+        super().__init__(f"{fn}: status {status} ({_status_text(status)}): {detail}")
+
+
+class BlockDesc(ctypes.Structure):
+    _fields_ = [
+        ("n", ctypes.c_int32), ("k", ctypes.c_int32), ("q", ctypes.c_int32), ("d", ctypes.c_int32),
+        ("resident_mask", ctypes.c_uint32),
+        ("plane", ctypes.c_void_p * PLANES),
+        ("lut", ctypes.c_void_p * (MAX_BITS + 1)),
+    ]
+
+
+_lib = None
+
+
+def _status_text(s: int) -> str:
+    try:
+        return lib().apmoe_status_string(s).decode()
+    except Exception:  # pragma: no cover - library missing
+        return "?"
+
+
+def lib() -> ctypes.CDLL:
+    """Load libapmoe.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with `python -m any_precision_weight_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        _declare(L)
+        _lib = L
+    return _lib
+
+
+def _declare(L):
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    S = ctypes.c_int32
+    sig = {
+        "apmoe_status_string": (ctypes.c_char_p, [S]),
+        "apmoe_last_error": (ctypes.c_char_p, []),
+        "apmoe_version": (I32, []),
+        "apmoe_create": (S, [ctypes.POINTER(P), ctypes.c_int]),
+        "apmoe_destroy": (S, [P]),
+        "apmoe_block_bytes": (I64, [I32, I32, I32]),
+        "apmoe_table_create": (S, [I32, I32, ctypes.POINTER(P)]),
+        "apmoe_table_destroy": (S, [P]),
+        "apmoe_table_set_block": (S, [P, I32, I32, I32, ctypes.POINTER(BlockDesc)]),
+        "apmoe_table_set_bits": (S, [P, I32, I32, I32, I32]),
+        "apmoe_table_set_plane": (S, [P, I32, I32, I32, I32, P, I32]),
+        "apmoe_table_validate": (S, [P]),
+        "apmoe_table_committed_bits": (S, [P, I32, I32, I32, ctypes.POINTER(I32)]),
+        "apmoe_table_commit": (S, [P, P, P]),
+        "apmoe_lut_build": (S, [P, P, I32, P, P]),
+        "apmoe_pack_planes": (S, [P, P, I32, I32, P, P]),
+        "apmoe_route": (S, [P, P, P, P, I32, I32, I32, I32, I32, P, P, P, P, P, P, P]),
+        "apmoe_gemm": (S, [P, P, I32, I32, P, I32, P, P, I32, I32, P, I32, P]),
+        "apmoe_act": (S, [P, P, I32, I32, P, P]),
+        "apmoe_combine": (S, [P, P, I32, P, P, I32, I32, I32, P, P]),
+        "apmoe_moe_workspace": (S, [P, I32, I32, I32, ctypes.POINTER(SZ)]),
+        "apmoe_moe_forward": (S, [P, P, I32, P, P, P, I32, I32, I32, P, SZ, P, P]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+
+
+def _check(status: int, fn: str) -> None:
+    if status != OK:
+        raise ApmoeError(status, fn, lib().apmoe_last_error().decode())
+
+
+def ptr(t) -> int | None:
+    """Raw pointer of a torch tensor / int / None."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def stream_handle(stream=None) -> int | None:
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream or None
+
+
+# --------------------------------------------------------------------------- API
+
+def version() -> int:
+    return lib().apmoe_version()
+
+
+def block_bytes(n: int, k: int, b: int) -> int:
+    return int(lib().apmoe_block_bytes(n, k, b))
+
+
+class Context:
+    """apmoe_create / apmoe_destroy."""
+
+    def __init__(self, device: int = 0):
+        h = ctypes.c_void_p()
+        _check(lib().apmoe_create(ctypes.byref(h), device), "apmoe_create")
+        self.handle = h.value
+        self.device = device
+
+    def close(self):
+        if self.handle:
+            lib().apmoe_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):  # pragma: no cover
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class Table:
+    """apmoe_table_* : staging, validation and stream-ordered commit."""
+
+    def __init__(self, n_layers: int, n_experts: int):
+        h = ctypes.c_void_p()
+        _check(lib().apmoe_table_create(n_layers, n_experts, ctypes.byref(h)), "apmoe_table_create")
+        self.handle = h.value
+        self.n_layers, self.n_experts = n_layers, n_experts
+
+    def set_block(self, layer: int, expert: int, kind: int, n: int, k: int, q: int, planes, luts,
+                  d: int | None = None, resident_mask: int | None = None) -> None:
+        """planes: 8 device pointers/tensors (None = not resident);
+        luts: dict {b: tensor/pointer} for b in 3..8."""
+        desc = BlockDesc()
+        desc.n, desc.k, desc.q = n, k, q
+        desc.d = q if d is None else d
+        mask = 0
+        for p in range(PLANES):
+            pp = ptr(planes[p]) if p < len(planes) else None
+            desc.plane[p] = pp
+            if pp:
+                mask |= 1 << p
+        desc.resident_mask = mask if resident_mask is None else resident_mask
+        for b in range(MAX_BITS + 1):
+            desc.lut[b] = ptr(luts.get(b)) if b in luts else None
+        _check(lib().apmoe_table_set_block(self.handle, layer, expert, kind, ctypes.byref(desc)),
+               "apmoe_table_set_block")
+
+    def set_bits(self, layer: int, expert: int, kind: int, q: int) -> None:
+        _check(lib().apmoe_table_set_bits(self.handle, layer, expert, kind, q), "apmoe_table_set_bits")
+
+    def set_plane(self, layer: int, expert: int, kind: int, p: int, plane, resident: bool) -> None:
+        _check(lib().apmoe_table_set_plane(self.handle, layer, expert, kind, p, ptr(plane), int(resident)),
+               "apmoe_table_set_plane")
+
+    def validate(self) -> int:
+        """Status apmoe_table_commit would return (no exception)."""
+        return int(lib().apmoe_table_validate(self.handle))
+
+    def committed_bits(self, layer: int, expert: int, kind: int) -> int:
+        q = ctypes.c_int32()
+        _check(lib().apmoe_table_committed_bits(self.handle, layer, expert, kind, ctypes.byref(q)),
+               "apmoe_table_committed_bits")
+        return q.value
+
+    def commit(self, ctx: Context, stream=None) -> None:
+        _check(lib().apmoe_table_commit(ctx.handle, self.handle, stream_handle(stream)), "apmoe_table_commit")
+
+    def close(self):
+        if self.handle:
+            lib().apmoe_table_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):  # pragma: no cover
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def lut_build(ctx: Context, parent, n: int, levels: dict, stream=None) -> None:
+    arr = (ctypes.c_void_p * (MAX_BITS + 1))(*[ptr(levels.get(b)) for b in range(MAX_BITS + 1)])
+    _check(lib().apmoe_lut_build(ctx.handle, ptr(parent), n, ctypes.cast(arr, ctypes.c_void_p),
+                                 stream_handle(stream)), "apmoe_lut_build")
+
+
+def pack_planes(ctx: Context, codes, n: int, k: int, planes, stream=None) -> None:
+    _check(lib().apmoe_pack_planes(ctx.handle, ptr(codes), n, k, ptr(planes), stream_handle(stream)),
+           "apmoe_pack_planes")
+
+
+def route(ctx: Context, x, w_router, bias, T: int, H: int, E: int, topk: int, renormalize: bool, topk_ids,
+          topk_w, counts, offsets, perm, inv_perm, stream=None) -> None:
+    _check(lib().apmoe_route(ctx.handle, ptr(x), ptr(w_router), ptr(bias), T, H, E, topk, int(renormalize),
+                             ptr(topk_ids), ptr(topk_w), ptr(counts), ptr(offsets), ptr(perm), ptr(inv_perm),
+                             stream_handle(stream)), "apmoe_route")
+
+
+def gemm(ctx: Context, table: Table, layer: int, kind: int, inp, gather: bool, perm, offsets, T: int, topk: int,
+         out, out_dtype: int, stream=None) -> None:
+    _check(lib().apmoe_gemm(ctx.handle, table.handle, layer, kind, ptr(inp), int(gather), ptr(perm), ptr(offsets),
+                            T, topk, ptr(out), out_dtype, stream_handle(stream)), "apmoe_gemm")
+
+
+def act(ctx: Context, h, R: int, F: int, a, stream=None) -> None:
+    _check(lib().apmoe_act(ctx.handle, ptr(h), R, F, ptr(a), stream_handle(stream)), "apmoe_act")
+
+
+def combine(ctx: Context, y, y_dtype: int, topk_w, inv_perm, T: int, topk: int, H: int, out, stream=None) -> None:
+    _check(lib().apmoe_combine(ctx.handle, ptr(y), y_dtype, ptr(topk_w), ptr(inv_perm), T, topk, H, ptr(out),
+                               stream_handle(stream)), "apmoe_combine")
+
+
+def moe_workspace(table: Table, layer: int, T: int, topk: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().apmoe_moe_workspace(table.handle, layer, T, topk, ctypes.byref(n)), "apmoe_moe_workspace")
+    return n.value
+
+
+def moe_forward(ctx: Context, table: Table, layer: int, x, w_router, bias, T: int, topk: int, renormalize: bool,
+                ws, ws_bytes: int, out, stream=None) -> None:
+    _check(lib().apmoe_moe_forward(ctx.handle, table.handle, layer, ptr(x), ptr(w_router), ptr(bias), T, topk,
+                                   int(renormalize), ptr(ws), ws_bytes, ptr(out), stream_handle(stream)),
+           "apmoe_moe_forward")

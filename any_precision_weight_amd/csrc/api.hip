@@ -1,0 +1,689 @@
+// api.hip -- host side of libapmoe: argument validation, the weight page table
+// with stream-ordered commits, and the launches of every layer step.
+//
+// Page-table semantics follow PagedWeight (arXiv:2607.16184), Section 3.1: each
+// linear-block row holds the committed bitwidth q_i used by inference, the
+// desired bitwidth d_i, and per-plane residency; offload lowers q_i before planes
+// leave and reload raises it only once they are resident; Section 3.3: changes
+// take effect only at safe boundaries -- here, between two launches on a stream.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <new>
+#include <string>
+#include <vector>
+
+#include "internal.h"
+
+using apmoe::DevBlock;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+apmoe_status fail(apmoe_status s, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+apmoe_status ok()
+{
+    return APMOE_OK;
+}
+
+apmoe_status hip_fail(hipError_t e, const char *what)
+{
+    return fail(APMOE_HIP_ERROR, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace
+
+struct apmoe_ctx {
+    int device;
+    int cus;
+    char arch[64];
+};
+
+struct apmoe_table {
+    int L, E;
+    std::vector<apmoe_block_desc> staged;
+    std::vector<uint8_t> staged_present;
+    // committed shadow (host view of what the last commit published)
+    std::vector<int32_t> cq, cn, ck;
+    std::vector<uint8_t> cpresent;
+    bool committed_once = false;
+    // device table and pinned snapshots (a ring, so commits never overwrite a
+    // snapshot whose copy is still pending)
+    int device = -1;
+    DevBlock *d_table = nullptr;
+    static constexpr int kSlots = 4;
+    DevBlock *h_snap[kSlots] = {nullptr, nullptr, nullptr, nullptr};
+    hipEvent_t ev[kSlots] = {nullptr, nullptr, nullptr, nullptr};
+    bool ev_pending[kSlots] = {false, false, false, false};
+    int slot = 0;
+
+    size_t entries() const { return (size_t)L * E * 2; }
+    size_t index(int l, int e, int u) const { return ((size_t)l * E + e) * 2 + u; }
+};
+
+namespace {
+
+apmoe_status check_ctx(apmoe_ctx *ctx)
+{
+    if (!ctx)
+        return fail(APMOE_INVALID_ARG, "ctx is NULL");
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipGetDevice");
+    if (cur != ctx->device) {
+        e = hipSetDevice(ctx->device);
+        if (e != hipSuccess)
+            return hip_fail(e, "hipSetDevice");
+    }
+    return ok();
+}
+
+apmoe_status check_index(const apmoe_table *t, int layer, int expert, int kind)
+{
+    if (!t)
+        return fail(APMOE_INVALID_ARG, "table is NULL");
+    if (layer < 0 || layer >= t->L)
+        return fail(APMOE_INVALID_ARG, "layer %d out of range [0, %d)", layer, t->L);
+    if (expert < 0 || expert >= t->E)
+        return fail(APMOE_INVALID_ARG, "expert %d out of range [0, %d)", expert, t->E);
+    if (kind != APMOE_GATE_UP && kind != APMOE_DOWN)
+        return fail(APMOE_INVALID_ARG, "kind %d is neither gate_up (0) nor down (1)", kind);
+    return ok();
+}
+
+// Validation of one staged entry (Section 3.1: q may only name resident planes).
+apmoe_status validate_entry(const apmoe_block_desc &d, int l, int e, int u)
+{
+    if (d.n < 1 || d.k < 128 || d.k % 128 != 0)
+        return fail(APMOE_INVALID_ARG, "block (%d,%d,%d): n=%d k=%d (need n>=1, k%%128==0)", l, e, u, d.n, d.k);
+    if (d.q < APMOE_MIN_BITS || d.q > APMOE_MAX_BITS)
+        return fail(APMOE_UNSUPPORTED, "block (%d,%d,%d): q=%d outside 3..8", l, e, u, d.q);
+    for (int p = 0; p < d.q; ++p) {
+        if (!((d.resident_mask >> p) & 1u) || !d.plane[p])
+            return fail(APMOE_NOT_RESIDENT, "block (%d,%d,%d): plane %d needed by q=%d is not resident", l, e, u,
+                        p, d.q);
+        if (!aligned16(d.plane[p]))
+            return fail(APMOE_INVALID_ARG, "block (%d,%d,%d): plane %d not 16-byte aligned", l, e, u, p);
+    }
+    if (!d.lut[d.q])
+        return fail(APMOE_NOT_RESIDENT, "block (%d,%d,%d): LUT level %d is NULL", l, e, u, d.q);
+    if (!aligned16(d.lut[d.q]))
+        return fail(APMOE_INVALID_ARG, "block (%d,%d,%d): LUT level %d not 16-byte aligned", l, e, u, d.q);
+    return ok();
+}
+
+apmoe_status validate_table(const apmoe_table *t)
+{
+    for (int l = 0; l < t->L; ++l)
+        for (int u = 0; u < 2; ++u) {
+            int n = -1, k = -1;
+            for (int e = 0; e < t->E; ++e) {
+                const size_t i = t->index(l, e, u);
+                if (!t->staged_present[i])
+                    continue;
+                const apmoe_block_desc &d = t->staged[i];
+                apmoe_status s = validate_entry(d, l, e, u);
+                if (s != APMOE_OK)
+                    return s;
+                if (n < 0) {
+                    n = d.n;
+                    k = d.k;
+                } else if (d.n != n || d.k != k) {
+                    return fail(APMOE_INVALID_ARG, "layer %d kind %d: experts disagree on shape (%dx%d vs %dx%d)", l,
+                                u, d.n, d.k, n, k);
+                }
+            }
+        }
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *apmoe_status_string(apmoe_status s)
+{
+    switch (s) {
+    case APMOE_OK: return "ok";
+    case APMOE_INVALID_ARG: return "invalid argument";
+    case APMOE_UNSUPPORTED: return "unsupported";
+    case APMOE_NOT_RESIDENT: return "not resident";
+    case APMOE_HIP_ERROR: return "HIP error";
+    case APMOE_OUT_OF_MEMORY: return "out of memory";
+    default: return "unknown status";
+    }
+}
+
+const char *apmoe_last_error(void) { return g_last_error.c_str(); }
+
+int32_t apmoe_version(void) { return 100; }
+
+apmoe_status apmoe_create(apmoe_ctx **out, int device)
+{
+    if (!out)
+        return fail(APMOE_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    int count = 0;
+    hipError_t e = hipGetDeviceCount(&count);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipGetDeviceCount");
+    if (device < 0 || device >= count)
+        return fail(APMOE_INVALID_ARG, "device %d out of range [0, %d)", device, count);
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, device);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipGetDeviceProperties");
+    if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+        return fail(APMOE_UNSUPPORTED, "device %d is %s; libapmoe is built for gfx950 only", device,
+                    prop.gcnArchName);
+    apmoe_ctx *c = new (std::nothrow) apmoe_ctx;
+    if (!c)
+        return fail(APMOE_OUT_OF_MEMORY, "context allocation");
+    c->device = device;
+    c->cus = prop.multiProcessorCount;
+    snprintf(c->arch, sizeof(c->arch), "%s", prop.gcnArchName);
+    *out = c;
+    return ok();
+}
+
+apmoe_status apmoe_destroy(apmoe_ctx *ctx)
+{
+    delete ctx;
+    return ok();
+}
+
+int64_t apmoe_block_bytes(int32_t n, int32_t k, int32_t b)
+{
+    if (n < 0 || k < 0 || b < 1 || b > APMOE_MAX_BITS)
+        return -1;
+    return (int64_t)n * b * k / 8 + (int64_t)n * ((int64_t)1 << b) * 2;
+}
+
+// ----------------------------------------------------------------------------
+// table
+// ----------------------------------------------------------------------------
+
+apmoe_status apmoe_table_create(int32_t n_layers, int32_t n_experts, apmoe_table **out)
+{
+    if (!out)
+        return fail(APMOE_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    if (n_layers < 1 || n_experts < 1 || n_experts > APMOE_MAX_EXPERTS)
+        return fail(APMOE_INVALID_ARG, "n_layers=%d n_experts=%d (need >=1, experts <= %d)", n_layers, n_experts,
+                    APMOE_MAX_EXPERTS);
+    apmoe_table *t = new (std::nothrow) apmoe_table;
+    if (!t)
+        return fail(APMOE_OUT_OF_MEMORY, "table allocation");
+    try {
+        t->L = n_layers;
+        t->E = n_experts;
+        apmoe_block_desc z;
+        memset(&z, 0, sizeof(z));
+        t->staged.assign(t->entries(), z);
+        t->staged_present.assign(t->entries(), 0);
+        t->cq.assign(t->entries(), 0);
+        t->cn.assign(t->entries(), 0);
+        t->ck.assign(t->entries(), 0);
+        t->cpresent.assign(t->entries(), 0);
+    } catch (...) {
+        delete t;
+        return fail(APMOE_OUT_OF_MEMORY, "table staging allocation");
+    }
+    *out = t;
+    return ok();
+}
+
+apmoe_status apmoe_table_destroy(apmoe_table *t)
+{
+    if (!t)
+        return ok();
+    apmoe_status st = APMOE_OK;
+    if (t->device >= 0) {
+        int cur = -1;
+        hipGetDevice(&cur);
+        hipSetDevice(t->device);
+        for (int i = 0; i < apmoe_table::kSlots; ++i) {
+            if (t->ev[i]) {
+                if (t->ev_pending[i] && hipEventSynchronize(t->ev[i]) != hipSuccess)
+                    st = fail(APMOE_HIP_ERROR, "pending commit failed while destroying the table");
+                hipEventDestroy(t->ev[i]);
+            }
+            if (t->h_snap[i])
+                hipHostFree(t->h_snap[i]);
+        }
+        if (t->d_table)
+            hipFree(t->d_table);
+        if (cur >= 0)
+            hipSetDevice(cur);
+    }
+    delete t;
+    return st;
+}
+
+apmoe_status apmoe_table_set_block(apmoe_table *t, int32_t layer, int32_t expert, int32_t kind,
+                                   const apmoe_block_desc *desc)
+{
+    apmoe_status s = check_index(t, layer, expert, kind);
+    if (s != APMOE_OK)
+        return s;
+    if (!desc)
+        return fail(APMOE_INVALID_ARG, "desc is NULL");
+    const size_t i = t->index(layer, expert, kind);
+    t->staged[i] = *desc;
+    t->staged_present[i] = 1;
+    return ok();
+}
+
+apmoe_status apmoe_table_set_bits(apmoe_table *t, int32_t layer, int32_t expert, int32_t kind, int32_t q)
+{
+    apmoe_status s = check_index(t, layer, expert, kind);
+    if (s != APMOE_OK)
+        return s;
+    const size_t i = t->index(layer, expert, kind);
+    if (!t->staged_present[i])
+        return fail(APMOE_INVALID_ARG, "block (%d,%d,%d) was never set", layer, expert, kind);
+    if (q < APMOE_MIN_BITS || q > APMOE_MAX_BITS)
+        return fail(APMOE_UNSUPPORTED, "q=%d outside 3..8", q);
+    t->staged[i].q = q;
+    return ok();
+}
+
+apmoe_status apmoe_table_set_plane(apmoe_table *t, int32_t layer, int32_t expert, int32_t kind, int32_t p,
+                                   const uint32_t *plane, int32_t resident)
+{
+    apmoe_status s = check_index(t, layer, expert, kind);
+    if (s != APMOE_OK)
+        return s;
+    const size_t i = t->index(layer, expert, kind);
+    if (!t->staged_present[i])
+        return fail(APMOE_INVALID_ARG, "block (%d,%d,%d) was never set", layer, expert, kind);
+    if (p < 0 || p >= APMOE_PLANES)
+        return fail(APMOE_INVALID_ARG, "plane %d out of range", p);
+    t->staged[i].plane[p] = plane;
+    if (resident)
+        t->staged[i].resident_mask |= 1u << p;
+    else
+        t->staged[i].resident_mask &= ~(1u << p);
+    return ok();
+}
+
+apmoe_status apmoe_table_validate(const apmoe_table *t)
+{
+    if (!t)
+        return fail(APMOE_INVALID_ARG, "table is NULL");
+    return validate_table(t);
+}
+
+apmoe_status apmoe_table_committed_bits(const apmoe_table *t, int32_t layer, int32_t expert, int32_t kind,
+                                        int32_t *q)
+{
+    apmoe_status s = check_index(t, layer, expert, kind);
+    if (s != APMOE_OK)
+        return s;
+    if (!q)
+        return fail(APMOE_INVALID_ARG, "q is NULL");
+    const size_t i = t->index(layer, expert, kind);
+    *q = t->cpresent[i] ? t->cq[i] : 0;
+    return ok();
+}
+
+apmoe_status apmoe_table_commit(apmoe_ctx *ctx, apmoe_table *t, void *stream)
+{
+    apmoe_status s = check_ctx(ctx);
+    if (s != APMOE_OK)
+        return s;
+    if (!t)
+        return fail(APMOE_INVALID_ARG, "table is NULL");
+    s = validate_table(t);
+    if (s != APMOE_OK)
+        return s;
+    if (t->device >= 0 && t->device != ctx->device)
+        return fail(APMOE_INVALID_ARG, "table lives on device %d, ctx on %d", t->device, ctx->device);
+    const size_t bytes = t->entries() * sizeof(DevBlock);
+    hipError_t e;
+    if (!t->d_table) {
+        e = hipMalloc(&t->d_table, bytes);
+        if (e != hipSuccess) {
+            t->d_table = nullptr;
+            return fail(APMOE_OUT_OF_MEMORY, "device table (%zu bytes): %s", bytes, hipGetErrorString(e));
+        }
+        for (int i = 0; i < apmoe_table::kSlots; ++i) {
+            e = hipHostMalloc(reinterpret_cast<void **>(&t->h_snap[i]), bytes, hipHostMallocDefault);
+            if (e == hipSuccess)
+                e = hipEventCreateWithFlags(&t->ev[i], hipEventDisableTiming);
+            if (e != hipSuccess) {
+                for (int j = 0; j <= i; ++j) {
+                    if (t->h_snap[j])
+                        hipHostFree(t->h_snap[j]);
+                    if (t->ev[j])
+                        hipEventDestroy(t->ev[j]);
+                    t->h_snap[j] = nullptr;
+                    t->ev[j] = nullptr;
+                }
+                hipFree(t->d_table);
+                t->d_table = nullptr;
+                return fail(APMOE_OUT_OF_MEMORY, "pinned table snapshot: %s", hipGetErrorString(e));
+            }
+        }
+        t->device = ctx->device;
+    }
+    const int slot = t->slot;
+    if (t->ev_pending[slot]) {
+        e = hipEventSynchronize(t->ev[slot]);
+        if (e != hipSuccess)
+            return hip_fail(e, "waiting for an earlier commit");
+        t->ev_pending[slot] = false;
+    }
+    DevBlock *snap = t->h_snap[slot];
+    for (size_t i = 0; i < t->entries(); ++i) {
+        DevBlock b;
+        memset(&b, 0, sizeof(b));
+        if (t->staged_present[i]) {
+            const apmoe_block_desc &d = t->staged[i];
+            for (int p = 0; p < APMOE_PLANES; ++p)
+                b.plane[p] = p < d.q ? d.plane[p] : nullptr;
+            b.lut = d.lut[d.q];
+            b.q = d.q;
+            b.n = d.n;
+            b.k = d.k;
+            b.present = 1;
+        }
+        snap[i] = b;
+    }
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    e = hipMemcpyAsync(t->d_table, snap, bytes, hipMemcpyHostToDevice, st);
+    if (e != hipSuccess)
+        return hip_fail(e, "table copy");
+    e = hipEventRecord(t->ev[slot], st);
+    if (e != hipSuccess)
+        return hip_fail(e, "table event");
+    t->ev_pending[slot] = true;
+    t->slot = (slot + 1) % apmoe_table::kSlots;
+    for (size_t i = 0; i < t->entries(); ++i) {
+        t->cpresent[i] = t->staged_present[i];
+        t->cq[i] = t->staged[i].q;
+        t->cn[i] = t->staged[i].n;
+        t->ck[i] = t->staged[i].k;
+    }
+    t->committed_once = true;
+    return ok();
+}
+
+// ----------------------------------------------------------------------------
+// format tools
+// ----------------------------------------------------------------------------
+
+apmoe_status apmoe_lut_build(apmoe_ctx *ctx, const uint16_t *parent, int32_t n, uint16_t *const *levels,
+                             void *stream)
+{
+    apmoe_status s = check_ctx(ctx);
+    if (s != APMOE_OK)
+        return s;
+    if (!parent || !levels)
+        return fail(APMOE_INVALID_ARG, "parent / levels is NULL");
+    if (n < 0)
+        return fail(APMOE_INVALID_ARG, "n=%d", n);
+    if (!aligned16(parent))
+        return fail(APMOE_INVALID_ARG, "parent not 16-byte aligned");
+    hipError_t e = apmoe::launch_lut_build(parent, n, levels, reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ok() : hip_fail(e, "lut_build launch");
+}
+
+apmoe_status apmoe_pack_planes(apmoe_ctx *ctx, const uint8_t *codes, int32_t n, int32_t k, uint32_t *planes,
+                               void *stream)
+{
+    apmoe_status s = check_ctx(ctx);
+    if (s != APMOE_OK)
+        return s;
+    if (!codes || !planes)
+        return fail(APMOE_INVALID_ARG, "codes / planes is NULL");
+    if (n < 0 || k < 0 || k % 32 != 0)
+        return fail(APMOE_INVALID_ARG, "n=%d k=%d (k %% 32 must be 0)", n, k);
+    hipError_t e = apmoe::launch_pack_planes(codes, n, k, planes, reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ok() : hip_fail(e, "pack_planes launch");
+}
+
+// ----------------------------------------------------------------------------
+// layer steps
+// ----------------------------------------------------------------------------
+
+apmoe_status apmoe_route(apmoe_ctx *ctx, const uint16_t *x, const uint16_t *w_router, const float *bias, int32_t T,
+                         int32_t H, int32_t E, int32_t topk, int32_t renormalize, int32_t *topk_ids, float *topk_w,
+                         int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv_perm, void *stream)
+{
+    apmoe_status s = check_ctx(ctx);
+    if (s != APMOE_OK)
+        return s;
+    if (T < 0 || H < 8 || H % 8 != 0)
+        return fail(APMOE_INVALID_ARG, "T=%d H=%d (need T>=0, H%%8==0)", T, H);
+    if (E < 1 || E > APMOE_MAX_EXPERTS)
+        return fail(APMOE_INVALID_ARG, "E=%d outside 1..%d", E, APMOE_MAX_EXPERTS);
+    if (topk < 1 || topk > E || topk > APMOE_MAX_TOPK)
+        return fail(APMOE_INVALID_ARG, "topk=%d (need 1..min(E,%d))", topk, APMOE_MAX_TOPK);
+    if (!counts || !offsets)
+        return fail(APMOE_INVALID_ARG, "counts / offsets is NULL");
+    if (T > 0 && (!x || !w_router || !topk_ids || !topk_w || !perm || !inv_perm))
+        return fail(APMOE_INVALID_ARG, "a required pointer is NULL");
+    if (T > 0 && (!aligned16(x) || !aligned16(w_router)))
+        return fail(APMOE_INVALID_ARG, "x / w_router not 16-byte aligned");
+    if ((int64_t)T * topk > (int64_t)1 << 30)
+        return fail(APMOE_INVALID_ARG, "T*topk too large");
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = apmoe::launch_route_topk(x, w_router, bias, T, H, E, topk, renormalize, topk_ids, topk_w, st);
+    if (e != hipSuccess)
+        return hip_fail(e, "route_topk launch");
+    e = apmoe::launch_route_sort(topk_ids, T * topk, E, counts, offsets, perm, inv_perm, st);
+    if (e != hipSuccess)
+        return hip_fail(e, "route_sort launch");
+    return ok();
+}
+
+static apmoe_status layer_shape(const apmoe_table *t, int layer, int kind, int *N, int *K, int *max_q)
+{
+    *N = *K = -1;
+    *max_q = 0;
+    for (int e = 0; e < t->E; ++e) {
+        const size_t i = t->index(layer, e, kind);
+        if (!t->cpresent[i])
+            return fail(APMOE_NOT_RESIDENT, "block (%d,%d,%d) has no committed entry", layer, e, kind);
+        if (*N < 0) {
+            *N = t->cn[i];
+            *K = t->ck[i];
+        }
+        if (t->cq[i] > *max_q)
+            *max_q = t->cq[i];
+    }
+    return ok();
+}
+
+apmoe_status apmoe_gemm(apmoe_ctx *ctx, const apmoe_table *tbl, int32_t layer, int32_t kind, const uint16_t *in,
+                        int32_t gather, const int32_t *perm, const int32_t *offsets, int32_t T, int32_t topk,
+                        void *out, int32_t out_dtype, void *stream)
+{
+    apmoe_status s = check_ctx(ctx);
+    if (s != APMOE_OK)
+        return s;
+    s = check_index(tbl, layer, 0, kind);
+    if (s != APMOE_OK)
+        return s;
+    if (!tbl->committed_once || !tbl->d_table)
+        return fail(APMOE_NOT_RESIDENT, "table was never committed");
+    if (tbl->device != ctx->device)
+        return fail(APMOE_INVALID_ARG, "table lives on device %d, ctx on %d", tbl->device, ctx->device);
+    if (T < 0 || topk < 1 || topk > APMOE_MAX_TOPK)
+        return fail(APMOE_INVALID_ARG, "T=%d topk=%d", T, topk);
+    if (out_dtype != APMOE_F16 && out_dtype != APMOE_F32)
+        return fail(APMOE_UNSUPPORTED, "out_dtype %d", out_dtype);
+    if (!offsets)
+        return fail(APMOE_INVALID_ARG, "offsets is NULL");
+    if (T == 0)
+        return ok();
+    if (!in || !out || (gather && !perm))
+        return fail(APMOE_INVALID_ARG, "in / out / perm is NULL");
+    if (!aligned16(in) || !aligned16(out))
+        return fail(APMOE_INVALID_ARG, "in / out not 16-byte aligned");
+    int N, K, max_q;
+    s = layer_shape(tbl, layer, kind, &N, &K, &max_q);
+    if (s != APMOE_OK)
+        return s;
+    const DevBlock *slice = tbl->d_table + tbl->index(layer, 0, 0);
+    hipError_t e = apmoe::launch_gemm(slice, kind, tbl->E, N, K, max_q, in, gather, perm, offsets, topk, out,
+                                      out_dtype == APMOE_F32, reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ok() : hip_fail(e, "gemm launch");
+}
+
+apmoe_status apmoe_act(apmoe_ctx *ctx, const uint16_t *h, int32_t R, int32_t F, uint16_t *a, void *stream)
+{
+    apmoe_status s = check_ctx(ctx);
+    if (s != APMOE_OK)
+        return s;
+    if (R < 0 || F < 8 || F % 8 != 0)
+        return fail(APMOE_INVALID_ARG, "R=%d F=%d (need F%%8==0)", R, F);
+    if (R > 0 && (!h || !a || !aligned16(h) || !aligned16(a)))
+        return fail(APMOE_INVALID_ARG, "h / a NULL or not 16-byte aligned");
+    hipError_t e = apmoe::launch_act(h, R, F, a, reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ok() : hip_fail(e, "act launch");
+}
+
+apmoe_status apmoe_combine(apmoe_ctx *ctx, const void *y, int32_t y_dtype, const float *topk_w,
+                           const int32_t *inv_perm, int32_t T, int32_t topk, int32_t H, uint16_t *out, void *stream)
+{
+    apmoe_status s = check_ctx(ctx);
+    if (s != APMOE_OK)
+        return s;
+    if (T < 0 || topk < 1 || topk > APMOE_MAX_TOPK || H < 8 || H % 8 != 0)
+        return fail(APMOE_INVALID_ARG, "T=%d topk=%d H=%d", T, topk, H);
+    if (y_dtype != APMOE_F16 && y_dtype != APMOE_F32)
+        return fail(APMOE_UNSUPPORTED, "y_dtype %d", y_dtype);
+    if (T > 0 && (!y || !topk_w || !inv_perm || !out || !aligned16(y) || !aligned16(out)))
+        return fail(APMOE_INVALID_ARG, "NULL or misaligned pointer");
+    hipError_t e = apmoe::launch_combine(y, y_dtype == APMOE_F32, topk_w, inv_perm, T, topk, H, out,
+                                         reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ok() : hip_fail(e, "combine launch");
+}
+
+// ----------------------------------------------------------------------------
+// whole layer
+// ----------------------------------------------------------------------------
+
+namespace {
+struct WsLayout {
+    size_t ids, w, counts, offsets, perm, inv_perm, h, a, y, total;
+};
+
+size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+WsLayout ws_layout(int T, int topk, int E, int H, int F)
+{
+    WsLayout L;
+    const size_t R = (size_t)T * topk;
+    size_t o = 0;
+    L.ids = o;
+    o = up256(o + R * 4);
+    L.w = o;
+    o = up256(o + R * 4);
+    L.counts = o;
+    o = up256(o + (size_t)E * 4);
+    L.offsets = o;
+    o = up256(o + ((size_t)E + 1) * 4);
+    L.perm = o;
+    o = up256(o + R * 4);
+    L.inv_perm = o;
+    o = up256(o + R * 4);
+    L.h = o;
+    o = up256(o + R * 2 * F * 2);
+    L.a = o;
+    o = up256(o + R * F * 2);
+    L.y = o;
+    o = up256(o + R * H * 4);
+    L.total = o;
+    return L;
+}
+}  // namespace
+
+apmoe_status apmoe_moe_workspace(const apmoe_table *tbl, int32_t layer, int32_t T, int32_t topk, size_t *bytes)
+{
+    apmoe_status s = check_index(tbl, layer, 0, 0);
+    if (s != APMOE_OK)
+        return s;
+    if (!bytes || T < 0 || topk < 1)
+        return fail(APMOE_INVALID_ARG, "bytes NULL or T/topk invalid");
+    int N0, K0, q0, N1, K1, q1;
+    s = layer_shape(tbl, layer, APMOE_GATE_UP, &N0, &K0, &q0);
+    if (s != APMOE_OK)
+        return s;
+    s = layer_shape(tbl, layer, APMOE_DOWN, &N1, &K1, &q1);
+    if (s != APMOE_OK)
+        return s;
+    *bytes = ws_layout(T, topk, tbl->E, K0, K1).total;
+    return ok();
+}
+
+apmoe_status apmoe_moe_forward(apmoe_ctx *ctx, const apmoe_table *tbl, int32_t layer, const uint16_t *x,
+                               const uint16_t *w_router, const float *bias, int32_t T, int32_t topk,
+                               int32_t renormalize, void *ws, size_t ws_bytes, uint16_t *out, void *stream)
+{
+    apmoe_status s = check_ctx(ctx);
+    if (s != APMOE_OK)
+        return s;
+    s = check_index(tbl, layer, 0, 0);
+    if (s != APMOE_OK)
+        return s;
+    int N0, K0, q0, N1, K1, q1;
+    s = layer_shape(tbl, layer, APMOE_GATE_UP, &N0, &K0, &q0);
+    if (s != APMOE_OK)
+        return s;
+    s = layer_shape(tbl, layer, APMOE_DOWN, &N1, &K1, &q1);
+    if (s != APMOE_OK)
+        return s;
+    const int H = K0, F = K1;
+    if (N0 != 2 * F || N1 != H)
+        return fail(APMOE_INVALID_ARG, "layer %d shapes: gate_up %dx%d, down %dx%d are not [2F x H], [H x F]",
+                    layer, N0, K0, N1, K1);
+    const WsLayout L = ws_layout(T, topk, tbl->E, H, F);
+    if (!ws || ws_bytes < L.total || ((uintptr_t)ws & 255u))
+        return fail(APMOE_INVALID_ARG, "workspace NULL, unaligned or smaller than %zu bytes", L.total);
+    if (T > 0 && (!out || !aligned16(out)))
+        return fail(APMOE_INVALID_ARG, "out NULL or misaligned");
+    char *w = reinterpret_cast<char *>(ws);
+    int32_t *ids = reinterpret_cast<int32_t *>(w + L.ids);
+    float *tw = reinterpret_cast<float *>(w + L.w);
+    int32_t *counts = reinterpret_cast<int32_t *>(w + L.counts);
+    int32_t *offsets = reinterpret_cast<int32_t *>(w + L.offsets);
+    int32_t *perm = reinterpret_cast<int32_t *>(w + L.perm);
+    int32_t *inv = reinterpret_cast<int32_t *>(w + L.inv_perm);
+    uint16_t *h = reinterpret_cast<uint16_t *>(w + L.h);
+    uint16_t *a = reinterpret_cast<uint16_t *>(w + L.a);
+    float *y = reinterpret_cast<float *>(w + L.y);
+    s = apmoe_route(ctx, x, w_router, bias, T, H, tbl->E, topk, renormalize, ids, tw, counts, offsets, perm, inv,
+                    stream);
+    if (s != APMOE_OK || T == 0)
+        return s;
+    s = apmoe_gemm(ctx, tbl, layer, APMOE_GATE_UP, x, 1, perm, offsets, T, topk, h, APMOE_F16, stream);
+    if (s != APMOE_OK)
+        return s;
+    s = apmoe_act(ctx, h, T * topk, F, a, stream);
+    if (s != APMOE_OK)
+        return s;
+    s = apmoe_gemm(ctx, tbl, layer, APMOE_DOWN, a, 0, perm, offsets, T, topk, y, APMOE_F32, stream);
+    if (s != APMOE_OK)
+        return s;
+    return apmoe_combine(ctx, y, APMOE_F32, tw, inv, T, topk, H, out, stream);
+}
+
+}  // extern "C"

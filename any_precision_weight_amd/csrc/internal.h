@@ -1,0 +1,41 @@
+// internal.h -- declarations shared by the libapmoe HIP sources (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "apmoe.h"
+
+namespace apmoe {
+
+// One committed linear-block as the kernels see it (device table entry).
+// plane[p] is valid for p < q; lut points at level q, fp16 [n][2^q].
+struct DevBlock {
+    const uint32_t *plane[APMOE_PLANES];
+    const uint16_t *lut;
+    int32_t q;
+    int32_t n;
+    int32_t k;
+    int32_t present;
+};
+
+// Rows of the weight matrix handled by one workgroup of the decode product.
+constexpr int kGemmRowsPerBlock = 64;
+
+hipError_t launch_route_topk(const uint16_t *x, const uint16_t *wr, const float *bias, int T, int H, int E, int topk,
+                             int renormalize, int32_t *ids, float *w, hipStream_t s);
+hipError_t launch_route_sort(const int32_t *ids, int R, int E, int32_t *counts, int32_t *offsets, int32_t *perm,
+                             int32_t *inv_perm, hipStream_t s);
+
+// table points at the (layer) slice: entry for expert e and kind u is table[2*e + u].
+hipError_t launch_gemm(const DevBlock *table, int kind, int E, int N, int K, int max_q, const uint16_t *in,
+                       int gather, const int32_t *perm, const int32_t *offsets, int topk, void *out, int out_f32,
+                       hipStream_t s);
+
+hipError_t launch_act(const uint16_t *h, int R, int F, uint16_t *a, hipStream_t s);
+hipError_t launch_combine(const void *y, int y_f32, const float *w, const int32_t *inv_perm, int T, int topk, int H,
+                          uint16_t *out, hipStream_t s);
+hipError_t launch_lut_build(const uint16_t *parent, int n, uint16_t *const *levels, hipStream_t s);
+hipError_t launch_pack_planes(const uint8_t *codes, int n, int k, uint32_t *planes, hipStream_t s);
+
+}  // namespace apmoe

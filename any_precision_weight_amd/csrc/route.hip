@@ -1,0 +1,234 @@
+// route.hip -- router of the MoE layer (PagedWeight, Section 2.1: the router
+// weights E experts per token and selects the top K) and the expert-grouped
+// ordering of the selected (token, slot) assignments that the expert products
+// consume.
+//
+// Logits are accumulated in fp64: every product of two fp16 values is exact in
+// fp64, so the only rounding is in the additions.  All experts of a token are
+// summed in the same order, which makes identical router rows give identical
+// logits and lets ties resolve to the lower expert index deterministically.
+#include "internal.h"
+
+namespace apmoe {
+namespace {
+
+constexpr int kWave = 64;
+constexpr int kTokensPerBlock = 4;
+
+__device__ inline double h2d(uint16_t h) { return (double)__builtin_bit_cast(_Float16, h); }
+
+// (z, e) ordering: larger logit first, lower expert index on ties.
+__device__ inline bool better(double za, int ea, double zb, int eb)
+{
+    return (za > zb) || (za == zb && ea < eb);
+}
+
+__global__ void __launch_bounds__(256) route_topk_kernel(const uint16_t *__restrict__ x,
+                                                         const uint16_t *__restrict__ wr,
+                                                         const float *__restrict__ bias, int T, int H, int E,
+                                                         int topk, int renormalize, int32_t *__restrict__ ids,
+                                                         float *__restrict__ wout)
+{
+    __shared__ double zs[kTokensPerBlock][APMOE_MAX_EXPERTS];
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int t = blockIdx.x * kTokensPerBlock + wave;
+    if (t >= T)
+        return;  // no block-wide barrier below
+    const uint16_t *xr = x + (size_t)t * H;
+
+    for (int e0 = 0; e0 < E; e0 += 8) {
+        double acc[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            acc[j] = 0.0;
+        for (int h = lane * 8; h < H; h += kWave * 8) {
+            const uint4 xv = *reinterpret_cast<const uint4 *>(xr + h);
+            double xd[8];
+            const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                xd[2 * i] = h2d((uint16_t)(xw[i] & 0xFFFFu));
+                xd[2 * i + 1] = h2d((uint16_t)(xw[i] >> 16));
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                if (e0 + j < E) {
+                    const uint4 wv = *reinterpret_cast<const uint4 *>(wr + (size_t)(e0 + j) * H + h);
+                    const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        acc[j] += xd[2 * i] * h2d((uint16_t)(ww[i] & 0xFFFFu));
+                        acc[j] += xd[2 * i + 1] * h2d((uint16_t)(ww[i] >> 16));
+                    }
+                }
+            }
+        }
+        // butterfly over the wave; lane 0's result is the logit (same order for every expert)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1)
+                acc[j] += __shfl_xor(acc[j], off, kWave);
+        }
+        if (lane == 0) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (e0 + j < E)
+                    zs[wave][e0 + j] = acc[j] + (bias ? (double)bias[e0 + j] : 0.0);
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // top-k: each lane owns experts lane, lane+64, ...
+    unsigned taken = 0;  // bit i: expert lane + 64*i selected
+    double zsel[APMOE_MAX_TOPK];
+    int esel[APMOE_MAX_TOPK];
+    for (int j = 0; j < topk; ++j) {
+        double bz = -INFINITY;
+        int be = 0x7FFFFFFF;
+        for (int i = 0; i * kWave + lane < E; ++i) {
+            const int e = i * kWave + lane;
+            if (taken & (1u << i))
+                continue;
+            const double z = zs[wave][e];
+            if (be == 0x7FFFFFFF || better(z, e, bz, be)) {
+                bz = z;
+                be = e;
+            }
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            const double oz = __shfl_xor(bz, off, kWave);
+            const int oe = __shfl_xor(be, off, kWave);
+            if (oe != 0x7FFFFFFF && (be == 0x7FFFFFFF || better(oz, oe, bz, be))) {
+                bz = oz;
+                be = oe;
+            }
+        }
+        if (be % kWave == lane)
+            taken |= 1u << (be / kWave);
+        zsel[j] = bz;
+        esel[j] = be;
+    }
+    if (lane == 0) {
+        const double zmax = zsel[0];
+        double den = 0.0;
+        if (renormalize) {
+            for (int j = 0; j < topk; ++j)
+                den += exp(zsel[j] - zmax);
+        } else {
+            for (int e = 0; e < E; ++e)
+                den += exp(zs[wave][e] - zmax);
+        }
+        for (int j = 0; j < topk; ++j) {
+            ids[(size_t)t * topk + j] = esel[j];
+            wout[(size_t)t * topk + j] = (float)(exp(zsel[j] - zmax) / den);
+        }
+    }
+}
+
+// Stable counting sort of the R = T*topk assignments by expert, in one
+// workgroup: per 1024-assignment chunk, every wave ranks its lanes inside each
+// expert with ballots, and waves are ordered by a prefix over per-wave counts.
+constexpr int kSortThreads = 1024;
+constexpr int kSortWaves = kSortThreads / kWave;
+
+__global__ void __launch_bounds__(kSortThreads) route_sort_kernel(const int32_t *__restrict__ ids, int R, int E,
+                                                                  int32_t *__restrict__ counts,
+                                                                  int32_t *__restrict__ offsets,
+                                                                  int32_t *__restrict__ perm,
+                                                                  int32_t *__restrict__ inv_perm)
+{
+    __shared__ int cnt[APMOE_MAX_EXPERTS];
+    __shared__ int off[APMOE_MAX_EXPERTS + 1];
+    __shared__ int wcnt[kSortWaves][APMOE_MAX_EXPERTS];
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+
+    for (int e = tid; e < E; e += kSortThreads)
+        cnt[e] = 0;
+    __syncthreads();
+    for (int a = tid; a < R; a += kSortThreads) {
+        const int e = ids[a];
+        if (e >= 0 && e < E)
+            atomicAdd(&cnt[e], 1);
+    }
+    __syncthreads();
+    if (tid == 0) {
+        off[0] = 0;
+        for (int e = 0; e < E; ++e)
+            off[e + 1] = off[e] + cnt[e];
+    }
+    __syncthreads();
+    for (int e = tid; e <= E; e += kSortThreads) {
+        offsets[e] = off[e];
+        if (e < E)
+            counts[e] = cnt[e];
+    }
+    __syncthreads();
+    for (int e = tid; e < E; e += kSortThreads)
+        cnt[e] = 0;  // running position inside each expert
+    __syncthreads();
+
+    for (int base = 0; base < R; base += kSortThreads) {
+        const int a = base + tid;
+        int e = a < R ? ids[a] : -1;
+        if (e < 0 || e >= E)
+            e = -1;  // never produced by the router; keeps every index in range
+        // rank among lower lanes of this wave with the same expert, and whether
+        // this lane is the last of its expert in the wave
+        int rank = 0, after = 0;
+        for (int l = 0; l < kWave; ++l) {
+            const int el = __shfl(e, l, kWave);
+            if (el == e) {
+                rank += l < lane;
+                after += l > lane;
+            }
+        }
+        for (int i = lane; i < E; i += kWave)
+            wcnt[wave][i] = 0;
+        __syncthreads();
+        if (e >= 0 && after == 0)
+            wcnt[wave][e] = rank + 1;
+        __syncthreads();
+        if (e >= 0) {
+            int pos = off[e] + cnt[e] + rank;
+            for (int w = 0; w < wave; ++w)
+                pos += wcnt[w][e];
+            perm[pos] = a;
+            inv_perm[a] = pos;
+        }
+        __syncthreads();
+        for (int i = tid; i < E; i += kSortThreads) {
+            int s = 0;
+            for (int w = 0; w < kSortWaves; ++w)
+                s += wcnt[w][i];
+            cnt[i] += s;
+        }
+        __syncthreads();
+    }
+}
+
+}  // namespace
+
+hipError_t launch_route_topk(const uint16_t *x, const uint16_t *wr, const float *bias, int T, int H, int E, int topk,
+                             int renormalize, int32_t *ids, float *w, hipStream_t s)
+{
+    if (T <= 0)
+        return hipSuccess;
+    const int blocks = (T + kTokensPerBlock - 1) / kTokensPerBlock;
+    hipLaunchKernelGGL(route_topk_kernel, dim3(blocks), dim3(kTokensPerBlock * kWave), 0, s, x, wr, bias, T, H, E,
+                       topk, renormalize, ids, w);
+    return hipGetLastError();
+}
+
+hipError_t launch_route_sort(const int32_t *ids, int R, int E, int32_t *counts, int32_t *offsets, int32_t *perm,
+                             int32_t *inv_perm, hipStream_t s)
+{
+    hipLaunchKernelGGL(route_sort_kernel, dim3(1), dim3(kSortThreads), 0, s, ids, R, E, counts, offsets, perm,
+                       inv_perm);
+    return hipGetLastError();
+}
+
+}  // namespace apmoe

@@ -1,0 +1,241 @@
+/*
+ * apmoe.h -- C ABI of libapmoe, the any-precision MoE expert layer for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The layer follows "PagedWeight: Efficient MoE LLM Serving with Dynamic
+ * Quality-Aware Weight Quantization" (arXiv:2607.16184):
+ *   - Section 3.1: a linear-block i = (layer, expert, u), u in {gate_up, down},
+ *     is the unit of quantisation; its weight page table row holds the committed
+ *     bitwidth q_i used by inference, the desired bitwidth d_i, and per-plane
+ *     residency (GPU-resident, CPU-resident, in transfer).
+ *   - Section 3 and the Figure 3 caption: weights are Any-Precision overlaid
+ *     bit-planes (a b-bit weight uses a subset of the planes) plus a LUT of
+ *     bitwidth-specific centroids.
+ *   - Section 3.1 (offload/reload) and Section 3.3: q_i is lowered before pages
+ *     leave the GPU and raised only after they are resident again, and changes
+ *     are committed only at safe boundaries.
+ *   - Section 3.3 ("Fused Mixed-Precision MoE Kernel"): routing, expert
+ *     activation, down projection and output accumulation, each gate_up / down
+ *     module at its own bitwidth.
+ *
+ * Format conventions (readings of the paper where it is silent):
+ *   - 8 parent planes.  Plane p holds bit (7 - p) of the 8-bit parent code, so a
+ *     q-bit block reads planes 0..q-1 and its code is the parent code >> (8 - q).
+ *   - Plane p of an n x k block is uint32 [n][k/32]; bit j of word w is column
+ *     32*w + j.
+ *   - The LUT is per output row: level b is fp16 [n][2^b], entry [row][code].
+ *   - gate_up is [2F x H] with rows [0, F) the gate and [F, 2F) the up
+ *     projection; down is [H x F].  Activation is SiLU(gate) * up.
+ *
+ * Conventions of every call:
+ *   - Every function returns an apmoe_status; no exception crosses the ABI and
+ *     the library never aborts.  Arguments are validated on the host before
+ *     anything is enqueued; a failed call enqueues nothing and changes nothing.
+ *     apmoe_last_error() gives a thread-local message for the last failure.
+ *   - Tensor arguments are device pointers owned by the caller, 16-byte
+ *     aligned, row-major and dense.  The library allocates device memory only in
+ *     apmoe_table_commit (the device table, once per table) and never on the
+ *     compute calls.
+ *   - Compute calls are asynchronous on the HIP stream passed as void*
+ *     (NULL = the default stream) and never synchronise the host.
+ *   - A context is bound to one device and is not thread-safe; use one per
+ *     host thread.
+ */
+#ifndef APMOE_H
+#define APMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t apmoe_status;
+
+#define APMOE_OK 0
+#define APMOE_INVALID_ARG 1   /* null pointer, bad shape, misalignment, index out of range */
+#define APMOE_UNSUPPORTED 2   /* q outside 3..8, unsupported dtype, device not gfx950 */
+#define APMOE_NOT_RESIDENT 3  /* commit would use a plane or LUT that is not resident */
+#define APMOE_HIP_ERROR 4     /* the HIP runtime reported an error */
+#define APMOE_OUT_OF_MEMORY 5 /* host or device allocation failed (create / first commit only) */
+
+#define APMOE_GATE_UP 0
+#define APMOE_DOWN 1
+
+#define APMOE_F16 0
+#define APMOE_F32 1
+
+#define APMOE_MIN_BITS 3
+#define APMOE_MAX_BITS 8
+#define APMOE_PLANES 8
+#define APMOE_MAX_EXPERTS 256
+#define APMOE_MAX_TOPK 8
+
+typedef struct apmoe_ctx apmoe_ctx;
+typedef struct apmoe_table apmoe_table;
+
+/*
+ * One linear-block (Section 3.1 page table row, GPU part).
+ *   n, k          : rows (outputs) and columns (inputs); k % 128 == 0, n >= 1.
+ *   q             : committed bitwidth to publish, 3..8 (the paper's q_i).
+ *   d             : desired bitwidth (the paper's d_i); stored, never read by kernels.
+ *   resident_mask : bit p set when plane[p] holds valid device data.
+ *   plane[p]      : device uint32 [n][k/32], code bit (7 - p); may be NULL when not
+ *                   resident.
+ *   lut[b]        : device fp16 [n][2^b] for b = 3..8; lut[0..2] are ignored.
+ * A commit of this block requires planes 0..q-1 resident and non-NULL and lut[q]
+ * non-NULL.  Planes p >= q and other LUT levels are never read by the kernels.
+ */
+typedef struct apmoe_block_desc {
+    int32_t n;
+    int32_t k;
+    int32_t q;
+    int32_t d;
+    uint32_t resident_mask;
+    const uint32_t *plane[APMOE_PLANES];
+    const uint16_t *lut[APMOE_MAX_BITS + 1];
+} apmoe_block_desc;
+
+/* Text of a status code (static storage). */
+const char *apmoe_status_string(apmoe_status s);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char *apmoe_last_error(void);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int32_t apmoe_version(void);
+
+/* Bind a context to HIP device `device`.  Fails with APMOE_UNSUPPORTED on a
+ * device that is not gfx950. */
+apmoe_status apmoe_create(apmoe_ctx **out, int device);
+apmoe_status apmoe_destroy(apmoe_ctx *ctx);
+
+/*
+ * Eq. 3 (Section 3.1): M_i^b, the GPU bytes of an n x k block at b bits,
+ * n * b * k / 8 plane bytes plus n * 2^b * 2 LUT bytes.  The memory released by
+ * b -> b' is apmoe_block_bytes(n,k,b) - apmoe_block_bytes(n,k,b').  Host only;
+ * returns -1 for invalid arguments.
+ */
+int64_t apmoe_block_bytes(int32_t n, int32_t k, int32_t b);
+
+/* ---------------------------------------------------------------------------
+ * Block table (Section 3.1 weight page table; Section 3.3 safe-boundary commit)
+ *
+ * The table has n_layers * n_experts * 2 entries.  set_* calls edit a host
+ * staging copy only.  apmoe_table_commit validates the whole staging copy and
+ * enqueues its publication on a stream: kernels enqueued on that stream before
+ * the commit read the previous committed table, kernels enqueued after read the
+ * new one.  Kernels enqueued on other streams are ordered only by the caller.
+ * The caller keeps every plane and LUT referenced by a committed table alive
+ * until a later commit no longer references it and the stream has passed that
+ * commit.  Host-side calls below need no GPU except commit and destroy.
+ * ------------------------------------------------------------------------ */
+apmoe_status apmoe_table_create(int32_t n_layers, int32_t n_experts, apmoe_table **out);
+
+/* Waits for this table's pending commits, then frees it. */
+apmoe_status apmoe_table_destroy(apmoe_table *tbl);
+
+/* Stage a whole block entry (copied; pointers are not dereferenced). */
+apmoe_status apmoe_table_set_block(apmoe_table *tbl, int32_t layer, int32_t expert, int32_t kind,
+                                   const apmoe_block_desc *desc);
+
+/* Stage a new committed bitwidth q (3..8) for one block (offload lowers q before
+ * pages leave; reload raises q after pages are resident). */
+apmoe_status apmoe_table_set_bits(apmoe_table *tbl, int32_t layer, int32_t expert, int32_t kind, int32_t q);
+
+/* Stage new residency for one block: mask bit p and plane[p] (NULL allowed). */
+apmoe_status apmoe_table_set_plane(apmoe_table *tbl, int32_t layer, int32_t expert, int32_t kind, int32_t p,
+                                   const uint32_t *plane, int32_t resident);
+
+/* What apmoe_table_commit would return for the current staging copy (host only). */
+apmoe_status apmoe_table_validate(const apmoe_table *tbl);
+
+/* Committed (last published) bitwidth of a block, 0 if never committed. */
+apmoe_status apmoe_table_committed_bits(const apmoe_table *tbl, int32_t layer, int32_t expert, int32_t kind,
+                                        int32_t *q);
+
+/* Validate the staging copy and publish it on `stream`.  On error the
+ * committed table is unchanged.  The first commit allocates the device table. */
+apmoe_status apmoe_table_commit(apmoe_ctx *ctx, apmoe_table *tbl, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * Format tools
+ * ------------------------------------------------------------------------ */
+
+/* Child LUT levels from the parent level 8 (fp16 [n][256], device):
+ * level b = fp16 round-to-nearest-even of the mean of entries 2c and 2c+1 of
+ * level b+1.  levels is a host array of 9 device pointers; levels[b] (fp16
+ * [n][2^b]) is written for each b in 3..7 that is non-NULL. */
+apmoe_status apmoe_lut_build(apmoe_ctx *ctx, const uint16_t *parent, int32_t n, uint16_t *const *levels,
+                             void *stream);
+
+/* Pack parent codes (uint8 [n][k], device) into 8 planes (uint32 [8][n][k/32]). */
+apmoe_status apmoe_pack_planes(apmoe_ctx *ctx, const uint8_t *codes, int32_t n, int32_t k, uint32_t *planes,
+                               void *stream);
+
+/* ---------------------------------------------------------------------------
+ * Layer steps
+ * ------------------------------------------------------------------------ */
+
+/*
+ * Router (Section 2.1: the router weights E experts and keeps the top K).
+ *   x [T][H] fp16, w_router [E][H] fp16, bias [E] fp32 or NULL.
+ *   logit z[t][e] = sum_h x*w in fp64 (exact fp16 products), then + bias[e].
+ *   topk_ids [T][topk] : experts by descending logit, ties to the lower index.
+ *   topk_w   [T][topk] : fp32; renormalize != 0: softmax over the selected
+ *                        logits; else the full softmax over E, at the selected.
+ *   counts [E], offsets [E+1] (offsets[E] = T*topk), perm [T*topk]: assignment
+ *   ids a = t*topk + j grouped by expert ascending, ascending a inside a
+ *   group; inv_perm [T*topk]: inv_perm[perm[r]] = r.
+ * Limits: 1 <= E <= 256, 1 <= topk <= min(E, 8), T >= 0 (T = 0 writes counts
+ * and offsets only), H % 8 == 0.
+ */
+apmoe_status apmoe_route(apmoe_ctx *ctx, const uint16_t *x, const uint16_t *w_router, const float *bias, int32_t T,
+                         int32_t H, int32_t E, int32_t topk, int32_t renormalize, int32_t *topk_ids, float *topk_w,
+                         int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv_perm, void *stream);
+
+/*
+ * Any-precision product of every expert of one (layer, kind) in one launch.
+ * For expert e, rows r in [offsets[e], offsets[e+1]) of the output:
+ *   out[r][n] = sum_c in_row(r)[c] * LUT_q[n][code_q(n, c)],   fp32 accumulation,
+ * with q, planes and LUT of block (layer, e, kind) read from the committed
+ * device table at execution time.  in_row(r) = in[perm[r] / topk] when
+ * gather != 0 (gate_up reading token activations), else in[r].
+ *   in  : fp16 [T][K] (gather) or [T*topk][K]
+ *   out : [T*topk][N] of out_dtype (APMOE_F16 rounds to nearest even).
+ * N and K are the block shape; every expert of (layer, kind) must be committed
+ * with the same shape.  offsets is device memory written by apmoe_route; no
+ * host synchronisation happens.
+ */
+apmoe_status apmoe_gemm(apmoe_ctx *ctx, const apmoe_table *tbl, int32_t layer, int32_t kind, const uint16_t *in,
+                        int32_t gather, const int32_t *perm, const int32_t *offsets, int32_t T, int32_t topk,
+                        void *out, int32_t out_dtype, void *stream);
+
+/* Expert activation: a[r][f] = SiLU(h[r][f]) * h[r][F + f] in fp32, stored fp16.
+ * h fp16 [R][2F], a fp16 [R][F], F % 8 == 0. */
+apmoe_status apmoe_act(apmoe_ctx *ctx, const uint16_t *h, int32_t R, int32_t F, uint16_t *a, void *stream);
+
+/* Output accumulation: out[t][n] = sum_{j < topk} topk_w[t][j] * y[inv_perm[t*topk + j]][n],
+ * fp32, summed in j order, stored fp16.  y is [T*topk][H] of y_dtype; H % 8 == 0. */
+apmoe_status apmoe_combine(apmoe_ctx *ctx, const void *y, int32_t y_dtype, const float *topk_w,
+                           const int32_t *inv_perm, int32_t T, int32_t topk, int32_t H, uint16_t *out, void *stream);
+
+/* Device workspace bytes needed by apmoe_moe_forward for one layer of tbl. */
+apmoe_status apmoe_moe_workspace(const apmoe_table *tbl, int32_t layer, int32_t T, int32_t topk, size_t *bytes);
+
+/*
+ * Whole layer: route, gate_up (gather, fp16 h), act, down (fp32 y), combine.
+ * ws is caller-owned device memory of at least apmoe_moe_workspace bytes, 256-byte
+ * aligned; it holds ids, weights, counts, offsets, perm, inv_perm, h, a and y.
+ * out fp16 [T][H].
+ */
+apmoe_status apmoe_moe_forward(apmoe_ctx *ctx, const apmoe_table *tbl, int32_t layer, const uint16_t *x,
+                               const uint16_t *w_router, const float *bias, int32_t T, int32_t topk,
+                               int32_t renormalize, void *ws, size_t ws_bytes, uint16_t *out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* APMOE_H */

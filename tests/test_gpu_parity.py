@@ -1,0 +1,374 @@
+"""GPU parity of libapmoe against the fp64 oracle (calls go through the C ABI).
+
+Bars: route ids, counts, offsets, perm, inv_perm bit-exact; routing weights
+within 1e-6; identity-LUT products (integers, fp32 out) bit-exact; fp16 products
+within half an fp16 ulp plus the fp32 accumulation bound; layer outputs within
+max-abs 1e-2 and relative L2 2e-3 of the fp64 oracle.
+
+Paper: PagedWeight (arXiv:2607.16184), Section 2.1 (router, Eq. 1), Section 3 /
+Figure 3 caption (bit-planes + LUT), Section 3.1 (page table, q_i only over
+resident planes), Section 3.3 (safe-boundary commits; fused MoE layer).
+"""
+import numpy as np
+import pytest
+import torch
+
+import any_precision_weight_amd as apw
+import oracle
+import synth
+from gpu_util import Layer, check_out, check_route, ctx, dev, host, topk_margin_ok, ulp16
+
+pytestmark = pytest.mark.gpu
+
+RNG = np.random.default_rng(2024)
+
+
+# --------------------------------------------------------------------------- route
+
+ROUTE_CASES = [
+    # (T, H, E, k, bias, renorm, seed)
+    (8, 256, 4, 2, False, True, 0),
+    (1, 4096, 8, 2, False, True, 1),
+    (13, 4096, 8, 2, True, True, 2),
+    (300, 512, 60, 4, False, True, 3),
+    (37, 256, 128, 8, True, True, 4),
+    (50, 256, 8, 2, True, False, 5),
+    (1500, 128, 8, 2, True, True, 6),
+    (0, 256, 8, 2, False, True, 7),
+]
+
+
+@pytest.mark.parametrize("case", ROUTE_CASES, ids=lambda c: f"T{c[0]}H{c[1]}E{c[2]}k{c[3]}")
+def test_route_parity(case):
+    T, H, E, k, use_bias, renorm, seed = case
+    x = synth.fp16_normal(100 + seed, 1, T * H, 1.0).reshape(T, H)
+    wr = synth.fp16_normal(100 + seed, 2, E * H, 0.02).reshape(E, H)
+    bias = synth.fp16_normal(100 + seed, 3, E, 1.0).astype(np.float32) if use_bias else None
+    if T > 0:
+        assert topk_margin_ok(x, wr, bias, k)
+    r = oracle.route(x, wr, bias, k, renorm)
+    R = T * k
+    o = dict(ids=torch.empty((T, k), dtype=torch.int32, device="cuda"),
+             w=torch.empty((T, k), dtype=torch.float32, device="cuda"),
+             counts=torch.full((E,), -1, dtype=torch.int32, device="cuda"),
+             offsets=torch.full((E + 1,), -1, dtype=torch.int32, device="cuda"),
+             perm=torch.empty(R, dtype=torch.int32, device="cuda"),
+             inv_perm=torch.empty(R, dtype=torch.int32, device="cuda"))
+    xd = dev(x) if T > 0 else torch.empty((1, H), dtype=torch.float16, device="cuda")
+    apw.route(ctx(), xd, dev(wr), None if bias is None else dev(bias), T, H, E, k, renorm, o["ids"], o["w"],
+              o["counts"], o["offsets"], o["perm"], o["inv_perm"])
+    torch.cuda.synchronize()
+    check_route(o, r)
+
+
+def test_route_ties_lower_index():
+    T, H, E, k = 40, 256, 8, 2
+    x = synth.fp16_normal(9, 1, T * H, 1.0).reshape(T, H)
+    wr = synth.fp16_normal(9, 2, E * H, 0.02).reshape(E, H)
+    wr[5] = wr[2]
+    wr[7] = wr[2]
+    r = oracle.route(x, wr, None, k)
+    o = dict(ids=torch.empty((T, k), dtype=torch.int32, device="cuda"),
+             w=torch.empty((T, k), dtype=torch.float32, device="cuda"),
+             counts=torch.empty(E, dtype=torch.int32, device="cuda"),
+             offsets=torch.empty(E + 1, dtype=torch.int32, device="cuda"),
+             perm=torch.empty(T * k, dtype=torch.int32, device="cuda"),
+             inv_perm=torch.empty(T * k, dtype=torch.int32, device="cuda"))
+    apw.route(ctx(), dev(x), dev(wr), None, T, H, E, k, True, o["ids"], o["w"], o["counts"], o["offsets"],
+              o["perm"], o["inv_perm"])
+    torch.cuda.synchronize()
+    check_route(o, r)
+    assert np.any(np.isin(r["ids"], [2, 5, 7]))
+
+
+# --------------------------------------------------------------------------- format tools
+
+def test_lut_build_parity():
+    n = 300
+    # random finite fp16 patterns (subnormals, large magnitudes, exact ties) and a real parent
+    bits = RNG.integers(0, 0x7C00, (n // 2, 256)).astype(np.uint16)
+    bits |= (RNG.integers(0, 2, bits.shape).astype(np.uint16) << 15)
+    parent = np.concatenate([bits.view(np.float16), synth.gen_parent_lut_shape(5, 0, 0, 0, n - n // 2)])
+    pd = dev(parent)
+    levels = {b: torch.empty((n, 1 << b), dtype=torch.float16, device="cuda") for b in range(3, 8)}
+    apw.lut_build(ctx(), pd, n, levels)
+    torch.cuda.synchronize()
+    for b in range(3, 8):
+        ref = oracle.lut_level(parent, b).view(np.uint16)
+        got = host(levels[b]).view(np.uint16)
+        assert np.array_equal(got, ref), b
+
+
+def test_pack_planes_parity():
+    n, k = 77, 384
+    codes = RNG.integers(0, 256, (n, k)).astype(np.uint8)
+    planes = torch.empty((8, n, k // 32), dtype=torch.int32, device="cuda")
+    apw.pack_planes(ctx(), dev(codes), n, k, planes)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(planes).view(np.uint32), oracle.pack_planes(codes))
+
+
+# --------------------------------------------------------------------------- expert product
+
+def _gemm_setup(qs, counts, N, K, identity, seed):
+    """One layer, E = len(qs) experts, gate_up kind, given per-expert token counts."""
+    E = len(qs)
+    tbl = apw.Table(1, E)
+    keep = []
+    planes_np, luts_np = [], []
+    for e, q in enumerate(qs):
+        P = synth.gen_planes_shape(seed, 0, e, 0, N, K)
+        Pd = dev(P)
+        if identity:
+            lut = np.tile(np.arange(1 << q, dtype=np.float16), (N, 1))
+        else:
+            lut = oracle.lut_level(synth.gen_parent_lut_shape(seed, 0, e, 0, N), q)
+        Ld = dev(lut)
+        keep += [Pd, Ld]
+        planes_np.append(P)
+        luts_np.append(lut)
+        tbl.set_block(0, e, 0, N, K, q, [Pd[p] for p in range(8)], {q: Ld})
+        # the down slot must be present for a complete layer; reuse the same block
+        tbl.set_block(0, e, 1, N, K, q, [Pd[p] for p in range(8)], {q: Ld})
+    tbl.commit(ctx())
+    R = int(sum(counts))
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    T = R  # gather: topk = 1, a random permutation of tokens
+    perm = RNG.permutation(R).astype(np.int32)
+    return tbl, keep, planes_np, luts_np, offsets, perm, T
+
+
+def _gemm_run(tbl, x, offsets, perm, T, N, out_dtype, gather=True):
+    R = int(offsets[-1])
+    out = torch.full((R, N), float("nan"), dtype=torch.float32 if out_dtype == apw.F32 else torch.float16,
+                     device="cuda")
+    apw.gemm(ctx(), tbl, 0, apw.GATE_UP, dev(x), gather, dev(perm), dev(offsets), T, 1, out, out_dtype)
+    torch.cuda.synchronize()
+    return host(out)
+
+
+GEMM_QS = [3, 4, 5, 6, 7, 8]
+GEMM_COUNTS = [0, 1, 33, 70, 5, 31]
+
+
+@pytest.mark.parametrize("NK", [(136, 384), (64, 256), (200, 1024)])
+def test_gemm_identity_lut_exact(NK):
+    """Identity LUT + integer activations: every partial sum is an integer below
+    2^24, so the fp32 result must equal the integer matmul exactly."""
+    N, K = NK
+    tbl, keep, P, L, offsets, perm, T = _gemm_setup(GEMM_QS, GEMM_COUNTS, N, K, True, 41)
+    x = RNG.integers(-2, 3, (T, K)).astype(np.float16)
+    got = _gemm_run(tbl, x, offsets, perm, T, N, apw.F32)
+    for e, q in enumerate(GEMM_QS):
+        rows = perm[offsets[e]:offsets[e + 1]]
+        codes = oracle.unpack_codes(P[e], q).astype(np.int64)
+        ref = x[rows].astype(np.int64) @ codes.T
+        assert np.array_equal(got[offsets[e]:offsets[e + 1]], ref.astype(np.float32)), (e, q)
+    tbl.close()
+
+
+@pytest.mark.parametrize("out_dtype", [apw.F16, apw.F32])
+def test_gemm_random_lut(out_dtype):
+    N, K = 136, 384
+    tbl, keep, P, L, offsets, perm, T = _gemm_setup(GEMM_QS, GEMM_COUNTS, N, K, False, 42)
+    x = synth.gen_aux_fp16(42, 0, T * K).reshape(T, K)
+    got = _gemm_run(tbl, x, offsets, perm, T, N, out_dtype).astype(np.float64)
+    for e, q in enumerate(GEMM_QS):
+        rows = perm[offsets[e]:offsets[e + 1]]
+        if rows.size == 0:
+            continue
+        xin = x[rows].astype(np.float64)
+        ref = oracle.block_gemm(P[e], L[e], q, xin)
+        S = oracle.block_gemm(P[e], np.abs(L[e]), q, np.abs(xin))
+        acc = K * 2.0 ** -24 * S
+        tol = acc + (0.5 * ulp16(np.abs(ref) + acc) if out_dtype == apw.F16 else 0.0)
+        d = np.abs(got[offsets[e]:offsets[e + 1]] - ref)
+        assert np.all(d <= tol), (e, q, float((d - tol).max()))
+    tbl.close()
+
+
+def test_gemm_non_gather_rows():
+    N, K = 64, 256
+    tbl, keep, P, L, offsets, perm, T = _gemm_setup(GEMM_QS, GEMM_COUNTS, N, K, True, 43)
+    R = int(offsets[-1])
+    a = RNG.integers(-2, 3, (R, K)).astype(np.float16)
+    got = _gemm_run(tbl, a, offsets, perm, R, N, apw.F32, gather=False)
+    for e, q in enumerate(GEMM_QS):
+        codes = oracle.unpack_codes(P[e], q).astype(np.int64)
+        ref = a[offsets[e]:offsets[e + 1]].astype(np.int64) @ codes.T
+        assert np.array_equal(got[offsets[e]:offsets[e + 1]], ref.astype(np.float32))
+    tbl.close()
+
+
+# --------------------------------------------------------------------------- act / combine
+
+def test_act_parity():
+    R, F = 37, 1024
+    h = synth.gen_aux_fp16(7, 1, R * 2 * F, 2.0).reshape(R, 2 * F)
+    a = torch.empty((R, F), dtype=torch.float16, device="cuda")
+    apw.act(ctx(), dev(h), R, F, a)
+    torch.cuda.synchronize()
+    ref = oracle.act(h.astype(np.float64))
+    got = host(a).astype(np.float64)
+    # fp32 SiLU (relative error well below 1e-5) then one fp16 rounding
+    tol = 0.5 * ulp16(np.abs(ref) * (1 + 1e-5)) + 1e-5 * np.abs(ref) + 1e-7
+    assert np.all(np.abs(got - ref) <= tol)
+
+
+@pytest.mark.parametrize("y_dtype", [apw.F32, apw.F16])
+def test_combine_parity(y_dtype):
+    T, k, H = 19, 3, 512
+    R = T * k
+    y = synth.gen_aux_fp16(8, 2, R * H, 1.5).reshape(R, H)
+    yin = y.astype(np.float32) if y_dtype == apw.F32 else y
+    w = RNG.dirichlet(np.ones(k), T).astype(np.float32)
+    inv = RNG.permutation(R).astype(np.int32)
+    out = torch.empty((T, H), dtype=torch.float16, device="cuda")
+    apw.combine(ctx(), dev(yin), y_dtype, dev(w), dev(inv), T, k, H, out)
+    torch.cuda.synchronize()
+    ref = oracle.combine(y.astype(np.float64), w.astype(np.float64), inv, k)
+    got = host(out).astype(np.float64)
+    acc = k * 2.0 ** -24 * (np.abs(w).astype(np.float64)[:, :, None] *
+                             np.abs(y.astype(np.float64))[inv.reshape(T, k)]).sum(axis=1)
+    tol = 0.5 * ulp16(np.abs(ref) + acc) + acc
+    assert np.all(np.abs(got - ref) <= tol)
+
+
+# --------------------------------------------------------------------------- whole layer
+
+def test_layer_tiny_parity():
+    cfg = synth.CONFIGS[0]
+    assert topk_margin_ok(synth.gen_x(cfg), synth.gen_router(cfg), synth.gen_bias(cfg), cfg.topk)
+    L = Layer(cfg)
+    o = L.run()
+    fused = L.run_fused_call()
+    torch.cuda.synchronize()
+    r = L.oracle(intermediates=True)
+    check_route(o, r)
+    check_out(host(o["out"]), r["out"])
+    assert np.array_equal(host(fused).view(np.uint16), host(o["out"]).view(np.uint16))
+    # h: fp16 rounding of an fp32 accumulation of the exact products
+    H = cfg.hidden
+    h = host(o["h"]).astype(np.float64)
+    for e in range(cfg.experts):
+        s, t = r["offsets"][e], r["offsets"][e + 1]
+        if s == t:
+            continue
+        q = int(L.q[e, 0])
+        lut = oracle.lut_level(L.parent[(e, 0)], q)
+        xin = np.abs(L.x[r["perm"][s:t] // cfg.topk].astype(np.float64))
+        S = oracle.block_gemm(L.planes[(e, 0)], np.abs(lut), q, xin)
+        acc = H * 2.0 ** -24 * S
+        tol = 0.5 * ulp16(np.abs(r["h"][s:t]) + acc) + acc
+        assert np.all(np.abs(h[s:t] - r["h"][s:t]) <= tol), e
+
+
+@pytest.mark.parametrize("T", [1, 5, 13])
+def test_layer_tiny_ragged_tokens(T):
+    cfg = synth.CONFIGS[0]
+    L = Layer(cfg, T=T)
+    o = L.run()
+    torch.cuda.synchronize()
+    r = L.oracle()
+    check_route(o, r)
+    check_out(host(o["out"]), r["out"])
+
+
+def test_layer_zero_tokens():
+    cfg = synth.CONFIGS[0]
+    L = Layer(cfg, T=0)
+    out = L.run_fused_call()
+    torch.cuda.synchronize()
+    assert out.shape == (0, cfg.hidden)
+
+
+def test_deterministic_and_uniform_q():
+    """Two runs give identical bits; a uniform q map (the paper's uniform
+    APL-style baseline, Section 4) is the special case all blocks equal."""
+    cfg = synth.CONFIGS[0]
+    L = Layer(cfg, qmap=np.full((cfg.experts, 2), 4, np.int32))
+    a = host(L.run()["out"])
+    b = host(L.run()["out"])
+    assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+    check_out(a, L.oracle()["out"])
+
+
+def test_commit_between_launches():
+    """Section 3.3: q changes only at safe boundaries.  Launches enqueued before a
+    commit use the old q map, launches after it the new one, with no host sync."""
+    cfg = synth.CONFIGS[0]
+    qa = synth.gen_qmap(cfg)
+    qb = 11 - qa  # 3..8 -> 8..3
+    L = Layer(cfg, qmap=qa)
+    s = torch.cuda.current_stream()
+    o1 = L.run(s)
+    L.rw.stage_qmap(0, qb)
+    L.rw.commit(s)
+    o2 = L.run(s)
+    L.rw.stage_qmap(0, qa)
+    L.rw.commit(s)
+    o3 = L.run(s)
+    torch.cuda.synchronize()
+    check_out(host(o1["out"]), L.oracle(qmap=qa)["out"])
+    check_out(host(o2["out"]), L.oracle(qmap=qb)["out"])
+    assert np.array_equal(host(o1["out"]).view(np.uint16), host(o3["out"]).view(np.uint16))
+    assert not np.array_equal(host(o1["out"]).view(np.uint16), host(o2["out"]).view(np.uint16))
+    assert L.rw.table.committed_bits(0, 0, 0) == qa[0, 0]
+
+
+def test_planes_above_q_are_never_read():
+    """Section 3.1: after an offload lowers q, planes p >= q may leave the GPU.
+    Poisoned or absent planes above q must not change a single output bit."""
+    cfg = synth.CONFIGS[0]
+    L = Layer(cfg)
+    ref = host(L.run()["out"])
+    for (e, u), pt in L.rw.planes.items():
+        q = int(L.q[e, u])
+        if q < 8:
+            pt[q:].fill_(-1)
+    poisoned = host(L.run()["out"])
+    for (e, u) in list(L.rw.planes):
+        q = int(L.q[e, u])
+        for p in range(q, 8):
+            L.rw.table.set_plane(0, e, u, p, None, False)
+    L.rw.commit()
+    absent = host(L.run()["out"])
+    torch.cuda.synchronize()
+    assert np.array_equal(poisoned.view(np.uint16), ref.view(np.uint16))
+    assert np.array_equal(absent.view(np.uint16), ref.view(np.uint16))
+
+
+def test_gemm_rejects_uncommitted_and_bad_args():
+    cfg = synth.CONFIGS[0]
+    tbl = apw.Table(1, cfg.experts)
+    x = torch.zeros((4, cfg.hidden), dtype=torch.float16, device="cuda")
+    out = torch.zeros((8, 2 * cfg.ffn), dtype=torch.float16, device="cuda")
+    offs = torch.zeros(cfg.experts + 1, dtype=torch.int32, device="cuda")
+    with pytest.raises(apw.ApmoeError) as ex:
+        apw.gemm(ctx(), tbl, 0, apw.GATE_UP, x, True, offs, offs, 4, 2, out, apw.F16)
+    assert ex.value.status == apw.NOT_RESIDENT
+    L = Layer(cfg)
+    with pytest.raises(apw.ApmoeError) as ex:
+        apw.gemm(ctx(), L.rw.table, 0, apw.GATE_UP, x, True, offs, offs, 4, 2, out, 7)
+    assert ex.value.status == apw.UNSUPPORTED
+    with pytest.raises(apw.ApmoeError) as ex:
+        apw.gemm(ctx(), L.rw.table, 1, apw.GATE_UP, x, True, offs, offs, 4, 2, out, apw.F16)
+    assert ex.value.status == apw.INVALID_ARG
+    tbl.close()
+
+
+@pytest.mark.slow
+def test_layer_mixtral_decode_full_size():
+    """Mixtral-8x7B-shaped decode layer (T = 16), the benchmark's workload and
+    launch configuration; oracle on every token."""
+    cfg = synth.CONFIGS[1]
+    assert topk_margin_ok(synth.gen_x(cfg), synth.gen_router(cfg), None, cfg.topk)
+    L = Layer(cfg)
+    o = L.run()
+    fused = L.run_fused_call()
+    torch.cuda.synchronize()
+    r = L.oracle()
+    check_route(o, r)
+    ma, rl = check_out(host(o["out"]), r["out"])
+    print(f"mixtral decode T=16: max-abs {ma:.3e} rel-L2 {rl:.3e}", flush=True)
+    assert np.array_equal(host(fused).view(np.uint16), host(o["out"]).view(np.uint16))
