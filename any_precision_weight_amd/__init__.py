@@ -25,7 +25,7 @@ EXPORTED = [
     "apmoe_status_string", "apmoe_last_error", "apmoe_version", "apmoe_create", "apmoe_destroy",
     "apmoe_block_bytes", "apmoe_table_create", "apmoe_table_destroy", "apmoe_table_set_block",
     "apmoe_table_set_bits", "apmoe_table_set_plane", "apmoe_table_validate", "apmoe_table_committed_bits",
-    "apmoe_table_commit", "apmoe_lut_build", "apmoe_pack_planes", "apmoe_route", "apmoe_gemm", "apmoe_act",
+    "apmoe_table_commit", "apmoe_lut_build", "apmoe_tiled_plane_words", "apmoe_tile_planes", "apmoe_pack_planes", "apmoe_route", "apmoe_gemm", "apmoe_act",
     "apmoe_combine", "apmoe_moe_workspace", "apmoe_moe_forward",
 ]
 
@@ -86,6 +86,8 @@ def _declare(L):
         "apmoe_table_committed_bits": (S, [P, I32, I32, I32, ctypes.POINTER(I32)]),
         "apmoe_table_commit": (S, [P, P, P]),
         "apmoe_lut_build": (S, [P, P, I32, P, P]),
+        "apmoe_tiled_plane_words": (I64, [I32, I32]),
+        "apmoe_tile_planes": (S, [P, P, I32, I32, P, P]),
         "apmoe_pack_planes": (S, [P, P, I32, I32, P, P]),
         "apmoe_route": (S, [P, P, P, P, I32, I32, I32, I32, I32, P, P, P, P, P, P, P]),
         "apmoe_gemm": (S, [P, P, I32, I32, P, I32, P, P, I32, I32, P, I32, P]),
@@ -215,6 +217,15 @@ def lut_build(ctx: Context, parent, n: int, levels: dict, stream=None) -> None:
     arr = (ctypes.c_void_p * (MAX_BITS + 1))(*[ptr(levels.get(b)) for b in range(MAX_BITS + 1)])
     _check(lib().apmoe_lut_build(ctx.handle, ptr(parent), n, ctypes.cast(arr, ctypes.c_void_p),
                                  stream_handle(stream)), "apmoe_lut_build")
+
+
+def tiled_plane_words(n: int, k: int) -> int:
+    return int(lib().apmoe_tiled_plane_words(n, k))
+
+
+def tile_planes(ctx: Context, canonical, n: int, k: int, tiled, stream=None) -> None:
+    _check(lib().apmoe_tile_planes(ctx.handle, ptr(canonical), n, k, ptr(tiled), stream_handle(stream)),
+           "apmoe_tile_planes")
 
 
 def pack_planes(ctx: Context, codes, n: int, k: int, planes, stream=None) -> None:

@@ -444,6 +444,27 @@ apmoe_status apmoe_lut_build(apmoe_ctx *ctx, const uint16_t *parent, int32_t n, 
     return e == hipSuccess ? ok() : hip_fail(e, "lut_build launch");
 }
 
+int64_t apmoe_tiled_plane_words(int32_t n, int32_t k)
+{
+    if (n < 1 || k < 128 || k % 128 != 0)
+        return -1;
+    return (int64_t)apmoe::tiled_plane_words(n, k);
+}
+
+apmoe_status apmoe_tile_planes(apmoe_ctx *ctx, const uint32_t *canonical, int32_t n, int32_t k, uint32_t *tiled,
+                               void *stream)
+{
+    apmoe_status s = check_ctx(ctx);
+    if (s != APMOE_OK)
+        return s;
+    if (!canonical || !tiled)
+        return fail(APMOE_INVALID_ARG, "canonical / tiled is NULL");
+    if (n < 1 || k < 128 || k % 128 != 0)
+        return fail(APMOE_INVALID_ARG, "n=%d k=%d (need n>=1, k%%128==0)", n, k);
+    hipError_t e = apmoe::launch_tile_planes(canonical, n, k, tiled, reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ok() : hip_fail(e, "tile_planes launch");
+}
+
 apmoe_status apmoe_pack_planes(apmoe_ctx *ctx, const uint8_t *codes, int32_t n, int32_t k, uint32_t *planes,
                                void *stream)
 {

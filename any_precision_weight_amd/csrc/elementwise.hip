@@ -177,6 +177,36 @@ __global__ void __launch_bounds__(256) pack_planes_kernel(const uint8_t *__restr
         planes[((size_t)p * n + row) * kw + w] = out[p];
 }
 
+// Canonical planes uint32 [8][n][k/32] -> tiled planes, 8 x tiled_words(n, k).
+// Tile (rt, kt) of a plane covers rows 32rt..32rt+31 and columns 128kt..128kt+127
+// in 128 words; lane slot L = 32g + i holds row i, columns 64g..64g+63 in words
+// 2L (columns 64g..64g+31) and 2L+1.  Rows past n are zero.
+__global__ void __launch_bounds__(256) tile_planes_kernel(const uint32_t *__restrict__ canon, int n, int k,
+                                                          uint32_t *__restrict__ tiled, size_t plane_words)
+{
+    const int kw = k / 32, kt_count = k / 128, rt_count = (n + 31) / 32;
+    const size_t per_plane = (size_t)rt_count * kt_count * 64;  // lane slots per plane
+    const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= 8 * per_plane)
+        return;
+    const int p = (int)(idx / per_plane);
+    const size_t rem = idx % per_plane;
+    const size_t tile = rem / 64;
+    const int L = (int)(rem % 64);
+    const int rt = (int)(tile / kt_count), kt = (int)(tile % kt_count);
+    const int i = L & 31, g = L >> 5;
+    const int row = 32 * rt + i;
+    uint32_t w0 = 0, w1 = 0;
+    if (row < n) {
+        const uint32_t *src = canon + ((size_t)p * n + row) * kw + 4 * kt + 2 * g;
+        w0 = src[0];
+        w1 = src[1];
+    }
+    uint32_t *dst = tiled + (size_t)p * plane_words + tile * 128 + 2 * L;
+    dst[0] = w0;
+    dst[1] = w1;
+}
+
 inline unsigned blocks_for(size_t work, unsigned threads) { return (unsigned)((work + threads - 1) / threads); }
 
 }  // namespace
@@ -213,6 +243,17 @@ hipError_t launch_lut_build(const uint16_t *parent, int n, uint16_t *const *leve
     for (int b = 0; b <= APMOE_MAX_BITS; ++b)
         L.lv[b] = (b >= 3 && b <= 7) ? levels[b] : nullptr;
     hipLaunchKernelGGL(lut_build_kernel, dim3(blocks_for((size_t)n, 256)), dim3(256), 0, s, parent, n, L);
+    return hipGetLastError();
+}
+
+hipError_t launch_tile_planes(const uint32_t *canon, int n, int k, uint32_t *tiled, hipStream_t s)
+{
+    const size_t per_plane = (size_t)((n + 31) / 32) * (k / 128) * 64;
+    const size_t work = 8 * per_plane;
+    if (work == 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(tile_planes_kernel, dim3(blocks_for(work, 256)), dim3(256), 0, s, canon, n, k, tiled,
+                       per_plane * 2);
     return hipGetLastError();
 }
 

@@ -8,14 +8,16 @@
 //   code_q(n, c) = bits of planes 0..q-1 at column c, plane 0 most significant.
 //
 // Workgroup = 4 waves = 64 weight rows of one expert.  Wave w covers rows
-// 32*(w&1) .. +31 and every other 256-column step (w>>1 picks the half); the two
-// halves are summed through LDS at the end.  For each step a lane loads, for its
-// row, one 16-byte word group of each of the q needed planes (128 columns; only
-// planes p < q are touched), turns them into 8-bit codes with an 8x8 bit
-// transpose, looks the codes up in the row's LUT level q staged in LDS, and feeds
-// the fp16 centroids as the A operand of v_mfma_f32_32x32x16_f16 against up to 32
-// tokens (B operand).  The reduction over columns is a sum, so the order in
-// which columns are assigned to MFMA k-slots is free as long as A and B agree.
+// 32*(w&1) .. +31 and every other 128-column step (w>>1 picks the half); the two
+// halves are summed through LDS at the end.  Planes are read in the tiled layout
+// (32-row x 128-column tiles of 512 bytes, one tile per wave step and plane).  For
+// each step a lane loads, for its row, two words (64 columns) of each of the q
+// needed planes (only planes p < q are touched), turns them into 8-bit codes with an 8x8 bit transpose, looks the
+// codes up in the row's LUT level q staged in LDS, and feeds the fp16 centroids as
+// the A operand of v_mfma_f32_32x32x16_f16 against up to 32 tokens (B operand).
+// The reduction over columns is a sum, so the order in which columns are assigned
+// to MFMA k-slots is free as long as A and B agree.  Plane words of the next step
+// and B fragments of the next word are requested ahead of use.
 //
 // LDS LUT layout (bank-conflict-free gathers): the transposed code byte v has
 // bit p = plane p's bit, i.e. v is the q-bit code with its bits reversed; entry
@@ -31,11 +33,17 @@ namespace {
 constexpr int kWave = 64;
 constexpr int kThreads = 256;
 constexpr int kRows = kGemmRowsPerBlock;  // 64
-constexpr int kStepCols = 256;            // columns per wave step (2 lane halves x 128)
+constexpr int kStepCols = 128;            // columns per wave step (2 lane halves x 64)
 constexpr int kTokTile = 32;
+constexpr int kLutBytes = 32 * 1024;                       // LUT region, every q
+constexpr int kRedBytes = 2 * 16 * kWave * sizeof(float);  // column-half reduction
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float float16v __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef const __attribute__((address_space(1))) u32x2 *gptr2;
+typedef const __attribute__((address_space(1))) u32x4 *gptr4;
 
 __device__ inline uint32_t bitrev(uint32_t c, int q) { return __builtin_bitreverse32(c) >> (32 - q); }
 
@@ -71,98 +79,108 @@ struct GemmParams {
     const int32_t *offsets;
     void *out;
     int kind, E, N, K, topk, gather, out_f32, row_blocks;
-    int lut_bytes;  // bytes of the LUT region (also the offset of the reduction buffer)
 };
 
-// One wave's share of a 32-token pass over this block's columns.
+// Plane bases are wave-uniform (scalar registers); the per-lane part is a 32-bit
+// word offset into the tiled plane, so each load is one global_load_dwordx2 with a
+// scalar base and a wave reads 512 contiguous bytes per plane.
 template <int Q>
-__device__ inline void wave_product(const GemmParams &P, const DevBlock &blk, uint32_t lut_base, int n_row,
-                                    bool row_ok, const uint16_t *tok_row, bool tok_ok, int half, uint32_t lane_const,
-                                    float16v &acc)
+__device__ inline void load_planes(u32x2 (&w)[Q], const DevBlock &blk, uint32_t word)
 {
-    const int lane = threadIdx.x % kWave;
-    const int g = lane >> 5;
-    const int K = P.K;
-    const int Kw = K / 32;
-    const int nsteps = (K + kStepCols - 1) / kStepCols;
-    const uint32_t *pl[Q];
 #pragma unroll
     for (int p = 0; p < Q; ++p)
-        pl[p] = blk.plane[p] + (size_t)n_row * Kw;
+        w[p] = *(gptr2)(blk.plane[p] + word);
+}
 
-    for (int step = half; step < nsteps; step += 2) {
-        const int col0 = step * kStepCols + 128 * g;
-        const bool k_ok = col0 < K;
-        uint4 w[Q];
+__device__ inline void load_x_group(u32x4 (&xg)[4], gptr4 p)
+{
 #pragma unroll
-        for (int p = 0; p < Q; ++p)
-            w[p] = (row_ok && k_ok) ? *reinterpret_cast<const uint4 *>(pl[p] + col0 / 32) : make_uint4(0, 0, 0, 0);
-        // all 16 B-operand fragments of this step are requested up front, next to the planes
-        const uint16_t *xb = tok_row + col0;
-        const bool x_ok = tok_ok && k_ok;
-        uint4 xv[16];
+    for (int f = 0; f < 4; ++f)
+        xg[f] = p[f];
+}
+
+// 4 MFMAs over one 32-column word of each needed plane: unpack, LUT gather, multiply.
+template <int Q, int W>
+__device__ inline void group_product(const u32x2 (&w)[Q], const u32x4 (&xg)[4], uint32_t lut_base,
+                                     uint32_t lane_const, float16v &acc)
+{
+    uint32_t d[8];
 #pragma unroll
-        for (int f = 0; f < 16; ++f)
-            xv[f] = x_ok ? *reinterpret_cast<const uint4 *>(xb + 8 * f) : make_uint4(0, 0, 0, 0);
+    for (int p = 0; p < 8; ++p)
+        d[p] = p < Q ? w[p < Q ? p : 0][W] : 0u;
+    transpose8x8(d);
 #pragma unroll
-        for (int w4 = 0; w4 < 4; ++w4) {
-            uint32_t d[8];
+    for (int b = 0; b < 4; ++b) {
+        half8 a;
 #pragma unroll
-            for (int p = 0; p < 8; ++p) {
-                if (p < Q) {
-                    const uint4 v = w[p < Q ? p : 0];
-                    d[p] = w4 == 0 ? v.x : w4 == 1 ? v.y : w4 == 2 ? v.z : v.w;
-                } else {
-                    d[p] = 0u;
-                }
-            }
-            transpose8x8(d);
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                half8 a;
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    uint32_t addr;
-                    if (Q < 8)
-                        addr = __builtin_amdgcn_perm(d[j], lane_const, 0x0C0C0000u | ((4u + b) << 8));
-                    else
-                        addr = (((d[j] >> (8 * b)) & 0xFFu) << 7) | lane_const;
-                    a[j] = *reinterpret_cast<const __attribute__((address_space(3))) _Float16 *>(
-                        (uintptr_t)(lut_base + addr));
-                }
-                const half8 bx = __builtin_bit_cast(half8, xv[4 * w4 + b]);
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bx, acc, 0, 0, 0);
-            }
+        for (int j = 0; j < 8; ++j) {
+            uint32_t addr;
+            if (Q < 8)
+                addr = __builtin_amdgcn_perm(d[j], lane_const, 0x0C0C0000u | ((4u + b) << 8));
+            else
+                addr = (((d[j] >> (8 * b)) & 0xFFu) << 7) | lane_const;
+            a[j] = *reinterpret_cast<const __attribute__((address_space(3))) _Float16 *>((uintptr_t)(lut_base + addr));
         }
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, __builtin_bit_cast(half8, xg[b]), acc, 0, 0, 0);
     }
 }
 
 template <int Q>
-__device__ void gemm_block(const GemmParams &P, const DevBlock &blk, int e, int rb, int r0, int Me, char *smem)
+__device__ void gemm_block(const GemmParams &P, const DevBlock &blk, int rb, int r0, int Me, char *smem)
 {
     const int tid = threadIdx.x;
     const int lane = tid % kWave, wave = tid / kWave;
     const int t = wave & 1, half = wave >> 1;
     const int i = lane & 31, g = lane >> 5;
-    const int N = P.N;
+    const int N = P.N, K = P.K;
     const int n0 = rb * kRows;
+    const int nsteps = K / kStepCols;  // K % 128 == 0
+    const int n_row = n0 + 32 * t + i;
+    const bool row_ok = n_row < N;
+    // tiled planes: tile (rt, kt) = rows 32rt.., columns 128kt.., 128 words; this lane
+    // reads words 2*lane, 2*lane+1 of each tile.  A row tile past the end (N % 64 in
+    // (0, 32]) reads tile row 0; its outputs are not written.
+    const int RT = (N + 31) / 32, KT = K / kStepCols;
+    const int rt = 2 * rb + t;
+    const uint32_t lane_word = ((uint32_t)(rt < RT ? rt : 0) * (uint32_t)KT + (uint32_t)half) * 128u + 2u * lane;
+    constexpr uint32_t kNextWords = 2 * 128;  // this wave's next step: two tiles on
 
-    // ---- stage LUT level Q of rows n0..n0+63 into LDS -------------------------
-    {
-        const uint16_t *lut = blk.lut + (size_t)n0 * (1u << Q);
-        const int total = kRows << Q;
-        for (int idx = tid; idx < total; idx += kThreads) {
-            const int nl = idx >> Q, c = idx & ((1 << Q) - 1);
-            if (n0 + nl >= N)
-                continue;
-            const uint16_t v = lut[idx];
-            const uint32_t vp = bitrev((uint32_t)c, Q);
+    // ---- LUT level Q of rows n0..n0+63: 16-byte loads (8 entries of one row),
+    //      lane -> row so that one wave touches 64 rows ----------------------------
+    constexpr int kLutU4 = (kRows << Q) / 8;
+    constexpr int kPer = (kLutU4 + kThreads - 1) / kThreads;
+    constexpr int kBatch = kPer < 4 ? kPer : 4;  // loads in flight per batch (register budget)
+    u32x2 wc[Q];
+#pragma unroll
+    for (int j0 = 0; j0 < kPer; j0 += kBatch) {
+        u32x4 lv[kBatch];
+#pragma unroll
+        for (int jj = 0; jj < kBatch; ++jj) {
+            const int idx = tid + (j0 + jj) * kThreads;
+            const int nl = idx % kRows, ch = idx / kRows;
+            const bool ok = idx < kLutU4 && n0 + nl < N;
+            lv[jj] = ok ? *(gptr4)(blk.lut + ((size_t)(n0 + nl) << Q) + 8 * ch) : u32x4{0, 0, 0, 0};
+        }
+        // first step's planes are requested before the LUT lands in LDS
+        if (j0 == 0)
+            load_planes<Q>(wc, blk, lane_word);
+#pragma unroll
+        for (int jj = 0; jj < kBatch; ++jj) {
+            const int idx = tid + (j0 + jj) * kThreads;
+            if (idx >= kLutU4)
+                break;
+            const int nl = idx % kRows, ch = idx / kRows;
             const int il = nl & 31, tl = nl >> 5;
-            if (Q < 8) {
-                *reinterpret_cast<uint16_t *>(smem + vp * 256 + 4 * il + 2 * tl) = v;
-                *reinterpret_cast<uint16_t *>(smem + vp * 256 + 4 * (32 + il) + 2 * tl) = v;
-            } else {
-                *reinterpret_cast<uint16_t *>(smem + vp * 128 + 4 * il + 2 * tl) = v;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint16_t v = (uint16_t)(lv[jj][e >> 1] >> (16 * (e & 1)));
+                const uint32_t vp = bitrev((uint32_t)(8 * ch + e), Q);
+                if (Q < 8) {
+                    *reinterpret_cast<uint16_t *>(smem + vp * 256 + 4 * il + 2 * tl) = v;
+                    *reinterpret_cast<uint16_t *>(smem + vp * 256 + 4 * (32 + il) + 2 * tl) = v;
+                } else {
+                    *reinterpret_cast<uint16_t *>(smem + vp * 128 + 4 * il + 2 * tl) = v;
+                }
             }
         }
     }
@@ -171,24 +189,40 @@ __device__ void gemm_block(const GemmParams &P, const DevBlock &blk, int e, int 
     // LDS byte address of the region (a compile-time constant for the static array)
     const uint32_t lds_base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char *)smem);
     const uint32_t lane_const = (Q < 8) ? (uint32_t)(4 * (32 * g + i) + 2 * t) : (uint32_t)(4 * i + 2 * t);
-    const int n_row = n0 + 32 * t + i;
-    const bool row_ok = n_row < N;
-    float *red = reinterpret_cast<float *>(smem + P.lut_bytes);
+    float *red = reinterpret_cast<float *>(smem + kLutBytes);
 
     for (int tp = 0; tp < Me; tp += kTokTile) {
         const int j = lane & 31;  // token of this lane in the B operand
         const bool tok_ok = tp + j < Me;
-        const uint16_t *tok_row = P.in;
-        if (tok_ok) {
-            const int r = r0 + tp + j;
-            const int src = P.gather ? P.perm[r] / P.topk : r;
-            tok_row = P.in + (size_t)src * P.K;
-        }
+        // lanes past the last token read the last token's row: their D columns are discarded
+        const int r = r0 + min(tp + j, Me - 1);
+        const int src = P.gather ? P.perm[r] / P.topk : r;
+        gptr4 xp = (gptr4)(P.in + (size_t)src * K + half * kStepCols + 64 * g);
+        if (tp > 0)
+            load_planes<Q>(wc, blk, lane_word);
         float16v acc;
 #pragma unroll
         for (int v = 0; v < 16; ++v)
             acc[v] = 0.f;
-        wave_product<Q>(P, blk, lds_base, n_row, row_ok, tok_row, tok_ok, half, lane_const, acc);
+        // B-operand groups (4 fragments = 32 columns) are double-buffered and requested
+        // one group ahead, continuing across steps; planes are requested one step ahead.
+        u32x4 xa[4], xb[4];
+        load_x_group(xa, xp);
+        uint32_t word = lane_word;
+        for (int step = half; step < nsteps; step += 2) {
+            const bool more = step + 2 < nsteps;
+            u32x2 wn[Q];
+            word += more ? kNextWords : 0u;
+            load_planes<Q>(wn, blk, word);
+            load_x_group(xb, xp + 4);
+            group_product<Q, 0>(wc, xa, lds_base, lane_const, acc);
+            xp += more ? 2 * kStepCols / 8 : 0;  // 8 fp16 per u32x4
+            load_x_group(xa, xp);
+            group_product<Q, 1>(wc, xb, lds_base, lane_const, acc);
+#pragma unroll
+            for (int p = 0; p < Q; ++p)
+                wc[p] = wn[p];
+        }
 
         // ---- sum the two column halves, write rows of this pass ------------------
         if (half == 1) {
@@ -221,10 +255,7 @@ __device__ void gemm_block(const GemmParams &P, const DevBlock &blk, int e, int 
     }
 }
 
-constexpr int kLutBytes = 32 * 1024;                       // LUT region, every q
-constexpr int kRedBytes = 2 * 16 * kWave * sizeof(float);  // column-half reduction
-
-__global__ void __launch_bounds__(kThreads) gemm_kernel(GemmParams P)
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) gemm_kernel(GemmParams P)
 {
     __shared__ __attribute__((aligned(16))) char smem[kLutBytes + kRedBytes];
     const int e = blockIdx.x % P.E;
@@ -235,12 +266,12 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(GemmParams P)
         return;  // expert without tokens: no weight reads
     const DevBlock blk = P.table[2 * e + P.kind];
     switch (blk.q) {
-    case 3: gemm_block<3>(P, blk, e, rb, r0, Me, smem); break;
-    case 4: gemm_block<4>(P, blk, e, rb, r0, Me, smem); break;
-    case 5: gemm_block<5>(P, blk, e, rb, r0, Me, smem); break;
-    case 6: gemm_block<6>(P, blk, e, rb, r0, Me, smem); break;
-    case 7: gemm_block<7>(P, blk, e, rb, r0, Me, smem); break;
-    case 8: gemm_block<8>(P, blk, e, rb, r0, Me, smem); break;
+    case 3: gemm_block<3>(P, blk, rb, r0, Me, smem); break;
+    case 4: gemm_block<4>(P, blk, rb, r0, Me, smem); break;
+    case 5: gemm_block<5>(P, blk, rb, r0, Me, smem); break;
+    case 6: gemm_block<6>(P, blk, rb, r0, Me, smem); break;
+    case 7: gemm_block<7>(P, blk, rb, r0, Me, smem); break;
+    case 8: gemm_block<8>(P, blk, rb, r0, Me, smem); break;
     default: break;  // unreachable: commit validates q
     }
 }
@@ -251,6 +282,7 @@ hipError_t launch_gemm(const DevBlock *table, int kind, int E, int N, int K, int
                        int gather, const int32_t *perm, const int32_t *offsets, int topk, void *out, int out_f32,
                        hipStream_t s)
 {
+    (void)max_q;
     GemmParams P;
     P.table = table;
     P.in = in;
@@ -265,8 +297,6 @@ hipError_t launch_gemm(const DevBlock *table, int kind, int E, int N, int K, int
     P.gather = gather;
     P.out_f32 = out_f32;
     P.row_blocks = (N + kRows - 1) / kRows;
-    P.lut_bytes = kLutBytes;
-    (void)max_q;
     hipLaunchKernelGGL(gemm_kernel, dim3(P.row_blocks * E), dim3(kThreads), 0, s, P);
     return hipGetLastError();
 }

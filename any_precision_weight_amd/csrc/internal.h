@@ -9,7 +9,8 @@
 namespace apmoe {
 
 // One committed linear-block as the kernels see it (device table entry).
-// plane[p] is valid for p < q; lut points at level q, fp16 [n][2^q].
+// plane[p] (tiled layout, see apmoe_tile_planes) is valid for p < q; lut points at
+// level q, fp16 [n][2^q].
 struct DevBlock {
     const uint32_t *plane[APMOE_PLANES];
     const uint16_t *lut;
@@ -21,6 +22,9 @@ struct DevBlock {
 
 // Rows of the weight matrix handled by one workgroup of the decode product.
 constexpr int kGemmRowsPerBlock = 64;
+
+// Words of one tiled plane: 32-row x 128-column tiles of 128 words.
+inline size_t tiled_plane_words(int n, int k) { return (size_t)((n + 31) / 32) * (k / 128) * 128; }
 
 hipError_t launch_route_topk(const uint16_t *x, const uint16_t *wr, const float *bias, int T, int H, int E, int topk,
                              int renormalize, int32_t *ids, float *w, hipStream_t s);
@@ -36,6 +40,7 @@ hipError_t launch_act(const uint16_t *h, int R, int F, uint16_t *a, hipStream_t 
 hipError_t launch_combine(const void *y, int y_f32, const float *w, const int32_t *inv_perm, int T, int topk, int H,
                           uint16_t *out, hipStream_t s);
 hipError_t launch_lut_build(const uint16_t *parent, int n, uint16_t *const *levels, hipStream_t s);
+hipError_t launch_tile_planes(const uint32_t *canon, int n, int k, uint32_t *tiled, hipStream_t s);
 hipError_t launch_pack_planes(const uint8_t *codes, int n, int k, uint32_t *planes, hipStream_t s);
 
 }  // namespace apmoe

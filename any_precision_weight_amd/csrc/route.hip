@@ -13,7 +13,6 @@ namespace apmoe {
 namespace {
 
 constexpr int kWave = 64;
-constexpr int kTokensPerBlock = 4;
 
 __device__ inline double h2d(uint16_t h) { return (double)__builtin_bit_cast(_Float16, h); }
 
@@ -23,63 +22,56 @@ __device__ inline bool better(double za, int ea, double zb, int eb)
     return (za > zb) || (za == zb && ea < eb);
 }
 
-__global__ void __launch_bounds__(256) route_topk_kernel(const uint16_t *__restrict__ x,
-                                                         const uint16_t *__restrict__ wr,
-                                                         const float *__restrict__ bias, int T, int H, int E,
-                                                         int topk, int renormalize, int32_t *__restrict__ ids,
-                                                         float *__restrict__ wout)
-{
-    __shared__ double zs[kTokensPerBlock][APMOE_MAX_EXPERTS];
-    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-    const int t = blockIdx.x * kTokensPerBlock + wave;
-    if (t >= T)
-        return;  // no block-wide barrier below
-    const uint16_t *xr = x + (size_t)t * H;
+// One workgroup per token.  Thread (e, c) sums chunk c of expert e's dot product
+// over 8-column units c, c + nch, c + 2*nch, ...; expert e's logit is then the sum of
+// its nch partial sums in ascending c.  Every expert uses the same order.
+constexpr int kRouteThreads = 256;
 
-    for (int e0 = 0; e0 < E; e0 += 8) {
-        double acc[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            acc[j] = 0.0;
-        for (int h = lane * 8; h < H; h += kWave * 8) {
-            const uint4 xv = *reinterpret_cast<const uint4 *>(xr + h);
-            double xd[8];
+__global__ void __launch_bounds__(kRouteThreads) route_topk_kernel(const uint16_t *__restrict__ x,
+                                                                   const uint16_t *__restrict__ wr,
+                                                                   const float *__restrict__ bias, int T, int H,
+                                                                   int E, int topk, int renormalize,
+                                                                   int32_t *__restrict__ ids,
+                                                                   float *__restrict__ wout)
+{
+    __shared__ double part[kRouteThreads];
+    __shared__ double zs[APMOE_MAX_EXPERTS];
+    const int tid = threadIdx.x;
+    const int t = blockIdx.x;
+    int nch = 1;
+    while (nch * 2 * E <= kRouteThreads)
+        nch *= 2;
+    const int units = H / 8;
+    const uint16_t *xr = x + (size_t)t * H;
+    if (tid < E * nch) {
+        const int e = tid / nch, c = tid % nch;
+        const uint16_t *wrow = wr + (size_t)e * H;
+        double acc = 0.0;
+#pragma unroll 4
+        for (int u = c; u < units; u += nch) {
+            const uint4 xv = *reinterpret_cast<const uint4 *>(xr + 8 * u);
+            const uint4 wv = *reinterpret_cast<const uint4 *>(wrow + 8 * u);
             const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+            const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                xd[2 * i] = h2d((uint16_t)(xw[i] & 0xFFFFu));
-                xd[2 * i + 1] = h2d((uint16_t)(xw[i] >> 16));
-            }
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                if (e0 + j < E) {
-                    const uint4 wv = *reinterpret_cast<const uint4 *>(wr + (size_t)(e0 + j) * H + h);
-                    const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        acc[j] += xd[2 * i] * h2d((uint16_t)(ww[i] & 0xFFFFu));
-                        acc[j] += xd[2 * i + 1] * h2d((uint16_t)(ww[i] >> 16));
-                    }
-                }
+                acc += h2d((uint16_t)(xw[i] & 0xFFFFu)) * h2d((uint16_t)(ww[i] & 0xFFFFu));
+                acc += h2d((uint16_t)(xw[i] >> 16)) * h2d((uint16_t)(ww[i] >> 16));
             }
         }
-        // butterfly over the wave; lane 0's result is the logit (same order for every expert)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-#pragma unroll
-            for (int off = 32; off >= 1; off >>= 1)
-                acc[j] += __shfl_xor(acc[j], off, kWave);
-        }
-        if (lane == 0) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                if (e0 + j < E)
-                    zs[wave][e0 + j] = acc[j] + (bias ? (double)bias[e0 + j] : 0.0);
-        }
+        part[tid] = acc;
     }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    __syncthreads();
+    for (int e = tid; e < E; e += kRouteThreads) {
+        double z = 0.0;
+        for (int c = 0; c < nch; ++c)
+            z += part[e * nch + c];
+        zs[e] = z + (bias ? (double)bias[e] : 0.0);
+    }
+    __syncthreads();
+    if (tid >= kWave)
+        return;
+    const int lane = tid;
 
     // top-k: each lane owns experts lane, lane+64, ...
     unsigned taken = 0;  // bit i: expert lane + 64*i selected
@@ -92,7 +84,7 @@ __global__ void __launch_bounds__(256) route_topk_kernel(const uint16_t *__restr
             const int e = i * kWave + lane;
             if (taken & (1u << i))
                 continue;
-            const double z = zs[wave][e];
+            const double z = zs[e];
             if (be == 0x7FFFFFFF || better(z, e, bz, be)) {
                 bz = z;
                 be = e;
@@ -120,7 +112,7 @@ __global__ void __launch_bounds__(256) route_topk_kernel(const uint16_t *__restr
                 den += exp(zsel[j] - zmax);
         } else {
             for (int e = 0; e < E; ++e)
-                den += exp(zs[wave][e] - zmax);
+                den += exp(zs[e] - zmax);
         }
         for (int j = 0; j < topk; ++j) {
             ids[(size_t)t * topk + j] = esel[j];
@@ -217,9 +209,8 @@ hipError_t launch_route_topk(const uint16_t *x, const uint16_t *wr, const float 
 {
     if (T <= 0)
         return hipSuccess;
-    const int blocks = (T + kTokensPerBlock - 1) / kTokensPerBlock;
-    hipLaunchKernelGGL(route_topk_kernel, dim3(blocks), dim3(kTokensPerBlock * kWave), 0, s, x, wr, bias, T, H, E,
-                       topk, renormalize, ids, w);
+    hipLaunchKernelGGL(route_topk_kernel, dim3(T), dim3(kRouteThreads), 0, s, x, wr, bias, T, H, E, topk,
+                       renormalize, ids, w);
     return hipGetLastError();
 }
 

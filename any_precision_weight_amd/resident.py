@@ -16,7 +16,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import DOWN, GATE_UP, Context, Table, lut_build
+from . import DOWN, GATE_UP, Context, Table, lut_build, tile_planes, tiled_plane_words
 
 
 class ResidentWeights:
@@ -32,13 +32,17 @@ class ResidentWeights:
     # -- upload -----------------------------------------------------------------
     def add_block(self, layer: int, expert: int, kind: int, planes: np.ndarray | torch.Tensor,
                   parent_lut: np.ndarray | torch.Tensor, q: int) -> None:
-        """planes uint32 [8][N][K/32] and parent LUT fp16 [N][256], host or device."""
+        """planes: canonical uint32 [8][N][K/32] (host or device) -- rearranged on the
+        device into the tiled layout the kernels read; parent LUT fp16 [N][256]."""
         if isinstance(planes, np.ndarray):
-            pt = torch.from_numpy(np.ascontiguousarray(planes).view(np.int32)).to(self.device)
+            canon = torch.from_numpy(np.ascontiguousarray(planes).view(np.int32)).to(self.device)
         else:
-            pt = planes.to(self.device).contiguous()
-        _, N, W = pt.shape
+            canon = planes.to(self.device).contiguous()
+        _, N, W = canon.shape
         K = W * 32
+        pt = torch.empty((8, tiled_plane_words(N, K)), dtype=torch.int32, device=self.device)
+        tile_planes(self.ctx, canon, N, K, pt)
+        del canon
         if isinstance(parent_lut, np.ndarray):
             l8 = torch.from_numpy(np.ascontiguousarray(parent_lut, dtype=np.float16)).to(self.device)
         else:

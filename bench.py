@@ -137,6 +137,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--copies", type=int, default=2, help="resident weight copies rotated between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="also run one plain device copy of MIB MiB (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (--gpus {args.gpus} requested); "
@@ -155,6 +157,13 @@ def main() -> int:
             L.step(i % args.copies)
         torch.cuda.synchronize()
         counts = L.b["counts"].cpu().numpy()
+        if args.copy_calibration:
+            n = args.copy_calibration << 20
+            src = torch.empty(n, dtype=torch.uint8, device="cuda")
+            dst = torch.empty_like(src)
+            dst.copy_(src)
+            torch.cuda.synchronize()
+            del src, dst
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
         t_start = torch.cuda.Event(enable_timing=True)
         t_end = torch.cuda.Event(enable_timing=True)

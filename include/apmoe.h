@@ -21,8 +21,11 @@
  * Format conventions (readings of the paper where it is silent):
  *   - 8 parent planes.  Plane p holds bit (7 - p) of the 8-bit parent code, so a
  *     q-bit block reads planes 0..q-1 and its code is the parent code >> (8 - q).
- *   - Plane p of an n x k block is uint32 [n][k/32]; bit j of word w is column
- *     32*w + j.
+ *   - Canonical plane layout: plane p of an n x k block is uint32 [n][k/32]; bit j
+ *     of word w is column 32*w + j.
+ *   - Device plane layout read by the kernels ("tiled"): apmoe_tile_planes
+ *     rearranges the canonical words of each plane into 32-row x 128-column tiles
+ *     of 512 bytes, so one wave reads whole contiguous cache lines.
  *   - The LUT is per output row: level b is fp16 [n][2^b], entry [row][code].
  *   - gate_up is [2F x H] with rows [0, F) the gate and [F, 2F) the up
  *     projection; down is [H x F].  Activation is SiLU(gate) * up.
@@ -81,8 +84,9 @@ typedef struct apmoe_table apmoe_table;
  *   q             : committed bitwidth to publish, 3..8 (the paper's q_i).
  *   d             : desired bitwidth (the paper's d_i); stored, never read by kernels.
  *   resident_mask : bit p set when plane[p] holds valid device data.
- *   plane[p]      : device uint32 [n][k/32], code bit (7 - p); may be NULL when not
- *                   resident.
+ *   plane[p]      : device plane p (code bit 7 - p) in the tiled layout of
+ *                   apmoe_tile_planes, apmoe_tiled_plane_words(n, k) words; may be
+ *                   NULL when not resident.
  *   lut[b]        : device fp16 [n][2^b] for b = 3..8; lut[0..2] are ignored.
  * A commit of this block requires planes 0..q-1 resident and non-NULL and lut[q]
  * non-NULL.  Planes p >= q and other LUT levels are never read by the kernels.
@@ -170,7 +174,20 @@ apmoe_status apmoe_table_commit(apmoe_ctx *ctx, apmoe_table *tbl, void *stream);
 apmoe_status apmoe_lut_build(apmoe_ctx *ctx, const uint16_t *parent, int32_t n, uint16_t *const *levels,
                              void *stream);
 
-/* Pack parent codes (uint8 [n][k], device) into 8 planes (uint32 [8][n][k/32]). */
+/* Words of one plane of an n x k block in the tiled layout (-1 for bad shapes):
+ * ceil(n/32) * (k/128) tiles of 128 words.  Host only. */
+int64_t apmoe_tiled_plane_words(int32_t n, int32_t k);
+
+/* Rearrange canonical planes (uint32 [8][n][k/32], device) into the tiled layout:
+ * plane p occupies tiled[p * W .. (p+1) * W), W = apmoe_tiled_plane_words(n, k).
+ * Tile (rt, kt) of a plane starts at word 128 * (rt * (k/128) + kt) and covers rows
+ * 32rt..32rt+31 and columns 128kt..128kt+127; inside it, words 2L and 2L+1 with
+ * L = 32g + i hold row 32rt+i, columns 128kt+64g .. +31 and +32 .. +63 (canonical
+ * bit order).  Rows past n are zero.  k % 128 == 0. */
+apmoe_status apmoe_tile_planes(apmoe_ctx *ctx, const uint32_t *canonical, int32_t n, int32_t k, uint32_t *tiled,
+                               void *stream);
+
+/* Pack parent codes (uint8 [n][k], device) into 8 canonical planes (uint32 [8][n][k/32]). */
 apmoe_status apmoe_pack_planes(apmoe_ctx *ctx, const uint8_t *codes, int32_t n, int32_t k, uint32_t *planes,
                                void *stream);
 

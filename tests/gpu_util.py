@@ -127,7 +127,7 @@ def check_route(o_gpu: dict, r: dict) -> None:
     assert np.array_equal(host(o_gpu["perm"]), r["perm"])
     assert np.array_equal(host(o_gpu["inv_perm"]), r["inv_perm"])
     dw = np.abs(host(o_gpu["w"]).astype(np.float64) - r["w32"].astype(np.float64))
-    assert dw.max() <= 1e-6, dw.max()
+    assert dw.size == 0 or dw.max() <= 1e-6, dw.max()
 
 
 def check_out(out_gpu: np.ndarray, out_ref: np.ndarray, max_abs=1e-2, rel_l2=2e-3) -> tuple[float, float]:

@@ -99,6 +99,29 @@ def test_lut_build_parity():
         assert np.array_equal(got, ref), b
 
 
+def _tiled_numpy(P):
+    """The documented tiled layout, written independently with numpy reshapes:
+    tiles of 32 rows x 128 columns; slot L = 32g + i holds row i, 2 words for
+    columns 64g..64g+63."""
+    _, N, W = P.shape
+    RT, KT = (N + 31) // 32, W // 4
+    pad = np.zeros((8, RT * 32, W), np.uint32)
+    pad[:, :N] = P
+    t = pad.reshape(8, RT, 32, KT, 2, 2)          # plane, rt, i, kt, g, word
+    t = t.transpose(0, 1, 3, 4, 2, 5)             # plane, rt, kt, g, i, word
+    return t.reshape(8, RT * KT * 128)
+
+
+@pytest.mark.parametrize("NK", [(77, 384), (64, 128), (200, 1024)])
+def test_tile_planes_layout(NK):
+    N, K = NK
+    P = synth.gen_planes_shape(13, 0, 0, 0, N, K)
+    out = torch.full((8, apw.tiled_plane_words(N, K)), -1, dtype=torch.int32, device="cuda")
+    apw.tile_planes(ctx(), dev(P), N, K, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(out).view(np.uint32), _tiled_numpy(P))
+
+
 def test_pack_planes_parity():
     n, k = 77, 384
     codes = RNG.integers(0, 256, (n, k)).astype(np.uint8)
@@ -118,7 +141,8 @@ def _gemm_setup(qs, counts, N, K, identity, seed):
     planes_np, luts_np = [], []
     for e, q in enumerate(qs):
         P = synth.gen_planes_shape(seed, 0, e, 0, N, K)
-        Pd = dev(P)
+        Pd = torch.empty((8, apw.tiled_plane_words(N, K)), dtype=torch.int32, device="cuda")
+        apw.tile_planes(ctx(), dev(P), N, K, Pd)
         if identity:
             lut = np.tile(np.arange(1 << q, dtype=np.float16), (N, 1))
         else:
@@ -322,12 +346,12 @@ def test_planes_above_q_are_never_read():
     cfg = synth.CONFIGS[0]
     L = Layer(cfg)
     ref = host(L.run()["out"])
-    for (e, u), pt in L.rw.planes.items():
+    for (_, e, u), pt in L.rw.planes.items():
         q = int(L.q[e, u])
         if q < 8:
             pt[q:].fill_(-1)
     poisoned = host(L.run()["out"])
-    for (e, u) in list(L.rw.planes):
+    for (_, e, u) in list(L.rw.planes):
         q = int(L.q[e, u])
         for p in range(q, 8):
             L.rw.table.set_plane(0, e, u, p, None, False)
