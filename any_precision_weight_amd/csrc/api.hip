@@ -562,9 +562,15 @@ apmoe_status apmoe_gemm(apmoe_ctx *ctx, const apmoe_table *tbl, int32_t layer, i
     s = layer_shape(tbl, layer, kind, &N, &K, &max_q);
     if (s != APMOE_OK)
         return s;
+    const size_t in_rows = gather ? (size_t)T : (size_t)T * topk;
+    const size_t in_bytes = in_rows * (size_t)K * 2;
+    const size_t plane_bytes = apmoe::tiled_plane_words(N, K) * 4;
+    if (in_bytes >= ((size_t)1 << 31) || plane_bytes >= ((size_t)1 << 31) || ((size_t)N << (max_q + 1)) >= ((size_t)1 << 31))
+        return fail(APMOE_INVALID_ARG, "operands above 2 GiB per buffer are not supported (in %zu B, plane %zu B)",
+                    in_bytes, plane_bytes);
     const DevBlock *slice = tbl->d_table + tbl->index(layer, 0, 0);
-    hipError_t e = apmoe::launch_gemm(slice, kind, tbl->E, N, K, max_q, in, gather, perm, offsets, topk, out,
-                                      out_dtype == APMOE_F32, reinterpret_cast<hipStream_t>(stream));
+    hipError_t e = apmoe::launch_gemm(slice, kind, tbl->E, N, K, max_q, in, in_bytes, gather, perm, offsets, topk,
+                                      out, out_dtype == APMOE_F32, reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? ok() : hip_fail(e, "gemm launch");
 }
 

@@ -42,8 +42,14 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float float16v __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef const __attribute__((address_space(1))) u32x2 *gptr2;
-typedef const __attribute__((address_space(1))) u32x4 *gptr4;
+
+// Buffer resource (base, byte range) in scalar registers: loads take a 32-bit lane
+// offset and return zeros past the range.  Word 3 is the gfx9-family raw-buffer
+// configuration.
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
 
 __device__ inline uint32_t bitrev(uint32_t c, int q) { return __builtin_bitreverse32(c) >> (32 - q); }
 
@@ -79,24 +85,27 @@ struct GemmParams {
     const int32_t *offsets;
     void *out;
     int kind, E, N, K, topk, gather, out_f32, row_blocks;
+    uint32_t in_bytes;     // bytes of `in` (buffer range of the B-operand loads)
+    uint32_t plane_bytes;  // bytes of one tiled plane
 };
 
 // Plane bases are wave-uniform (scalar registers); the per-lane part is a 32-bit
 // word offset into the tiled plane, so each load is one global_load_dwordx2 with a
 // scalar base and a wave reads 512 contiguous bytes per plane.
 template <int Q>
-__device__ inline void load_planes(u32x2 (&w)[Q], const DevBlock &blk, uint32_t word)
+__device__ inline void load_planes(u32x2 (&w)[Q], const __amdgpu_buffer_rsrc_t (&rs)[Q], uint32_t word)
 {
 #pragma unroll
     for (int p = 0; p < Q; ++p)
-        w[p] = *(gptr2)(blk.plane[p] + word);
+        w[p] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs[p], (int)(word * 4u), 0, 0));
 }
 
-__device__ inline void load_x_group(u32x4 (&xg)[4], gptr4 p)
+// 4 B fragments (32 fp16 columns) of this lane's token row, starting at byte `off`.
+__device__ inline void load_x_group(u32x4 (&xg)[4], __amdgpu_buffer_rsrc_t rx, uint32_t off)
 {
 #pragma unroll
     for (int f = 0; f < 4; ++f)
-        xg[f] = p[f];
+        xg[f] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(off + 16u * f), 0, 0));
 }
 
 // 4 MFMAs over one 32-column word of each needed plane: unpack, LUT gather, multiply.
@@ -129,12 +138,15 @@ template <int Q>
 __device__ void gemm_block(const GemmParams &P, const DevBlock &blk, int rb, int r0, int Me, char *smem)
 {
     const int tid = threadIdx.x;
-    const int lane = tid % kWave, wave = tid / kWave;
+    const int lane = tid % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform (scalar)
     const int t = wave & 1, half = wave >> 1;
     const int i = lane & 31, g = lane >> 5;
     const int N = P.N, K = P.K;
     const int n0 = rb * kRows;
     const int nsteps = K / kStepCols;  // K % 128 == 0
+    // half 1 has no step when K == 128: it must not touch planes or token rows at all
+    const bool has_steps = half < nsteps;
     const int n_row = n0 + 32 * t + i;
     const bool row_ok = n_row < N;
     // tiled planes: tile (rt, kt) = rows 32rt.., columns 128kt.., 128 words; this lane
@@ -144,6 +156,12 @@ __device__ void gemm_block(const GemmParams &P, const DevBlock &blk, int rb, int
     const int rt = 2 * rb + t;
     const uint32_t lane_word = ((uint32_t)(rt < RT ? rt : 0) * (uint32_t)KT + (uint32_t)half) * 128u + 2u * lane;
     constexpr uint32_t kNextWords = 2 * 128;  // this wave's next step: two tiles on
+    __amdgpu_buffer_rsrc_t rs[Q];
+#pragma unroll
+    for (int p = 0; p < Q; ++p)
+        rs[p] = make_rsrc(blk.plane[p], P.plane_bytes);
+    const __amdgpu_buffer_rsrc_t rl = make_rsrc(blk.lut, (uint32_t)N << (Q + 1));
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(P.in, P.in_bytes);
 
     // ---- LUT level Q of rows n0..n0+63: 16-byte loads (8 entries of one row),
     //      lane -> row so that one wave touches 64 rows ----------------------------
@@ -159,11 +177,13 @@ __device__ void gemm_block(const GemmParams &P, const DevBlock &blk, int rb, int
             const int idx = tid + (j0 + jj) * kThreads;
             const int nl = idx % kRows, ch = idx / kRows;
             const bool ok = idx < kLutU4 && n0 + nl < N;
-            lv[jj] = ok ? *(gptr4)(blk.lut + ((size_t)(n0 + nl) << Q) + 8 * ch) : u32x4{0, 0, 0, 0};
+            lv[jj] = ok ? __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                              rl, (int)((((uint32_t)(n0 + nl) << Q) + 8u * ch) * 2u), 0, 0))
+                        : u32x4{0, 0, 0, 0};
         }
         // first step's planes are requested before the LUT lands in LDS
-        if (j0 == 0)
-            load_planes<Q>(wc, blk, lane_word);
+        if (j0 == 0 && has_steps)
+            load_planes<Q>(wc, rs, lane_word);
 #pragma unroll
         for (int jj = 0; jj < kBatch; ++jj) {
             const int idx = tid + (j0 + jj) * kThreads;
@@ -197,9 +217,9 @@ __device__ void gemm_block(const GemmParams &P, const DevBlock &blk, int rb, int
         // lanes past the last token read the last token's row: their D columns are discarded
         const int r = r0 + min(tp + j, Me - 1);
         const int src = P.gather ? P.perm[r] / P.topk : r;
-        gptr4 xp = (gptr4)(P.in + (size_t)src * K + half * kStepCols + 64 * g);
-        if (tp > 0)
-            load_planes<Q>(wc, blk, lane_word);
+        uint32_t xoff = ((uint32_t)src * (uint32_t)K + (uint32_t)(half * kStepCols + 64 * g)) * 2u;  // bytes
+        if (tp > 0 && has_steps)
+            load_planes<Q>(wc, rs, lane_word);
         float16v acc;
 #pragma unroll
         for (int v = 0; v < 16; ++v)
@@ -207,17 +227,18 @@ __device__ void gemm_block(const GemmParams &P, const DevBlock &blk, int rb, int
         // B-operand groups (4 fragments = 32 columns) are double-buffered and requested
         // one group ahead, continuing across steps; planes are requested one step ahead.
         u32x4 xa[4], xb[4];
-        load_x_group(xa, xp);
+        if (has_steps)
+            load_x_group(xa, rx, xoff);
         uint32_t word = lane_word;
         for (int step = half; step < nsteps; step += 2) {
             const bool more = step + 2 < nsteps;
             u32x2 wn[Q];
             word += more ? kNextWords : 0u;
-            load_planes<Q>(wn, blk, word);
-            load_x_group(xb, xp + 4);
+            load_planes<Q>(wn, rs, word);
+            load_x_group(xb, rx, xoff + 64);
             group_product<Q, 0>(wc, xa, lds_base, lane_const, acc);
-            xp += more ? 2 * kStepCols / 8 : 0;  // 8 fp16 per u32x4
-            load_x_group(xa, xp);
+            xoff += more ? 2 * kStepCols * 2 : 0;  // this wave's next step: 256 columns on
+            load_x_group(xa, rx, xoff);
             group_product<Q, 1>(wc, xb, lds_base, lane_const, acc);
 #pragma unroll
             for (int p = 0; p < Q; ++p)
@@ -255,7 +276,9 @@ __device__ void gemm_block(const GemmParams &P, const DevBlock &blk, int rb, int
     }
 }
 
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) gemm_kernel(GemmParams P)
+// KIND (APMOE_GATE_UP / APMOE_DOWN) only names the launch, so profiles tell them apart.
+template <int KIND>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) gemm_kernel(GemmParams P)
 {
     __shared__ __attribute__((aligned(16))) char smem[kLutBytes + kRedBytes];
     const int e = blockIdx.x % P.E;
@@ -279,8 +302,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
 }  // namespace
 
 hipError_t launch_gemm(const DevBlock *table, int kind, int E, int N, int K, int max_q, const uint16_t *in,
-                       int gather, const int32_t *perm, const int32_t *offsets, int topk, void *out, int out_f32,
-                       hipStream_t s)
+                       size_t in_bytes, int gather, const int32_t *perm, const int32_t *offsets, int topk, void *out,
+                       int out_f32, hipStream_t s)
 {
     (void)max_q;
     GemmParams P;
@@ -297,7 +320,12 @@ hipError_t launch_gemm(const DevBlock *table, int kind, int E, int N, int K, int
     P.gather = gather;
     P.out_f32 = out_f32;
     P.row_blocks = (N + kRows - 1) / kRows;
-    hipLaunchKernelGGL(gemm_kernel, dim3(P.row_blocks * E), dim3(kThreads), 0, s, P);
+    P.in_bytes = (uint32_t)in_bytes;
+    P.plane_bytes = (uint32_t)(tiled_plane_words(N, K) * 4);
+    if (kind == APMOE_GATE_UP)
+        hipLaunchKernelGGL(gemm_kernel<APMOE_GATE_UP>, dim3(P.row_blocks * E), dim3(kThreads), 0, s, P);
+    else
+        hipLaunchKernelGGL(gemm_kernel<APMOE_DOWN>, dim3(P.row_blocks * E), dim3(kThreads), 0, s, P);
     return hipGetLastError();
 }
 

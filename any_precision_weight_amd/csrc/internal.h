@@ -32,9 +32,10 @@ hipError_t launch_route_sort(const int32_t *ids, int R, int E, int32_t *counts, 
                              int32_t *inv_perm, hipStream_t s);
 
 // table points at the (layer) slice: entry for expert e and kind u is table[2*e + u].
+// in_bytes: size of `in` (rows x K fp16); must be below 2^31.
 hipError_t launch_gemm(const DevBlock *table, int kind, int E, int N, int K, int max_q, const uint16_t *in,
-                       int gather, const int32_t *perm, const int32_t *offsets, int topk, void *out, int out_f32,
-                       hipStream_t s);
+                       size_t in_bytes, int gather, const int32_t *perm, const int32_t *offsets, int topk, void *out,
+                       int out_f32, hipStream_t s);
 
 hipError_t launch_act(const uint16_t *h, int R, int F, uint16_t *a, hipStream_t s);
 hipError_t launch_combine(const void *y, int y_f32, const float *w, const int32_t *inv_perm, int T, int topk, int H,
