@@ -1,8 +1,10 @@
 """Counter-based generators and the workload table.
 
 All arithmetic here is random-number plumbing: SplitMix64 outputs, uniform and
-normal variates, RNE rounding to fp16 (numpy's float64 -> float16 cast), sorting
-of the parent LUT rows, and the Zipf prior used as a router bias.
+approximately normal variates, RNE rounding to fp16 (numpy's float64 -> float16
+cast), sorting of the parent LUT rows, and the Zipf prior used as a router bias.
+synth/synth_gpu.hip implements the same definitions for bulk generation on the
+device; both produce identical bits.
 """
 from __future__ import annotations
 
@@ -53,16 +55,25 @@ def uniform01(u: np.ndarray) -> np.ndarray:
 
 
 def normal(seed: int, tid: int, idx) -> np.ndarray:
-    """Standard normal variate number ``idx`` (Box-Muller, cosine branch) using
-    stream elements 2*idx and 2*idx+1."""
+    """Approximately standard normal variate number ``idx``: the Irwin-Hall sum of
+    twelve 16-bit uniforms minus 6 (stream elements 3*idx .. 3*idx+2, each split into
+    four 16-bit chunks).  Mean 0, variance 1 - 2^-32, support [-6, 6], resolution
+    2^-16.  The sum is exact integer arithmetic and the scaling by 2^-16 is exact, so
+    a device implementation of the same definition reproduces the bits."""
     idx = np.asarray(idx, dtype=np.uint64)
-    u1 = uniform01(u64(seed, tid, idx * np.uint64(2)))
-    u2 = uniform01(u64(seed, tid, idx * np.uint64(2) + np.uint64(1)))
-    return np.sqrt(-2.0 * np.log(u1)) * np.cos(2.0 * math.pi * u2)
+    acc = np.zeros(idx.shape, dtype=np.int64)
+    base = idx * np.uint64(3)
+    m16 = np.uint64(0xFFFF)
+    for i in range(3):
+        u = u64(seed, tid, base + np.uint64(i))
+        for sh in (0, 16, 32, 48):
+            acc += ((u >> np.uint64(sh)) & m16).astype(np.int64)
+    return (acc - 393210).astype(np.float64) * (2.0 ** -16)  # 393210 = 12 * 65535 / 2
 
 
 def fp16_normal(seed: int, tid: int, n: int, std: float, offset: int = 0) -> np.ndarray:
-    """``n`` consecutive N(0, std^2) values rounded to fp16 (round to nearest even)."""
+    """``n`` consecutive normal(0, std^2) values: fp64 product normal*std (one
+    correctly rounded multiply), then rounded to fp16 (round to nearest even)."""
     out = np.empty(n, dtype=np.float16)
     step = 1 << 22
     for s in range(0, n, step):
