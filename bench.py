@@ -21,6 +21,7 @@ import sys
 import time
 
 HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X published dense fp16 matrix peak
 
 
 def algorithmic_bytes(cfg, counts, qmap, kind):
@@ -65,7 +66,7 @@ def cpu_baseline(cfg, layer):
 
 
 class BenchLayer:
-    def __init__(self, cfg, copies):
+    def __init__(self, cfg, copies, device_gen=False, uniform_q=0):
         import numpy as np
         import torch
 
@@ -79,13 +80,19 @@ class BenchLayer:
         self.copies = copies
         E = cfg.experts
         self.q = synth.gen_qmap(cfg, 0)
+        if uniform_q:
+            self.q[:] = uniform_q
         self.rw = ResidentWeights(self.ctx, copies, E)
         self.planes, self.parent = {}, {}
         for e in range(E):
             for u in (0, 1):
-                P = synth.gen_planes(cfg, 0, e, u)
-                L8 = synth.gen_parent_lut(cfg, 0, e, u)
-                self.planes[(e, u)], self.parent[(e, u)] = P, L8
+                if device_gen:  # bit-identical device generator; no host copies (no CPU baseline)
+                    import synth.gpu
+                    P, L8 = synth.gpu.planes(cfg, 0, e, u), synth.gpu.parent_lut(cfg, 0, e, u)
+                else:
+                    P = synth.gen_planes(cfg, 0, e, u)
+                    L8 = synth.gen_parent_lut(cfg, 0, e, u)
+                    self.planes[(e, u)], self.parent[(e, u)] = P, L8
                 for c in range(copies):
                     self.rw.add_block(c, e, u, P, L8, int(self.q[e, u]))
         self.rw.commit()
@@ -137,6 +144,10 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--copies", type=int, default=2, help="resident weight copies rotated between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--uniform-q", type=int, default=0, metavar="Q",
+                    help="commit every block at bitwidth Q instead of the workload's map (per-q study)")
+    ap.add_argument("--workload", default="mixtral8x7b_decode_t16",
+                    help="synthetic workload (default: the Mixtral-8x7B decode layer the metric is quoted on)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run one plain device copy of MIB MiB (HBM counter calibration)")
     args = ap.parse_args()
@@ -148,9 +159,13 @@ def main() -> int:
     import torch
 
     import synth
-    cfg = synth.config_by_name("mixtral8x7b_decode_t16")
+    cfg = synth.config_by_name(args.workload)
+    if cfg.layers != 1:
+        print("bench.py: multi-layer workloads are exercised by the tests, not timed here", file=sys.stderr)
+        return 2
+    big = cfg.tokens * cfg.hidden > 16 * 4096 or cfg.hidden > 4096
     print(f"[bench] generating and uploading {cfg.name} ({args.copies} weight copies)", file=sys.stderr, flush=True)
-    L = BenchLayer(cfg, args.copies)
+    L = BenchLayer(cfg, args.copies, device_gen=big, uniform_q=args.uniform_q)
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
         for i in range(args.warmup):
@@ -182,7 +197,10 @@ def main() -> int:
     lb = layer_bytes(cfg, counts, L.q)
     gu_gbs = gu_bytes / (gu_ms * 1e-3) / 1e9
     tokens_per_s = cfg.tokens / (ms * 1e-3)
-    print(f"[bench] step {ms * 1e3:.1f} us  gate_up {gu_ms * 1e3:.1f} us ({gu_gbs:.0f} GB/s)  "
+    flops = 2 * cfg.tokens * cfg.topk * 3 * cfg.hidden * cfg.ffn + 2 * cfg.tokens * cfg.experts * cfg.hidden
+    tflops = flops / (ms * 1e-3) / 1e12
+    print(f"[bench] {cfg.name}: {tflops:.1f} TFLOP/s  "
+          f"step {ms * 1e3:.1f} us  gate_up {gu_ms * 1e3:.1f} us ({gu_gbs:.0f} GB/s)  "
           f"down {dn_ms * 1e3:.1f} us ({dn_bytes / (dn_ms * 1e-3) / 1e9:.0f} GB/s)  "
           f"layer {lb / (ms * 1e-3) / 1e9:.0f} GB/s", file=sys.stderr, flush=True)
 
@@ -205,11 +223,13 @@ def main() -> int:
         "layer_gbps": round(lb / (ms * 1e-3) / 1e9, 1),
         "layer_hbm_frac": round(lb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "kernels_us": {"gate_up": round(gu_ms * 1e3, 2), "down": round(dn_ms * 1e3, 2)},
+        "layer_tflops": round(tflops, 2),
+        "layer_mfma_frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
         "roofline": {"kernel": "apmoe gemm (gate_up)", "bound": "hbm", "achieved": round(gu_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
                      "algorithmic_bytes": gu_bytes, "traffic": None},
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and L.planes:
         print("[bench] timing the fp64 CPU oracle on the same layer", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(cfg, L)
     print(json.dumps(result), flush=True)
