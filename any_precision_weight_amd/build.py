@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libapmoe.so")
-SOURCES = ["api.hip", "route.hip", "gemm.hip", "elementwise.hip"]
+SOURCES = ["api.hip", "route.hip", "gemm.hip", "gemm_tile.hip", "elementwise.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -570,7 +570,7 @@ apmoe_status apmoe_gemm(apmoe_ctx *ctx, const apmoe_table *tbl, int32_t layer, i
                     in_bytes, plane_bytes);
     const DevBlock *slice = tbl->d_table + tbl->index(layer, 0, 0);
     hipError_t e = apmoe::launch_gemm(slice, kind, tbl->E, N, K, max_q, in, in_bytes, gather, perm, offsets, topk,
-                                      out, out_dtype == APMOE_F32, reinterpret_cast<hipStream_t>(stream));
+                                      T * topk, out, out_dtype == APMOE_F32, reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? ok() : hip_fail(e, "gemm launch");
 }
 

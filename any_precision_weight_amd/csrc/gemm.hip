@@ -85,6 +85,7 @@ struct GemmParams {
     const int32_t *offsets;
     void *out;
     int kind, E, N, K, topk, gather, out_f32, row_blocks;
+    int max_rows;          // experts with more rows belong to the tile product
     uint32_t in_bytes;     // bytes of `in` (buffer range of the B-operand loads)
     uint32_t plane_bytes;  // bytes of one tiled plane
 };
@@ -285,8 +286,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
     const int rb = blockIdx.x / P.E;
     const int r0 = P.offsets[e];
     const int Me = P.offsets[e + 1] - r0;
-    if (Me <= 0)
-        return;  // expert without tokens: no weight reads
+    if (Me <= 0 || Me > P.max_rows)
+        return;  // expert without tokens (no weight reads), or one for the tile product
     const DevBlock blk = P.table[2 * e + P.kind];
     switch (blk.q) {
     case 3: gemm_block<3>(P, blk, rb, r0, Me, smem); break;
@@ -302,8 +303,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
 }  // namespace
 
 hipError_t launch_gemm(const DevBlock *table, int kind, int E, int N, int K, int max_q, const uint16_t *in,
-                       size_t in_bytes, int gather, const int32_t *perm, const int32_t *offsets, int topk, void *out,
-                       int out_f32, hipStream_t s)
+                       size_t in_bytes, int gather, const int32_t *perm, const int32_t *offsets, int topk, int R,
+                       void *out, int out_f32, hipStream_t s)
 {
     (void)max_q;
     GemmParams P;
@@ -322,11 +323,15 @@ hipError_t launch_gemm(const DevBlock *table, int kind, int E, int N, int K, int
     P.row_blocks = (N + kRows - 1) / kRows;
     P.in_bytes = (uint32_t)in_bytes;
     P.plane_bytes = (uint32_t)(tiled_plane_words(N, K) * 4);
+    P.max_rows = kDecodeMaxRows;
     if (kind == APMOE_GATE_UP)
         hipLaunchKernelGGL(gemm_kernel<APMOE_GATE_UP>, dim3(P.row_blocks * E), dim3(kThreads), 0, s, P);
     else
         hipLaunchKernelGGL(gemm_kernel<APMOE_DOWN>, dim3(P.row_blocks * E), dim3(kThreads), 0, s, P);
-    return hipGetLastError();
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess || R <= kDecodeMaxRows)
+        return err;  // no expert can have more rows than the decode product takes
+    return launch_gemm_tile(table, kind, E, N, K, in, in_bytes, gather, perm, offsets, topk, out, out_f32, R, s);
 }
 
 }  // namespace apmoe

@@ -1,0 +1,464 @@
+// gemm_tile.hip -- any-precision expert product, MFMA tile variant for experts with
+// many rows (prefill, hot experts).  Same result as the decode product in gemm.hip
+// (PagedWeight, Section 3.3: the fused kernel reads bit-planes and LUTs directly and
+// follows each linear-block's bitwidth):
+//
+//   out[r][n] = sum_c in_row(r)[c] * LUT_q[n][code_q(n, c)],  fp32 accumulation.
+//
+// The weights are dequantised exactly (an fp16 LUT entry is the fp16 operand), so
+// the product is an fp16 MFMA GEMM whose A operand is produced by lookups.
+//
+// Tile: 128 weight rows x 256 expert rows (tokens).  Workgroup = 4 waves; wave w
+// owns weight rows 32w..32w+31 of the tile and all 256 tokens (8 column tiles of
+// v_mfma_f32_32x32x16_f16, 8 x 16 fp32 accumulators per lane).  A lane decodes its
+// own weight row: per 128-column step it loads, for each needed plane, the two
+// words of its row (64 columns, the same tiled layout as the decode product), turns
+// them into codes with an 8x8 bit transpose and looks the codes up in LUT_q staged
+// in LDS.  Each decoded A fragment is reused by the 8 token tiles; the token rows
+// (B operand) are staged in LDS, 64 columns at a time, double-buffered.
+//
+// LDS (128 KB, one workgroup per CU):
+//   [0, 64 KB)    LUT_q of the tile's 128 rows: entry (row nl, code) at
+//                 v*256 + 4*(nl % 64) + 2*(nl / 64), v = code with its q bits reversed
+//                 (the transposed code byte), so a lookup address is one v_perm.
+//   [64, 128 KB)  two 32 KB stages of 256 token rows x 64 columns fp16; row tr holds
+//                 eight 16-byte chunks (chunk c = columns 64*(c/4) + 32*s + 8*(c%4) of
+//                 the step, s the stage's word), stored at chunk c ^ ((tr/2) % 8) so that
+//                 16 lanes reading one chunk of 16 consecutive rows hit distinct banks.
+//
+// Tile order: tiles of one expert are grouped as (8 weight-row tiles) x (all token
+// tiles), consecutive tiles run on the same XCD (workgroup b runs on XCD b % 8), so
+// a group's weight and token tiles are shared through that XCD's L2.
+#include "internal.h"
+
+namespace apmoe {
+namespace {
+
+constexpr int kWave = 64;
+constexpr int kThreads = 256;
+constexpr int kBN = 128;  // weight rows per tile
+constexpr int kBM = kTileTokens;  // token rows per tile (256)
+constexpr int kTT = kBM / 32;      // MFMA column tiles
+constexpr int kStepCols = 128;
+constexpr int kLutBytes = 64 * 1024;
+constexpr int kStageBytes = kBM * 64 * 2;  // 32 KB
+constexpr int kXBase = kLutBytes;
+constexpr int kGroupN = 8;  // weight-row tiles per group
+constexpr int kXcds = 8;
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float float16v __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ inline uint32_t bitrev(uint32_t c, int q) { return __builtin_bitreverse32(c) >> (32 - q); }
+
+__device__ inline void swap_bits(uint32_t &a, uint32_t &b, int s, uint32_t m)
+{
+    const uint32_t t = ((a >> s) ^ b) & m;
+    b ^= t;
+    a ^= t << s;
+}
+
+// 4 independent 8x8 bit transposes: in, d[p] byte b bit j = plane p, column 8b+j;
+// out, d[j] byte b bit p = the same bit.
+__device__ inline void transpose8x8(uint32_t (&d)[8])
+{
+    swap_bits(d[0], d[4], 4, 0x0F0F0F0Fu);
+    swap_bits(d[1], d[5], 4, 0x0F0F0F0Fu);
+    swap_bits(d[2], d[6], 4, 0x0F0F0F0Fu);
+    swap_bits(d[3], d[7], 4, 0x0F0F0F0Fu);
+    swap_bits(d[0], d[2], 2, 0x33333333u);
+    swap_bits(d[1], d[3], 2, 0x33333333u);
+    swap_bits(d[4], d[6], 2, 0x33333333u);
+    swap_bits(d[5], d[7], 2, 0x33333333u);
+    swap_bits(d[0], d[1], 1, 0x55555555u);
+    swap_bits(d[2], d[3], 1, 0x55555555u);
+    swap_bits(d[4], d[5], 1, 0x55555555u);
+    swap_bits(d[6], d[7], 1, 0x55555555u);
+}
+
+struct TileParams {
+    const DevBlock *table;  // layer slice; entry 2*e + kind
+    const uint16_t *in;
+    const int32_t *perm;
+    const int32_t *offsets;
+    void *out;
+    int kind, E, N, K, topk, gather, out_f32, NT, min_rows;
+    uint32_t in_bytes;     // bytes of `in`
+    uint32_t plane_bytes;  // bytes of one tiled plane
+};
+
+struct Tile {
+    int e, r0, m0, M, n0;
+};
+
+// Workgroup -> tile.  Every thread computes the same answer; E <= 256 = blockDim.
+__device__ bool resolve_tile(const TileParams &P, int *scan, Tile &T)
+{
+    const int tid = threadIdx.x;
+    int tiles = 0;
+    if (tid < P.E) {
+        const int me = P.offsets[tid + 1] - P.offsets[tid];
+        tiles = me > P.min_rows ? (me + kBM - 1) / kBM * P.NT : 0;
+    }
+    scan[tid] = tiles;
+    __syncthreads();
+    for (int d = 1; d < kThreads; d <<= 1) {  // inclusive scan (Hillis-Steele)
+        const int v = tid >= d ? scan[tid - d] : 0;
+        __syncthreads();
+        scan[tid] += v;
+        __syncthreads();
+    }
+    const int total = scan[kThreads - 1];
+    const int per_xcd = (total + kXcds - 1) / kXcds;
+    const int b = blockIdx.x;
+    const int local = b / kXcds;
+    const int l = (b % kXcds) * per_xcd + local;
+    if (local >= per_xcd || l >= total)
+        return false;
+    // expert: the first e with scan[e] > l
+    int e = 0;
+    {
+        int lo = 0, hi = P.E - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (scan[mid] > l)
+                hi = mid;
+            else
+                lo = mid + 1;
+        }
+        e = lo;
+    }
+    const int t = l - (e > 0 ? scan[e - 1] : 0);
+    const int r0 = P.offsets[e];
+    const int me = P.offsets[e + 1] - r0;
+    const int mt_n = (me + kBM - 1) / kBM;
+    const int full_groups = P.NT / kGroupN;
+    int mt, nt;
+    if (t < full_groups * kGroupN * mt_n) {
+        const int ng = t / (kGroupN * mt_n), w = t % (kGroupN * mt_n);
+        mt = w / kGroupN;
+        nt = ng * kGroupN + w % kGroupN;
+    } else {
+        const int gs = P.NT - full_groups * kGroupN;
+        const int w = t - full_groups * kGroupN * mt_n;
+        mt = w / gs;
+        nt = full_groups * kGroupN + w % gs;
+    }
+    // identical in every lane: keep the tile in scalar registers
+    T.e = __builtin_amdgcn_readfirstlane(e);
+    T.r0 = __builtin_amdgcn_readfirstlane(r0);
+    T.m0 = __builtin_amdgcn_readfirstlane(mt * kBM);
+    T.M = __builtin_amdgcn_readfirstlane(min(kBM, me - mt * kBM));
+    T.n0 = __builtin_amdgcn_readfirstlane(nt * kBN);
+    return true;
+}
+
+template <int Q>
+__device__ inline void load_planes(u32x2 (&w)[Q], const __amdgpu_buffer_rsrc_t (&rs)[Q], uint32_t word)
+{
+#pragma unroll
+    for (int p = 0; p < Q; ++p)
+        w[p] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs[p], (int)(word * 4u), 0, 0));
+}
+
+// Codes of word W (32 columns) of this lane's row: d[j] byte b = transposed code of
+// column 8b + j of the word.
+template <int Q, int W>
+__device__ inline void word_codes(const u32x2 (&w)[Q], uint32_t (&d)[8])
+{
+#pragma unroll
+    for (int p = 0; p < 8; ++p)
+        d[p] = p < Q ? w[p < Q ? p : 0][W] : 0u;
+    transpose8x8(d);
+}
+
+// A fragment for k-group b of a word: the 8 LUT entries of columns 8b..8b+7.
+__device__ inline half8 lookup8(const uint32_t (&d)[8], int b, uint32_t lane_const)
+{
+    half8 a;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const uint32_t addr = __builtin_amdgcn_perm(d[j], lane_const, 0x0C0C0000u | ((4u + b) << 8));
+        a[j] = *(const __attribute__((address_space(3))) _Float16 *)(uintptr_t)addr;
+    }
+    return a;
+}
+
+__device__ inline u32x4 lds_b128(uint32_t addr)
+{
+    return *(const __attribute__((address_space(3))) u32x4 *)(uintptr_t)addr;
+}
+
+__device__ inline void lds_store_b128(uint32_t addr, u32x4 v)
+{
+    *(__attribute__((address_space(3))) u32x4 *)(uintptr_t)addr = v;
+}
+
+// token-row stage: thread -> chunk c = tid % 8 of rows tid/8 + 32u (u < 8)
+struct XStage {
+    uint32_t row_off[8];  // byte offset of the row in `in` (clamped to the tile's last row)
+    uint32_t col_off;     // byte offset of chunk c in stage 0 of step 0
+    uint32_t lds_off;     // LDS offset of (row tid/8, chunk c) within a stage
+};
+
+__device__ inline void x_load(u32x4 (&v)[8], __amdgpu_buffer_rsrc_t rx, const XStage &X, uint32_t step_off)
+{
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+        v[u] = __builtin_bit_cast(u32x4,
+                                  __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(X.row_off[u] + step_off), 0, 0));
+}
+
+__device__ inline void x_store(const u32x4 (&v)[8], const XStage &X, uint32_t stage_base)
+{
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+        lds_store_b128(stage_base + X.lds_off + 32u * 128u * u, v[u]);
+}
+
+template <int Q>
+__device__ void tile_block(const TileParams &P, const DevBlock &blk, const Tile &T)
+{
+    const int tid = threadIdx.x;
+    const int lane = tid % kWave;
+    const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int i = lane & 31, g = lane >> 5;
+    const int N = P.N, K = P.K;
+    const int KT = K / kStepCols;
+    const int RT = (N + 31) / 32;
+    const int rt = T.n0 / 32 + w;
+    const uint32_t lane_word = (uint32_t)(rt < RT ? rt : 0) * (uint32_t)KT * 128u + 2u * lane;
+
+    __amdgpu_buffer_rsrc_t rs[Q];
+#pragma unroll
+    for (int p = 0; p < Q; ++p)
+        rs[p] = make_rsrc(blk.plane[p], P.plane_bytes);
+    const __amdgpu_buffer_rsrc_t rl = make_rsrc(blk.lut, (uint32_t)N << (Q + 1));
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(P.in, P.in_bytes);
+
+    // ---- token rows of this tile -------------------------------------------------
+    XStage X;
+    {
+        const int c = tid & 7;
+        const int trb = tid >> 3;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int tr = min(trb + 32 * u, T.M - 1);
+            const int r = T.r0 + T.m0 + tr;
+            const int src = P.gather ? P.perm[r] / P.topk : r;
+            X.row_off[u] = (uint32_t)src * (uint32_t)K * 2u;
+        }
+        X.col_off = (uint32_t)(64 * (c >> 2) + 8 * (c & 3)) * 2u;
+        X.lds_off = (uint32_t)(trb * 128 + 16 * (c ^ ((trb >> 1) & 7)));
+    }
+    // byte offset of stage s of step st relative to X.col_off: step st covers columns
+    // 128*st.., word s adds 32 columns
+    auto stage_off = [&](int idx) -> uint32_t {
+        return X.col_off + (uint32_t)((idx >> 1) * kStepCols + 32 * (idx & 1)) * 2u;
+    };
+
+    u32x4 xv[8];
+    x_load(xv, rx, X, stage_off(0));
+    u32x2 wc[Q];
+    load_planes<Q>(wc, rs, lane_word);
+
+    // ---- LUT level Q of the tile's rows -> LDS (row pairs nl, nl+64 share a word) --
+    {
+        constexpr int kChunksPerRow = (1 << Q) / 8;  // 16-byte chunks of one row
+        constexpr int kPairChunks = 64 * kChunksPerRow;
+        constexpr int kPer = (kPairChunks + kThreads - 1) / kThreads;
+#pragma unroll
+        for (int jj = 0; jj < kPer; ++jj) {
+            const int pc = tid + jj * kThreads;
+            if (pc < kPairChunks) {
+                const int pr = pc / kChunksPerRow, ch = pc % kChunksPerRow;
+                const int na = T.n0 + pr, nb = T.n0 + pr + 64;
+                const u32x4 za = {0, 0, 0, 0};
+                const u32x4 la = na < N ? __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                                     rl, (int)((((uint32_t)na << Q) + 8u * ch) * 2u), 0, 0))
+                                        : za;
+                const u32x4 lb = nb < N ? __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                                     rl, (int)((((uint32_t)nb << Q) + 8u * ch) * 2u), 0, 0))
+                                        : za;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t a = (la[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+                    const uint32_t b = (lb[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+                    const uint32_t v = bitrev((uint32_t)(8 * ch + e), Q);
+                    *(__attribute__((address_space(3))) uint32_t *)(uintptr_t)(v * 256u + 4u * pr) = a | (b << 16);
+                }
+            }
+        }
+    }
+    x_store(xv, X, kXBase);
+    __syncthreads();
+
+    const uint32_t lane_const = (uint32_t)(4 * (32 * (w & 1) + i) + 2 * (w >> 1));
+    // B fragment (token tile tt, k-group b of the stage): row 32tt + j, chunk 4g + b
+    uint32_t bo[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+        bo[b] = (uint32_t)(i * 128 + 16 * ((4 * g + b) ^ ((i >> 1) & 7)));
+    const int ntt = (T.M + 31) / 32;
+
+    float16v acc[kTT];
+#pragma unroll
+    for (int tt = 0; tt < kTT; ++tt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+            acc[tt][v] = 0.f;
+
+    const int nstages = 2 * KT;
+    uint32_t word = lane_word;
+    u32x2 wn[Q];
+    for (int idx = 0; idx < nstages; ++idx) {
+        const int s = idx & 1;
+        const uint32_t cur = kXBase + (uint32_t)s * kStageBytes;
+        const bool more = idx + 1 < nstages;
+        if (more)
+            x_load(xv, rx, X, stage_off(idx + 1));
+        uint32_t d[8];
+        if (s == 0) {
+            if (idx + 2 < nstages)
+                word += 128u;
+            load_planes<Q>(wn, rs, word);  // next step (the last step reloads its own words)
+            word_codes<Q, 0>(wc, d);
+        } else {
+            word_codes<Q, 1>(wc, d);
+        }
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const half8 a = lookup8(d, b, lane_const);
+#pragma unroll
+            for (int tt = 0; tt < kTT; ++tt) {
+                if (tt < ntt) {
+                    const u32x4 xb = lds_b128(cur + bo[b] + 4096u * tt);
+                    acc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, __builtin_bit_cast(half8, xb), acc[tt], 0, 0,
+                                                                     0);
+                }
+            }
+        }
+        if (more)
+            x_store(xv, X, kXBase + (uint32_t)(s ^ 1) * kStageBytes);
+        if (s == 1) {
+#pragma unroll
+            for (int p = 0; p < Q; ++p)
+                wc[p] = wn[p];
+        }
+        __syncthreads();
+    }
+
+    // ---- write: acc[tt][v] is token 32tt + (lane % 32), weight row
+    //      32w + 8(v/4) + 4g + v%4; four consecutive rows per store ------------------
+    const int j = i;
+#pragma unroll
+    for (int tt = 0; tt < kTT; ++tt) {
+        const int tok = 32 * tt + j;
+        if (tt < ntt && tok < T.M) {
+            const size_t orow = (size_t)(T.r0 + T.m0 + tok) * N;
+#pragma unroll
+            for (int a4 = 0; a4 < 4; ++a4) {
+                const int n = T.n0 + 32 * w + 8 * a4 + 4 * g;
+                if (P.out_f32) {
+                    float *o = reinterpret_cast<float *>(P.out) + orow + n;
+                    if ((N & 3) == 0 && n + 3 < N) {
+                        *reinterpret_cast<float4 *>(o) =
+                            make_float4(acc[tt][4 * a4], acc[tt][4 * a4 + 1], acc[tt][4 * a4 + 2], acc[tt][4 * a4 + 3]);
+                    } else {
+#pragma unroll
+                        for (int b = 0; b < 4; ++b)
+                            if (n + b < N)
+                                o[b] = acc[tt][4 * a4 + b];
+                    }
+                } else {
+                    _Float16 *o = reinterpret_cast<_Float16 *>(P.out) + orow + n;
+                    if ((N & 3) == 0 && n + 3 < N) {
+                        typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+                        half4 h;
+#pragma unroll
+                        for (int b = 0; b < 4; ++b)
+                            h[b] = (_Float16)acc[tt][4 * a4 + b];
+                        *reinterpret_cast<half4 *>(o) = h;
+                    } else {
+#pragma unroll
+                        for (int b = 0; b < 4; ++b)
+                            if (n + b < N)
+                                o[b] = (_Float16)acc[tt][4 * a4 + b];
+                    }
+                }
+            }
+        }
+    }
+}
+
+template <int KIND>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) tile_kernel(TileParams P)
+{
+    __shared__ __attribute__((aligned(16))) char smem[kLutBytes + 2 * kStageBytes];
+    Tile T;
+    if (!resolve_tile(P, reinterpret_cast<int *>(smem + kXBase), T))
+        return;
+    __syncthreads();  // the scan scratch is reused as a token stage
+    const DevBlock blk = P.table[2 * T.e + P.kind];
+    switch (blk.q) {
+    case 3: tile_block<3>(P, blk, T); break;
+    case 4: tile_block<4>(P, blk, T); break;
+    case 5: tile_block<5>(P, blk, T); break;
+    case 6: tile_block<6>(P, blk, T); break;
+    case 7: tile_block<7>(P, blk, T); break;
+    case 8: tile_block<8>(P, blk, T); break;
+    default: break;  // unreachable: commit validates q
+    }
+}
+
+}  // namespace
+
+int tile_grid(int N, int E, int R)
+{
+    const int NT = (N + kBN - 1) / kBN;
+    // sum over experts with more than kDecodeMaxRows rows of ceil(M_e / 256) is at
+    // most R / 256 + (number of such experts)
+    const int big = min(E, R / (kDecodeMaxRows + 1));
+    const long long tiles = (long long)NT * (R / kBM + big);
+    return (int)((tiles + kXcds - 1) / kXcds * kXcds);
+}
+
+hipError_t launch_gemm_tile(const DevBlock *table, int kind, int E, int N, int K, const uint16_t *in, size_t in_bytes,
+                            int gather, const int32_t *perm, const int32_t *offsets, int topk, void *out, int out_f32,
+                            int R, hipStream_t s)
+{
+    TileParams P;
+    P.table = table;
+    P.in = in;
+    P.perm = perm;
+    P.offsets = offsets;
+    P.out = out;
+    P.kind = kind;
+    P.E = E;
+    P.N = N;
+    P.K = K;
+    P.topk = topk;
+    P.gather = gather;
+    P.out_f32 = out_f32;
+    P.NT = (N + kBN - 1) / kBN;
+    P.min_rows = kDecodeMaxRows;
+    P.in_bytes = (uint32_t)in_bytes;
+    P.plane_bytes = (uint32_t)(tiled_plane_words(N, K) * 4);
+    const int grid = tile_grid(N, E, R);
+    if (grid == 0)
+        return hipSuccess;
+    if (kind == APMOE_GATE_UP)
+        hipLaunchKernelGGL(tile_kernel<APMOE_GATE_UP>, dim3(grid), dim3(kThreads), 0, s, P);
+    else
+        hipLaunchKernelGGL(tile_kernel<APMOE_DOWN>, dim3(grid), dim3(kThreads), 0, s, P);
+    return hipGetLastError();
+}
+
+}  // namespace apmoe

@@ -22,6 +22,11 @@ struct DevBlock {
 
 // Rows of the weight matrix handled by one workgroup of the decode product.
 constexpr int kGemmRowsPerBlock = 64;
+// Experts with at most this many rows use the decode product (one pass of 32 token
+// columns); larger ones use the MFMA tile product.
+constexpr int kDecodeMaxRows = 32;
+// Token rows per tile of the MFMA tile product.
+constexpr int kTileTokens = 256;
 
 // Words of one tiled plane: 32-row x 128-column tiles of 128 words.
 inline size_t tiled_plane_words(int n, int k) { return (size_t)((n + 31) / 32) * (k / 128) * 128; }
@@ -33,9 +38,14 @@ hipError_t launch_route_sort(const int32_t *ids, int R, int E, int32_t *counts, 
 
 // table points at the (layer) slice: entry for expert e and kind u is table[2*e + u].
 // in_bytes: size of `in` (rows x K fp16); must be below 2^31.
+// R = T * topk rows in total; experts are split between the decode and the tile
+// product by their row count (read on the device).
 hipError_t launch_gemm(const DevBlock *table, int kind, int E, int N, int K, int max_q, const uint16_t *in,
-                       size_t in_bytes, int gather, const int32_t *perm, const int32_t *offsets, int topk, void *out,
-                       int out_f32, hipStream_t s);
+                       size_t in_bytes, int gather, const int32_t *perm, const int32_t *offsets, int topk, int R,
+                       void *out, int out_f32, hipStream_t s);
+hipError_t launch_gemm_tile(const DevBlock *table, int kind, int E, int N, int K, const uint16_t *in, size_t in_bytes,
+                            int gather, const int32_t *perm, const int32_t *offsets, int topk, void *out, int out_f32,
+                            int R, hipStream_t s);
 
 hipError_t launch_act(const uint16_t *h, int R, int F, uint16_t *a, hipStream_t s);
 hipError_t launch_combine(const void *y, int y_f32, const float *w, const int32_t *inv_perm, int T, int topk, int H,

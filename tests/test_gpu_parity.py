@@ -224,6 +224,63 @@ def test_gemm_non_gather_rows():
     tbl.close()
 
 
+# Experts above 32 rows take the MFMA tile product (128 weight rows x 256 rows per
+# tile): several token tiles per expert with ragged tails, a weight-row tail, and
+# more than one group of 8 weight-row tiles.
+TILE_CASES = [
+    (200, 384, [300, 0, 257, 33, 600, 64]),
+    (1280, 256, [40, 300, 1, 31, 500, 32]),
+    (64, 1024, [256, 512, 3, 0, 129, 70]),
+]
+
+
+@pytest.mark.parametrize("case", TILE_CASES)
+def test_gemm_tile_identity_lut_exact(case):
+    N, K, counts = case
+    tbl, keep, P, L, offsets, perm, T = _gemm_setup(GEMM_QS, counts, N, K, True, 44)
+    x = RNG.integers(-2, 3, (T, K)).astype(np.float16)
+    got = _gemm_run(tbl, x, offsets, perm, T, N, apw.F32)
+    for e, q in enumerate(GEMM_QS):
+        rows = perm[offsets[e]:offsets[e + 1]]
+        codes = oracle.unpack_codes(P[e], q).astype(np.int64)
+        ref = x[rows].astype(np.int64) @ codes.T
+        assert np.array_equal(got[offsets[e]:offsets[e + 1]], ref.astype(np.float32)), (e, q, counts[e])
+    tbl.close()
+
+
+@pytest.mark.parametrize("out_dtype", [apw.F16, apw.F32])
+def test_gemm_tile_random_lut(out_dtype):
+    N, K, counts = 200, 384, [300, 0, 257, 33, 600, 64]
+    tbl, keep, P, L, offsets, perm, T = _gemm_setup(GEMM_QS, counts, N, K, False, 45)
+    x = synth.gen_aux_fp16(45, 0, T * K).reshape(T, K)
+    got = _gemm_run(tbl, x, offsets, perm, T, N, out_dtype).astype(np.float64)
+    for e, q in enumerate(GEMM_QS):
+        rows = perm[offsets[e]:offsets[e + 1]]
+        if rows.size == 0:
+            continue
+        xin = x[rows].astype(np.float64)
+        ref = oracle.block_gemm(P[e], L[e], q, xin)
+        S = oracle.block_gemm(P[e], np.abs(L[e]), q, np.abs(xin))
+        acc = K * 2.0 ** -24 * S
+        tol = acc + (0.5 * ulp16(np.abs(ref) + acc) if out_dtype == apw.F16 else 0.0)
+        d = np.abs(got[offsets[e]:offsets[e + 1]] - ref)
+        assert np.all(d <= tol), (e, q, float((d - tol).max()))
+    tbl.close()
+
+
+def test_gemm_tile_non_gather_rows():
+    N, K, counts = 136, 256, [70, 300, 0, 33, 1, 260]
+    tbl, keep, P, L, offsets, perm, T = _gemm_setup(GEMM_QS, counts, N, K, True, 46)
+    R = int(offsets[-1])
+    a = RNG.integers(-2, 3, (R, K)).astype(np.float16)
+    got = _gemm_run(tbl, a, offsets, perm, R, N, apw.F16, gather=False)
+    for e, q in enumerate(GEMM_QS):
+        codes = oracle.unpack_codes(P[e], q).astype(np.int64)
+        ref = a[offsets[e]:offsets[e + 1]].astype(np.int64) @ codes.T
+        assert np.array_equal(got[offsets[e]:offsets[e + 1]].astype(np.float64), ref.astype(np.float16).astype(np.float64))
+    tbl.close()
+
+
 # --------------------------------------------------------------------------- act / combine
 
 def test_act_parity():
