@@ -42,6 +42,7 @@ constexpr int kTT = kBM / 32;      // MFMA column tiles
 constexpr int kStepCols = 128;
 constexpr int kLutBytes = 64 * 1024;
 constexpr int kStageBytes = kBM * 64 * 2;  // 32 KB
+constexpr int kStages = 3;                  // token stages in flight (ring)
 constexpr int kXBase = kLutBytes;
 constexpr int kGroupN = 8;  // weight-row tiles per group
 constexpr int kXcds = 8;
@@ -99,7 +100,7 @@ struct Tile {
 };
 
 // Workgroup -> tile.  Every thread computes the same answer; E <= 256 = blockDim.
-__device__ bool resolve_tile(const TileParams &P, int *scan, Tile &T)
+__device__ __attribute__((always_inline)) bool resolve_tile(const TileParams &P, int *scan, Tile &T)
 {
     const int tid = threadIdx.x;
     int tiles = 0;
@@ -201,30 +202,114 @@ __device__ inline void lds_store_b128(uint32_t addr, u32x4 v)
     *(__attribute__((address_space(3))) u32x4 *)(uintptr_t)addr = v;
 }
 
-// token-row stage: thread -> chunk c = tid % 8 of rows tid/8 + 32u (u < 8)
+// Token stages are copied global -> LDS by the buffer unit (buffer_load ... lds):
+// one instruction writes 64 x 16 bytes at consecutive LDS addresses, so wave w,
+// instruction u fills rows 64w + 8u .. +7 of a stage, lane L the 16-byte slot L % 8
+// of row 64w + 8u + L / 8, and fetches the token chunk stored in that slot.
 struct XStage {
-    uint32_t row_off[8];  // byte offset of the row in `in` (clamped to the tile's last row)
-    uint32_t col_off;     // byte offset of chunk c in stage 0 of step 0
-    uint32_t lds_off;     // LDS offset of (row tid/8, chunk c) within a stage
+    uint32_t off[8];  // byte offset of the lane's chunk (token row + column) for instruction u
 };
 
-__device__ inline void x_load(u32x4 (&v)[8], __amdgpu_buffer_rsrc_t rx, const XStage &X, uint32_t step_off)
+__device__ inline uint32_t lds_addr(const void *p) { return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)p; }
+
+// Stage k = word (k % 2) of step k / 2 into ring buffer k % 3.
+__device__ inline void x_stage(char *smem, __amdgpu_buffer_rsrc_t rx, const XStage &X, int w, int k)
 {
+    const uint32_t step_off = (uint32_t)((k >> 1) * kStepCols * 2 + (k & 1) * 64);  // scalar offset
+    char *base = smem + kXBase + (k % kStages) * kStageBytes + 8192 * w;
 #pragma unroll
     for (int u = 0; u < 8; ++u)
-        v[u] = __builtin_bit_cast(u32x4,
-                                  __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(X.row_off[u] + step_off), 0, 0));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (__attribute__((address_space(3))) void *)(base + 1024 * u), 16,
+                                                 X.off[u], step_off, 0, 0);
 }
 
-__device__ inline void x_store(const u32x4 (&v)[8], const XStage &X, uint32_t stage_base)
+// s_waitcnt with only the vector-memory count constrained (gfx9 encoding)
+template <int N>
+__device__ inline void wait_vmcnt()
 {
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-        lds_store_b128(stage_base + X.lds_off + 32u * 128u * u, v[u]);
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-template <int Q>
-__device__ void tile_block(const TileParams &P, const DevBlock &blk, const Tile &T)
+// Workgroup barrier ordering LDS only: outstanding global loads stay in flight.
+__device__ inline void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// A fragments of one word (4 k-groups) of this lane's row.
+template <int Q, int W>
+__device__ inline void word_fragments(const u32x2 (&w)[Q], uint32_t lane_const, half8 (&a)[4])
+{
+    uint32_t d[8];
+    word_codes<Q, W>(w, d);
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+        a[b] = lookup8(d, b, lane_const);
+}
+
+// One LUT entry of the lane's row: code byte b of d (transposed code) -> fp16.
+__device__ inline _Float16 lookup1(uint32_t dj, int b, uint32_t lane_const)
+{
+    const uint32_t addr = __builtin_amdgcn_perm(dj, lane_const, 0x0C0C0000u | ((4u + b) << 8));
+    return *(const __attribute__((address_space(3))) _Float16 *)(uintptr_t)addr;
+}
+
+// One token stage: 4 k-groups x TTN token tiles of v_mfma_f32_32x32x16_f16 with the
+// A fragments `a`, while the next stage's fragments `an` are produced from word W of
+// `wn` (bit transpose + 32 lookups).  The work is laid out as 4*TTN bundles, one
+// MFMA each, fenced from one another: a bundle also requests the B fragment of the
+// same token tile for the next k-group (double-buffered) and its share of the
+// lookups, so LDS latency hides behind the matrix pipe of the previous bundles.
+template <int Q, int W, int TTN>
+__device__ inline void stage_product(const half8 (&a)[4], const u32x2 (&wn)[Q], uint32_t stage, const uint32_t (&bo)[4],
+                                     uint32_t lane_const, float16v (&acc)[TTN], half8 (&an)[4])
+{
+    constexpr int kBundles = 4 * TTN;
+    constexpr int kFirstLookup = kBundles / 8;  // bundles before it absorb the transpose
+    constexpr int kLookupBundles = kBundles - kFirstLookup;
+    // one address per k-group; token tiles are immediate offsets (the opaque stage
+    // base keeps the compiler from materialising one address per fragment)
+    stage = __builtin_amdgcn_readfirstlane(stage);
+    uint32_t sb[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+        sb[b] = stage + bo[b];
+    u32x4 xb[2][TTN];
+#pragma unroll
+    for (int tt = 0; tt < TTN; ++tt)
+        xb[0][tt] = lds_b128(sb[0] + 4096u * tt);
+    __builtin_amdgcn_sched_barrier(0);
+    uint32_t d[8];
+    word_codes<Q, W>(wn, d);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+#pragma unroll
+        for (int tt = 0; tt < TTN; ++tt) {
+            const int bundle = b * TTN + tt;
+            acc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[b], __builtin_bit_cast(half8, xb[b & 1][tt]), acc[tt], 0,
+                                                             0, 0);
+            if (b < 3)
+                xb[(b + 1) & 1][tt] = lds_b128(sb[b < 3 ? b + 1 : 3] + 4096u * tt);
+            if (bundle >= kFirstLookup) {
+                const int lb = bundle - kFirstLookup;
+                // lookups [32*lb/kLookupBundles, 32*(lb+1)/kLookupBundles)
+#pragma unroll
+                for (int li = 32 * lb / kLookupBundles; li < 32 * (lb + 1) / kLookupBundles; ++li)
+                    an[li >> 3][li & 7] = lookup1(d[li & 7], li >> 3, lane_const);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
+
+// TTN: token tiles computed (a power of two >= the tile's valid token tiles); rows
+// past the tile's last token repeat that token and are not written.
+template <int Q, int TTN>
+__device__ __attribute__((always_inline)) void tile_block(const TileParams &P, const DevBlock &blk, const Tile &T,
+                                                          char *smem)
 {
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
@@ -232,9 +317,12 @@ __device__ void tile_block(const TileParams &P, const DevBlock &blk, const Tile 
     const int i = lane & 31, g = lane >> 5;
     const int N = P.N, K = P.K;
     const int KT = K / kStepCols;
+    const int nst = 2 * KT;  // token stages (one per plane word)
     const int RT = (N + 31) / 32;
     const int rt = T.n0 / 32 + w;
     const uint32_t lane_word = (uint32_t)(rt < RT ? rt : 0) * (uint32_t)KT * 128u + 2u * lane;
+    // plane words of step st (clamped to the last step)
+    auto step_word = [&](int st) -> uint32_t { return lane_word + 128u * (uint32_t)(st < KT ? st : KT - 1); };
 
     __amdgpu_buffer_rsrc_t rs[Q];
 #pragma unroll
@@ -243,31 +331,31 @@ __device__ void tile_block(const TileParams &P, const DevBlock &blk, const Tile 
     const __amdgpu_buffer_rsrc_t rl = make_rsrc(blk.lut, (uint32_t)N << (Q + 1));
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(P.in, P.in_bytes);
 
-    // ---- token rows of this tile -------------------------------------------------
+    // ---- token rows: lane's slot in each of its wave's 8 copy instructions --------
     XStage X;
     {
-        const int c = tid & 7;
-        const int trb = tid >> 3;
+        const int slot = lane & 7;
+        // chunk c sits in slot c ^ ((tr / 2) % 8); for these rows (tr / 2) % 8 = 4 (u % 2) + lane / 16
+        uint32_t col_off[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int c = slot ^ ((4 * h + (lane >> 4)) & 7);
+            col_off[h] = (uint32_t)(64 * (c >> 2) + 8 * (c & 3)) * 2u;
+        }
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-            const int tr = min(trb + 32 * u, T.M - 1);
-            const int r = T.r0 + T.m0 + tr;
+            const int tr = 64 * w + 8 * u + (lane >> 3);
+            const int r = T.r0 + T.m0 + min(tr, T.M - 1);
             const int src = P.gather ? P.perm[r] / P.topk : r;
-            X.row_off[u] = (uint32_t)src * (uint32_t)K * 2u;
+            X.off[u] = (uint32_t)src * (uint32_t)K * 2u + col_off[u & 1];
         }
-        X.col_off = (uint32_t)(64 * (c >> 2) + 8 * (c & 3)) * 2u;
-        X.lds_off = (uint32_t)(trb * 128 + 16 * (c ^ ((trb >> 1) & 7)));
     }
-    // byte offset of stage s of step st relative to X.col_off: step st covers columns
-    // 128*st.., word s adds 32 columns
-    auto stage_off = [&](int idx) -> uint32_t {
-        return X.col_off + (uint32_t)((idx >> 1) * kStepCols + 32 * (idx & 1)) * 2u;
-    };
-
-    u32x4 xv[8];
-    x_load(xv, rx, X, stage_off(0));
-    u32x2 wc[Q];
-    load_planes<Q>(wc, rs, lane_word);
+    x_stage(smem, rx, X, w, 0);
+    if (nst > 1)
+        x_stage(smem, rx, X, w, 1);
+    u32x2 wc[Q], wn[Q], wnn[Q];
+    load_planes<Q>(wc, rs, step_word(0));
+    load_planes<Q>(wn, rs, step_word(1));
 
     // ---- LUT level Q of the tile's rows -> LDS (row pairs nl, nl+64 share a word) --
     {
@@ -278,7 +366,7 @@ __device__ void tile_block(const TileParams &P, const DevBlock &blk, const Tile 
         for (int jj = 0; jj < kPer; ++jj) {
             const int pc = tid + jj * kThreads;
             if (pc < kPairChunks) {
-                const int pr = pc / kChunksPerRow, ch = pc % kChunksPerRow;
+                const int pr = pc % 64, ch = pc / 64;  // lane -> row pair: distinct LDS banks
                 const int na = T.n0 + pr, nb = T.n0 + pr + 64;
                 const u32x4 za = {0, 0, 0, 0};
                 const u32x4 la = na < N ? __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
@@ -297,8 +385,8 @@ __device__ void tile_block(const TileParams &P, const DevBlock &blk, const Tile 
             }
         }
     }
-    x_store(xv, X, kXBase);
-    __syncthreads();
+    wait_vmcnt<0>();  // stages 0 and 1 and the first plane words have landed
+    lds_barrier();
 
     const uint32_t lane_const = (uint32_t)(4 * (32 * (w & 1) + i) + 2 * (w >> 1));
     // B fragment (token tile tt, k-group b of the stage): row 32tt + j, chunk 4g + b
@@ -306,62 +394,57 @@ __device__ void tile_block(const TileParams &P, const DevBlock &blk, const Tile 
 #pragma unroll
     for (int b = 0; b < 4; ++b)
         bo[b] = (uint32_t)(i * 128 + 16 * ((4 * g + b) ^ ((i >> 1) & 7)));
-    const int ntt = (T.M + 31) / 32;
+    const uint32_t xbase = lds_addr(smem) + kXBase;
 
-    float16v acc[kTT];
+    float16v acc[TTN];
 #pragma unroll
-    for (int tt = 0; tt < kTT; ++tt)
+    for (int tt = 0; tt < TTN; ++tt)
 #pragma unroll
         for (int v = 0; v < 16; ++v)
             acc[tt][v] = 0.f;
 
-    const int nstages = 2 * KT;
-    uint32_t word = lane_word;
-    u32x2 wn[Q];
-    for (int idx = 0; idx < nstages; ++idx) {
-        const int s = idx & 1;
-        const uint32_t cur = kXBase + (uint32_t)s * kStageBytes;
-        const bool more = idx + 1 < nstages;
+    half8 a0[4], a1[4];
+    word_fragments<Q, 0>(wc, lane_const, a0);
+    // Stage k: word k % 2 of step k / 2, ring buffer k % 3.  Stage k requests stage
+    // k + 2; an even stage also requests the plane words of step k / 2 + 2.  Before the
+    // barrier that ends stage k, stage k + 1 must have landed: everything issued
+    // before it is complete once at most (requests issued after it) are outstanding.
+    for (int st = 0; st < KT; ++st) {
+        const int k = 2 * st;
+        // even stage: A from a0 (word 0 of step st), next fragments from word 1 of wc
+        if (k + 2 < nst)
+            x_stage(smem, rx, X, w, k + 2);
+        load_planes<Q>(wnn, rs, step_word(st + 2));
+        stage_product<Q, 1, TTN>(a0, wc, xbase + (uint32_t)(k % kStages) * kStageBytes, bo, lane_const, acc, a1);
+        if (k + 2 < nst)
+            wait_vmcnt<8 + Q>();
+        else
+            wait_vmcnt<Q>();
+        lds_barrier();
+        // odd stage: A from a1 (word 1 of step st), next fragments from word 0 of wn
+        const bool more = k + 3 < nst;
         if (more)
-            x_load(xv, rx, X, stage_off(idx + 1));
-        uint32_t d[8];
-        if (s == 0) {
-            if (idx + 2 < nstages)
-                word += 128u;
-            load_planes<Q>(wn, rs, word);  // next step (the last step reloads its own words)
-            word_codes<Q, 0>(wc, d);
-        } else {
-            word_codes<Q, 1>(wc, d);
-        }
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const half8 a = lookup8(d, b, lane_const);
-#pragma unroll
-            for (int tt = 0; tt < kTT; ++tt) {
-                if (tt < ntt) {
-                    const u32x4 xb = lds_b128(cur + bo[b] + 4096u * tt);
-                    acc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, __builtin_bit_cast(half8, xb), acc[tt], 0, 0,
-                                                                     0);
-                }
-            }
-        }
+            x_stage(smem, rx, X, w, k + 3);
+        stage_product<Q, 0, TTN>(a1, wn, xbase + (uint32_t)((k + 1) % kStages) * kStageBytes, bo, lane_const, acc, a0);
         if (more)
-            x_store(xv, X, kXBase + (uint32_t)(s ^ 1) * kStageBytes);
-        if (s == 1) {
+            wait_vmcnt<8>();
+        else
+            wait_vmcnt<0>();
+        lds_barrier();
 #pragma unroll
-            for (int p = 0; p < Q; ++p)
-                wc[p] = wn[p];
+        for (int p = 0; p < Q; ++p) {
+            wc[p] = wn[p];
+            wn[p] = wnn[p];
         }
-        __syncthreads();
     }
 
     // ---- write: acc[tt][v] is token 32tt + (lane % 32), weight row
     //      32w + 8(v/4) + 4g + v%4; four consecutive rows per store ------------------
     const int j = i;
 #pragma unroll
-    for (int tt = 0; tt < kTT; ++tt) {
+    for (int tt = 0; tt < TTN; ++tt) {
         const int tok = 32 * tt + j;
-        if (tt < ntt && tok < T.M) {
+        if (tok < T.M) {
             const size_t orow = (size_t)(T.r0 + T.m0 + tok) * N;
 #pragma unroll
             for (int a4 = 0; a4 < 4; ++a4) {
@@ -398,24 +481,39 @@ __device__ void tile_block(const TileParams &P, const DevBlock &blk, const Tile 
     }
 }
 
+template <int TTN>
+__device__ __attribute__((always_inline)) void dispatch_q(const TileParams &P, const DevBlock &blk, const Tile &T,
+                                                          char *smem)
+{
+    switch (blk.q) {
+    case 3: tile_block<3, TTN>(P, blk, T, smem); break;
+    case 4: tile_block<4, TTN>(P, blk, T, smem); break;
+    case 5: tile_block<5, TTN>(P, blk, T, smem); break;
+    case 6: tile_block<6, TTN>(P, blk, T, smem); break;
+    case 7: tile_block<7, TTN>(P, blk, T, smem); break;
+    case 8: tile_block<8, TTN>(P, blk, T, smem); break;
+    default: break;  // unreachable: commit validates q
+    }
+}
+
 template <int KIND>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) tile_kernel(TileParams P)
 {
-    __shared__ __attribute__((aligned(16))) char smem[kLutBytes + 2 * kStageBytes];
+    __shared__ __attribute__((aligned(16))) char smem[kLutBytes + kStages * kStageBytes];
     Tile T;
     if (!resolve_tile(P, reinterpret_cast<int *>(smem + kXBase), T))
         return;
     __syncthreads();  // the scan scratch is reused as a token stage
     const DevBlock blk = P.table[2 * T.e + P.kind];
-    switch (blk.q) {
-    case 3: tile_block<3>(P, blk, T); break;
-    case 4: tile_block<4>(P, blk, T); break;
-    case 5: tile_block<5>(P, blk, T); break;
-    case 6: tile_block<6>(P, blk, T); break;
-    case 7: tile_block<7>(P, blk, T); break;
-    case 8: tile_block<8>(P, blk, T); break;
-    default: break;  // unreachable: commit validates q
-    }
+    const int ntt = (T.M + 31) / 32;
+    if (ntt > 4)
+        dispatch_q<8>(P, blk, T, smem);
+    else if (ntt > 2)
+        dispatch_q<4>(P, blk, T, smem);
+    else if (ntt > 1)
+        dispatch_q<2>(P, blk, T, smem);
+    else
+        dispatch_q<1>(P, blk, T, smem);
 }
 
 }  // namespace
