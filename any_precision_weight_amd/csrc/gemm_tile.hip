@@ -8,23 +8,31 @@
 // The weights are dequantised exactly (an fp16 LUT entry is the fp16 operand), so
 // the product is an fp16 MFMA GEMM whose A operand is produced by lookups.
 //
-// Tile: 128 weight rows x 256 expert rows (tokens).  Workgroup = 4 waves; wave w
-// owns weight rows 32w..32w+31 of the tile and all 256 tokens (8 column tiles of
-// v_mfma_f32_32x32x16_f16, 8 x 16 fp32 accumulators per lane).  A lane decodes its
-// own weight row: per 128-column step it loads, for each needed plane, the two
-// words of its row (64 columns, the same tiled layout as the decode product), turns
-// them into codes with an 8x8 bit transpose and looks the codes up in LUT_q staged
-// in LDS.  Each decoded A fragment is reused by the 8 token tiles; the token rows
-// (B operand) are staged in LDS, 64 columns at a time, double-buffered.
+// Tile: 128 weight rows x 256 expert rows (tokens), one workgroup of 8 waves with
+// split roles (two waves per SIMD, so the decoding VALU work of one overlaps the
+// matrix pipe of the other):
+//   producer wave p (waves 4..7) decodes weight rows 32p..32p+31: per 64-column
+//     stage a lane loads, for each needed plane, one word of its row (same tiled
+//     layout as the decode product), turns the 32 columns into codes with an 8x8 bit
+//     transpose, looks them up in LUT_q (LDS) and writes the four fp16 A fragments to
+//     the stage's A buffer; it also copies its quarter of the stage's token rows
+//     global -> registers (two stages ahead) -> LDS.
+//   consumer wave c (waves 0..3) multiplies weight rows 64(c%2)..+63 (two A row
+//     sets) by tokens 128(c/2)..+127 (four token tiles) with v_mfma_f32_32x32x16_f16,
+//     2 x 4 x 16 fp32 accumulators per lane; each B fragment serves two A fragments.
+// Stage n (word n%2 of 128-column step n/2) is produced in phase n and consumed in
+// phase n+1; one workgroup barrier ends each phase, and stage buffers alternate.
 //
-// LDS (128 KB, one workgroup per CU):
+// LDS (160 KB, one workgroup per CU):
 //   [0, 64 KB)    LUT_q of the tile's 128 rows: entry (row nl, code) at
 //                 v*256 + 4*(nl % 64) + 2*(nl / 64), v = code with its q bits reversed
 //                 (the transposed code byte), so a lookup address is one v_perm.
-//   [64, 128 KB)  two 32 KB stages of 256 token rows x 64 columns fp16; row tr holds
+//   [64, 128 KB)  two 32 KB token stages of 256 rows x 64 columns fp16; row tr holds
 //                 eight 16-byte chunks (chunk c = columns 64*(c/4) + 32*s + 8*(c%4) of
 //                 the step, s the stage's word), stored at chunk c ^ ((tr/2) % 8) so that
 //                 16 lanes reading one chunk of 16 consecutive rows hit distinct banks.
+//   [128, 160 KB) two 16 KB A stages: fragment (producer p, k-group b) of lane L at
+//                 ((4p + b) * 64 + L) * 16.
 //
 // Tile order: tiles of one expert are grouped as (8 weight-row tiles) x (all token
 // tiles), consecutive tiles run on the same XCD (workgroup b runs on XCD b % 8), so
@@ -35,15 +43,28 @@ namespace apmoe {
 namespace {
 
 constexpr int kWave = 64;
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;  // 4 consumer + 4 producer waves
 constexpr int kBN = 128;  // weight rows per tile
 constexpr int kBM = kTileTokens;  // token rows per tile (256)
-constexpr int kTT = kBM / 32;      // MFMA column tiles
 constexpr int kStepCols = 128;
 constexpr int kLutBytes = 64 * 1024;
-constexpr int kStageBytes = kBM * 64 * 2;  // 32 KB
-constexpr int kStages = 3;                  // token stages in flight (ring)
-constexpr int kXBase = kLutBytes;
+constexpr int kStageBytes = kBM * 64 * 2;  // 32 KB token stage
+constexpr int kAStageBytes = 16 * 1024;     // A fragments of one stage
+constexpr int kLdsBytes = 160 * 1024;
+
+// LDS layout for bitwidth Q: LUT_Q (2^Q x 256 bytes), then NXB token buffers, then
+// two A buffers.  NXB = 3 where the LUT leaves room (Q <= 7), else 2.  A token stage
+// is requested D = NXB - 2 phases before the phase it must land in (one buffer is
+// being read, one is landing).
+template <int Q>
+struct Layout {
+    static constexpr int kLut = (1 << Q) * 256;
+    static constexpr int kNxb = kLut <= 32 * 1024 ? 3 : 2;
+    static constexpr int kD = kNxb - 2;
+    static constexpr int kX = kLut;
+    static constexpr int kA = kX + kNxb * kStageBytes;
+    static_assert(kA + 2 * kAStageBytes <= kLdsBytes, "LDS budget");
+};
 constexpr int kGroupN = 8;  // weight-row tiles per group
 constexpr int kXcds = 8;
 
@@ -99,7 +120,7 @@ struct Tile {
     int e, r0, m0, M, n0;
 };
 
-// Workgroup -> tile.  Every thread computes the same answer; E <= 256 = blockDim.
+// Workgroup -> tile.  Every thread computes the same answer; E <= 256 < blockDim.
 __device__ __attribute__((always_inline)) bool resolve_tile(const TileParams &P, int *scan, Tile &T)
 {
     const int tid = threadIdx.x;
@@ -180,18 +201,6 @@ __device__ inline void word_codes(const u32x2 (&w)[Q], uint32_t (&d)[8])
     transpose8x8(d);
 }
 
-// A fragment for k-group b of a word: the 8 LUT entries of columns 8b..8b+7.
-__device__ inline half8 lookup8(const uint32_t (&d)[8], int b, uint32_t lane_const)
-{
-    half8 a;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const uint32_t addr = __builtin_amdgcn_perm(d[j], lane_const, 0x0C0C0000u | ((4u + b) << 8));
-        a[j] = *(const __attribute__((address_space(3))) _Float16 *)(uintptr_t)addr;
-    }
-    return a;
-}
-
 __device__ inline u32x4 lds_b128(uint32_t addr)
 {
     return *(const __attribute__((address_space(3))) u32x4 *)(uintptr_t)addr;
@@ -203,162 +212,131 @@ __device__ inline void lds_store_b128(uint32_t addr, u32x4 v)
 }
 
 // Token stages are copied global -> LDS by the buffer unit (buffer_load ... lds):
-// one instruction writes 64 x 16 bytes at consecutive LDS addresses, so wave w,
-// instruction u fills rows 64w + 8u .. +7 of a stage, lane L the 16-byte slot L % 8
-// of row 64w + 8u + L / 8, and fetches the token chunk stored in that slot.
+// one instruction writes 64 x 16 bytes at consecutive LDS addresses, so producer p,
+// instruction u fills rows 64p + 8u .. +7 of a stage, lane L the 16-byte slot L % 8
+// of row 64p + 8u + L / 8, and fetches the token chunk stored in that slot.
 struct XStage {
     uint32_t off[8];  // byte offset of the lane's chunk (token row + column) for instruction u
 };
 
 __device__ inline uint32_t lds_addr(const void *p) { return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)p; }
 
-// Stage k = word (k % 2) of step k / 2 into ring buffer k % 3.
-__device__ inline void x_stage(char *smem, __amdgpu_buffer_rsrc_t rx, const XStage &X, int w, int k)
+// Token stage n (word n % 2 of step n / 2, clamped to the last stage) into the LDS
+// buffer at `dst` (this producer's quarter).
+__device__ inline void x_stage(char *dst, __amdgpu_buffer_rsrc_t rx, const XStage &X, int n, int nst)
 {
-    const uint32_t step_off = (uint32_t)((k >> 1) * kStepCols * 2 + (k & 1) * 64);  // scalar offset
-    char *base = smem + kXBase + (k % kStages) * kStageBytes + 8192 * w;
+    n = n < nst ? n : nst - 1;
+    const uint32_t step_off = (uint32_t)((n >> 1) * kStepCols * 2 + (n & 1) * 64);  // scalar offset
 #pragma unroll
     for (int u = 0; u < 8; ++u)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (__attribute__((address_space(3))) void *)(base + 1024 * u), 16,
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (__attribute__((address_space(3))) void *)(dst + 1024 * u), 16,
                                                  X.off[u], step_off, 0, 0);
 }
 
-// s_waitcnt with only the vector-memory count constrained (gfx9 encoding)
-template <int N>
-__device__ inline void wait_vmcnt()
+// Workgroup barrier for the phase pipeline.  The wave's LDS accesses are complete
+// (lgkmcnt 0) and at most VM vector-memory requests -- token copies into LDS among
+// them -- are outstanding; a memory fence here would wait for every token copy, so
+// the barrier is an s_barrier with a memory clobber (no compiler reordering of memory
+// accesses across it) preceded by explicit waits.
+template <int VM>
+__device__ inline void phase_barrier()
 {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+    static_assert(VM >= 0 && VM < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | (0 << 8) | ((VM >> 4) << 14));
+    asm volatile("s_barrier" ::: "memory");
 }
 
-// Workgroup barrier ordering LDS only: outstanding global loads stay in flight.
-__device__ inline void lds_barrier()
-{
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
-// A fragments of one word (4 k-groups) of this lane's row.
-template <int Q, int W>
-__device__ inline void word_fragments(const u32x2 (&w)[Q], uint32_t lane_const, half8 (&a)[4])
-{
-    uint32_t d[8];
-    word_codes<Q, W>(w, d);
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-        a[b] = lookup8(d, b, lane_const);
-}
-
-// One LUT entry of the lane's row: code byte b of d (transposed code) -> fp16.
+// One LUT entry of the lane's row: code byte b of dj (transposed code) -> fp16.
 __device__ inline _Float16 lookup1(uint32_t dj, int b, uint32_t lane_const)
 {
     const uint32_t addr = __builtin_amdgcn_perm(dj, lane_const, 0x0C0C0000u | ((4u + b) << 8));
     return *(const __attribute__((address_space(3))) _Float16 *)(uintptr_t)addr;
 }
 
-// One token stage: 4 k-groups x TTN token tiles of v_mfma_f32_32x32x16_f16 with the
-// A fragments `a`, while the next stage's fragments `an` are produced from word W of
-// `wn` (bit transpose + 32 lookups).  The work is laid out as 4*TTN bundles, one
-// MFMA each, fenced from one another: a bundle also requests the B fragment of the
-// same token tile for the next k-group (double-buffered) and its share of the
-// lookups, so LDS latency hides behind the matrix pipe of the previous bundles.
-template <int Q, int W, int TTN>
-__device__ inline void stage_product(const half8 (&a)[4], const u32x2 (&wn)[Q], uint32_t stage, const uint32_t (&bo)[4],
-                                     uint32_t lane_const, float16v (&acc)[TTN], half8 (&an)[4])
+// Producer side of one stage: the lane's 32 weights of word W of `wc` -> four fp16 A
+// fragments in the A buffer.
+template <int Q, int W>
+__device__ inline void produce_a(const u32x2 (&wc)[Q], uint32_t lane_const, uint32_t a_dst)
 {
-    constexpr int kBundles = 4 * TTN;
-    constexpr int kFirstLookup = kBundles / 8;  // bundles before it absorb the transpose
-    constexpr int kLookupBundles = kBundles - kFirstLookup;
-    // one address per k-group; token tiles are immediate offsets (the opaque stage
-    // base keeps the compiler from materialising one address per fragment)
-    stage = __builtin_amdgcn_readfirstlane(stage);
+    uint32_t d[8];
+    word_codes<Q, W>(wc, d);
+    half8 a[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            a[b][j] = lookup1(d[j], b, lane_const);
+    __builtin_amdgcn_sched_barrier(0);  // every lookup is requested before the first is used
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+        lds_store_b128(a_dst + 1024u * b, __builtin_bit_cast(u32x4, a[b]));
+}
+
+// Consumer side of one stage: 4 k-groups x 2 row sets x TTN token tiles.  A
+// fragments of the stage and the B fragments of k-group 0 are requested first; the
+// B fragments of k-group b+1 are requested while k-group b multiplies (fenced
+// bundles of one MFMA and at most one LDS read).
+template <int TTN>
+__device__ inline void consume(uint32_t a_stage, uint32_t a_lane, uint32_t x_stage, const uint32_t (&bo)[4],
+                               float16v (&acc)[2][TTN])
+{
+    // stage bases are wave-uniform; the per-lane parts are a_lane and bo
+    const uint32_t a_src = __builtin_amdgcn_readfirstlane(a_stage) + a_lane;
+    const uint32_t x_src = __builtin_amdgcn_readfirstlane(x_stage);
+    half8 a[2][4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+            a[h][b] = __builtin_bit_cast(half8, lds_b128(a_src + 4096u * h + 1024u * b));
     uint32_t sb[4];
 #pragma unroll
     for (int b = 0; b < 4; ++b)
-        sb[b] = stage + bo[b];
+        sb[b] = x_src + bo[b];
     u32x4 xb[2][TTN];
 #pragma unroll
     for (int tt = 0; tt < TTN; ++tt)
         xb[0][tt] = lds_b128(sb[0] + 4096u * tt);
     __builtin_amdgcn_sched_barrier(0);
-    uint32_t d[8];
-    word_codes<Q, W>(wn, d);
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
 #pragma unroll
-        for (int tt = 0; tt < TTN; ++tt) {
-            const int bundle = b * TTN + tt;
-            acc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[b], __builtin_bit_cast(half8, xb[b & 1][tt]), acc[tt], 0,
-                                                             0, 0);
-            if (b < 3)
-                xb[(b + 1) & 1][tt] = lds_b128(sb[b < 3 ? b + 1 : 3] + 4096u * tt);
-            if (bundle >= kFirstLookup) {
-                const int lb = bundle - kFirstLookup;
-                // lookups [32*lb/kLookupBundles, 32*(lb+1)/kLookupBundles)
+        for (int h = 0; h < 2; ++h) {
 #pragma unroll
-                for (int li = 32 * lb / kLookupBundles; li < 32 * (lb + 1) / kLookupBundles; ++li)
-                    an[li >> 3][li & 7] = lookup1(d[li & 7], li >> 3, lane_const);
+            for (int tt = 0; tt < TTN; ++tt) {
+                acc[h][tt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[h][b], __builtin_bit_cast(half8, xb[b & 1][tt]),
+                                                                    acc[h][tt], 0, 0, 0);
+                if (h == 0 && b < 3)
+                    xb[(b + 1) & 1][tt] = lds_b128(sb[b < 3 ? b + 1 : 3] + 4096u * tt);
+                __builtin_amdgcn_sched_barrier(0);
             }
-            __builtin_amdgcn_sched_barrier(0);
         }
     }
 }
 
-// TTN: token tiles computed (a power of two >= the tile's valid token tiles); rows
-// past the tile's last token repeat that token and are not written.
+// TTN: token tiles per consumer (a power of two, at most 4); consumers whose token
+// half holds no row of the tile skip their products.  Rows past the tile's last
+// token repeat that token and are not written.
 template <int Q, int TTN>
 __device__ __attribute__((always_inline)) void tile_block(const TileParams &P, const DevBlock &blk, const Tile &T,
                                                           char *smem)
 {
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
-    const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const bool producer = wave >= 4;
+    const int pw = wave & 3;  // producer index / consumer index
     const int i = lane & 31, g = lane >> 5;
     const int N = P.N, K = P.K;
     const int KT = K / kStepCols;
-    const int nst = 2 * KT;  // token stages (one per plane word)
-    const int RT = (N + 31) / 32;
-    const int rt = T.n0 / 32 + w;
-    const uint32_t lane_word = (uint32_t)(rt < RT ? rt : 0) * (uint32_t)KT * 128u + 2u * lane;
-    // plane words of step st (clamped to the last step)
-    auto step_word = [&](int st) -> uint32_t { return lane_word + 128u * (uint32_t)(st < KT ? st : KT - 1); };
+    const int KT2 = (KT + 1) & ~1;  // steps rounded up to even (the pipeline runs two per loop)
+    const int nst = 2 * KT;         // token stages (one per plane word)
+    const uint32_t base = lds_addr(smem);
 
-    __amdgpu_buffer_rsrc_t rs[Q];
-#pragma unroll
-    for (int p = 0; p < Q; ++p)
-        rs[p] = make_rsrc(blk.plane[p], P.plane_bytes);
-    const __amdgpu_buffer_rsrc_t rl = make_rsrc(blk.lut, (uint32_t)N << (Q + 1));
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(P.in, P.in_bytes);
-
-    // ---- token rows: lane's slot in each of its wave's 8 copy instructions --------
-    XStage X;
+    // ---- LUT level Q of the tile's rows -> LDS (row pairs nl, nl+64 share a word;
+    //      lane -> row pair, so the writes of a wave hit distinct banks) ----------------
     {
-        const int slot = lane & 7;
-        // chunk c sits in slot c ^ ((tr / 2) % 8); for these rows (tr / 2) % 8 = 4 (u % 2) + lane / 16
-        uint32_t col_off[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int c = slot ^ ((4 * h + (lane >> 4)) & 7);
-            col_off[h] = (uint32_t)(64 * (c >> 2) + 8 * (c & 3)) * 2u;
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int tr = 64 * w + 8 * u + (lane >> 3);
-            const int r = T.r0 + T.m0 + min(tr, T.M - 1);
-            const int src = P.gather ? P.perm[r] / P.topk : r;
-            X.off[u] = (uint32_t)src * (uint32_t)K * 2u + col_off[u & 1];
-        }
-    }
-    x_stage(smem, rx, X, w, 0);
-    if (nst > 1)
-        x_stage(smem, rx, X, w, 1);
-    u32x2 wc[Q], wn[Q], wnn[Q];
-    load_planes<Q>(wc, rs, step_word(0));
-    load_planes<Q>(wn, rs, step_word(1));
-
-    // ---- LUT level Q of the tile's rows -> LDS (row pairs nl, nl+64 share a word) --
-    {
+        const __amdgpu_buffer_rsrc_t rl = make_rsrc(blk.lut, (uint32_t)N << (Q + 1));
         constexpr int kChunksPerRow = (1 << Q) / 8;  // 16-byte chunks of one row
         constexpr int kPairChunks = 64 * kChunksPerRow;
         constexpr int kPer = (kPairChunks + kThreads - 1) / kThreads;
@@ -366,7 +344,7 @@ __device__ __attribute__((always_inline)) void tile_block(const TileParams &P, c
         for (int jj = 0; jj < kPer; ++jj) {
             const int pc = tid + jj * kThreads;
             if (pc < kPairChunks) {
-                const int pr = pc % 64, ch = pc / 64;  // lane -> row pair: distinct LDS banks
+                const int pr = pc % 64, ch = pc / 64;
                 const int na = T.n0 + pr, nb = T.n0 + pr + 64;
                 const u32x4 za = {0, 0, 0, 0};
                 const u32x4 la = na < N ? __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
@@ -385,95 +363,170 @@ __device__ __attribute__((always_inline)) void tile_block(const TileParams &P, c
             }
         }
     }
-    wait_vmcnt<0>();  // stages 0 and 1 and the first plane words have landed
-    lds_barrier();
 
-    const uint32_t lane_const = (uint32_t)(4 * (32 * (w & 1) + i) + 2 * (w >> 1));
-    // B fragment (token tile tt, k-group b of the stage): row 32tt + j, chunk 4g + b
+    if (producer) {
+        // ---------------------------------------------------------------- producer
+        const int RT = (N + 31) / 32;
+        const int rt = T.n0 / 32 + pw;
+        const uint32_t lane_word = (uint32_t)(rt < RT ? rt : 0) * (uint32_t)KT * 128u + 2u * lane;
+        auto step_word = [&](int st) -> uint32_t { return lane_word + 128u * (uint32_t)(st < KT ? st : KT - 1); };
+        __amdgpu_buffer_rsrc_t rs[Q];
+#pragma unroll
+        for (int p = 0; p < Q; ++p)
+            rs[p] = make_rsrc(blk.plane[p], P.plane_bytes);
+        const __amdgpu_buffer_rsrc_t rx = make_rsrc(P.in, P.in_bytes);
+        XStage X;
+        {
+            const int slot = lane & 7;
+            // chunk c sits in slot c ^ ((tr / 2) % 8); for these rows (tr / 2) % 8 = 4 (u % 2) + lane / 16
+            uint32_t col_off[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int c = slot ^ ((4 * h + (lane >> 4)) & 7);
+                col_off[h] = (uint32_t)(64 * (c >> 2) + 8 * (c & 3)) * 2u;
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int tr = 64 * pw + 8 * u + (lane >> 3);
+                const int r = T.r0 + T.m0 + min(tr, T.M - 1);
+                const int src = P.gather ? P.perm[r] / P.topk : r;
+                X.off[u] = (uint32_t)src * (uint32_t)K * 2u + col_off[u & 1];
+            }
+        }
+        const uint32_t lane_const = (uint32_t)(4 * (32 * (pw & 1) + i) + 2 * (pw >> 1));
+        const uint32_t a_dst = base + Layout<Q>::kA + (uint32_t)(pw * 4 * 1024 + lane * 16);
+        using L = Layout<Q>;
+        constexpr int D = L::kD;
+        char *x_dst = smem + L::kX + 8192 * pw;
+        u32x2 pa[Q], pb[Q];  // plane words of even / odd steps
+        // Phase n: request token stage n + D into buffer (n + D) % NXB (last read by the
+        // consumers in phase n - 1), then -- in even phases -- the plane words of step
+        // n/2 + 1, then produce A of stage n.  At the end of phase n token stage n must
+        // have landed; the requests issued after it are 8 D token copies plus the plane
+        // words of the even phases among n - D .. n (the oldest of those are due two
+        // phases later anyway): wait until at most that many are outstanding.
+        constexpr int kWaitOdd = 8 * D + Q * (D == 0 ? 0 : 1);
+        constexpr int kWaitEven = 8 * D + Q;
+        auto xbuf = [&](int n) -> char * { return x_dst + (n % L::kNxb) * kStageBytes; };
+        load_planes<Q>(pa, rs, step_word(0));
+#pragma unroll
+        for (int n = 0; n < D; ++n)
+            x_stage(xbuf(n), rx, X, n, nst);
+        phase_barrier<Q + 8 * D>();  // the LUT written by all waves is visible
+        // phase 0: stage 0 = word 0 of step 0
+        x_stage(xbuf(D), rx, X, D, nst);
+        __builtin_amdgcn_sched_barrier(0);
+        load_planes<Q>(pb, rs, step_word(1));
+        produce_a<Q, 0>(pa, lane_const, a_dst);
+        phase_barrier<kWaitEven>();
+        for (int m = 0; m < KT2 / 2; ++m) {
+            const int n = 4 * m;
+            // phase n+1: stage n+1 = word 1 of step 2m -> A buffer 1
+            x_stage(xbuf(n + 1 + D), rx, X, n + 1 + D, nst);
+            produce_a<Q, 1>(pa, lane_const, a_dst + kAStageBytes);
+            phase_barrier<kWaitOdd>();
+            // phase n+2: stage n+2 = word 0 of step 2m+1 -> A buffer 0
+            x_stage(xbuf(n + 2 + D), rx, X, n + 2 + D, nst);
+            __builtin_amdgcn_sched_barrier(0);  // the plane requests follow the token copies
+            load_planes<Q>(pa, rs, step_word(2 * m + 2));
+            produce_a<Q, 0>(pb, lane_const, a_dst);
+            phase_barrier<kWaitEven>();
+            // phase n+3: stage n+3 = word 1 of step 2m+1 -> A buffer 1
+            x_stage(xbuf(n + 3 + D), rx, X, n + 3 + D, nst);
+            produce_a<Q, 1>(pb, lane_const, a_dst + kAStageBytes);
+            phase_barrier<kWaitOdd>();
+            // phase n+4: stage n+4 = word 0 of step 2m+2 -> A buffer 0
+            x_stage(xbuf(n + 4 + D), rx, X, n + 4 + D, nst);
+            __builtin_amdgcn_sched_barrier(0);
+            load_planes<Q>(pb, rs, step_word(2 * m + 3));
+            produce_a<Q, 0>(pa, lane_const, a_dst);
+            phase_barrier<kWaitEven>();
+        }
+        return;
+    }
+
+    // -------------------------------------------------------------------- consumer
+    const int c = pw;
+    const int ntt = (T.M + 31) / 32;
+    const bool active = 4 * (c >> 1) < ntt;  // this token half holds rows of the tile
+    // B fragment (token tile tt of this half, k-group b): row 128(c/2) + 32tt + j, chunk 4g + b
     uint32_t bo[4];
 #pragma unroll
     for (int b = 0; b < 4; ++b)
-        bo[b] = (uint32_t)(i * 128 + 16 * ((4 * g + b) ^ ((i >> 1) & 7)));
-    const uint32_t xbase = lds_addr(smem) + kXBase;
+        bo[b] = (uint32_t)((128 * (c >> 1) + i) * 128 + 16 * ((4 * g + b) ^ ((i >> 1) & 7)));
+    using L = Layout<Q>;
+    const uint32_t a_stage = base + L::kA + (uint32_t)((2 * (c & 1)) * 4 * 1024);  // row sets 2(c%2), +1
+    const uint32_t a_lane = (uint32_t)(lane * 16);
+    auto xsrc = [&](int s) -> uint32_t { return base + L::kX + (uint32_t)((s % L::kNxb) * kStageBytes); };
 
-    float16v acc[TTN];
+    float16v acc[2][TTN];
 #pragma unroll
-    for (int tt = 0; tt < TTN; ++tt)
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int v = 0; v < 16; ++v)
-            acc[tt][v] = 0.f;
+        for (int tt = 0; tt < TTN; ++tt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                acc[h][tt][v] = 0.f;
 
-    half8 a0[4], a1[4];
-    word_fragments<Q, 0>(wc, lane_const, a0);
-    // Stage k: word k % 2 of step k / 2, ring buffer k % 3.  Stage k requests stage
-    // k + 2; an even stage also requests the plane words of step k / 2 + 2.  Before the
-    // barrier that ends stage k, stage k + 1 must have landed: everything issued
-    // before it is complete once at most (requests issued after it) are outstanding.
-    for (int st = 0; st < KT; ++st) {
-        const int k = 2 * st;
-        // even stage: A from a0 (word 0 of step st), next fragments from word 1 of wc
-        if (k + 2 < nst)
-            x_stage(smem, rx, X, w, k + 2);
-        load_planes<Q>(wnn, rs, step_word(st + 2));
-        stage_product<Q, 1, TTN>(a0, wc, xbase + (uint32_t)(k % kStages) * kStageBytes, bo, lane_const, acc, a1);
-        if (k + 2 < nst)
-            wait_vmcnt<8 + Q>();
-        else
-            wait_vmcnt<Q>();
-        lds_barrier();
-        // odd stage: A from a1 (word 1 of step st), next fragments from word 0 of wn
-        const bool more = k + 3 < nst;
-        if (more)
-            x_stage(smem, rx, X, w, k + 3);
-        stage_product<Q, 0, TTN>(a1, wn, xbase + (uint32_t)((k + 1) % kStages) * kStageBytes, bo, lane_const, acc, a0);
-        if (more)
-            wait_vmcnt<8>();
-        else
-            wait_vmcnt<0>();
-        lds_barrier();
-#pragma unroll
-        for (int p = 0; p < Q; ++p) {
-            wc[p] = wn[p];
-            wn[p] = wnn[p];
-        }
+    phase_barrier<0>();  // the LUT written by all waves is visible
+    phase_barrier<0>();  // phase 0: stage 0 is being produced
+    for (int m = 0; m < KT2 / 2; ++m) {
+        const int n = 4 * m;  // phases n+1 .. n+4 consume stages n .. n+3
+        if (active)
+            consume<TTN>(a_stage, a_lane, xsrc(n), bo, acc);
+        phase_barrier<0>();
+        if (active)
+            consume<TTN>(a_stage + kAStageBytes, a_lane, xsrc(n + 1), bo, acc);
+        phase_barrier<0>();
+        if (active && n + 2 < nst)
+            consume<TTN>(a_stage, a_lane, xsrc(n + 2), bo, acc);
+        phase_barrier<0>();
+        if (active && n + 3 < nst)
+            consume<TTN>(a_stage + kAStageBytes, a_lane, xsrc(n + 3), bo, acc);
+        phase_barrier<0>();
     }
+    if (!active)
+        return;
 
-    // ---- write: acc[tt][v] is token 32tt + (lane % 32), weight row
-    //      32w + 8(v/4) + 4g + v%4; four consecutive rows per store ------------------
+    // ---- write: acc[h][tt][v] is token 128(c/2) + 32tt + (lane % 32), weight row
+    //      64(c%2) + 32h + 8(v/4) + 4g + v%4; four consecutive rows per store ----------
     const int j = i;
 #pragma unroll
     for (int tt = 0; tt < TTN; ++tt) {
-        const int tok = 32 * tt + j;
+        const int tok = 128 * (c >> 1) + 32 * tt + j;
         if (tok < T.M) {
             const size_t orow = (size_t)(T.r0 + T.m0 + tok) * N;
 #pragma unroll
-            for (int a4 = 0; a4 < 4; ++a4) {
-                const int n = T.n0 + 32 * w + 8 * a4 + 4 * g;
-                if (P.out_f32) {
-                    float *o = reinterpret_cast<float *>(P.out) + orow + n;
-                    if ((N & 3) == 0 && n + 3 < N) {
-                        *reinterpret_cast<float4 *>(o) =
-                            make_float4(acc[tt][4 * a4], acc[tt][4 * a4 + 1], acc[tt][4 * a4 + 2], acc[tt][4 * a4 + 3]);
+            for (int h = 0; h < 2; ++h) {
+#pragma unroll
+                for (int a4 = 0; a4 < 4; ++a4) {
+                    const int n = T.n0 + 64 * (c & 1) + 32 * h + 8 * a4 + 4 * g;
+                    const float16v &A = acc[h][tt];
+                    if (P.out_f32) {
+                        float *o = reinterpret_cast<float *>(P.out) + orow + n;
+                        if ((N & 3) == 0 && n + 3 < N) {
+                            *reinterpret_cast<float4 *>(o) = make_float4(A[4 * a4], A[4 * a4 + 1], A[4 * a4 + 2], A[4 * a4 + 3]);
+                        } else {
+#pragma unroll
+                            for (int b = 0; b < 4; ++b)
+                                if (n + b < N)
+                                    o[b] = A[4 * a4 + b];
+                        }
                     } else {
+                        _Float16 *o = reinterpret_cast<_Float16 *>(P.out) + orow + n;
+                        if ((N & 3) == 0 && n + 3 < N) {
+                            typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+                            half4 hv;
 #pragma unroll
-                        for (int b = 0; b < 4; ++b)
-                            if (n + b < N)
-                                o[b] = acc[tt][4 * a4 + b];
-                    }
-                } else {
-                    _Float16 *o = reinterpret_cast<_Float16 *>(P.out) + orow + n;
-                    if ((N & 3) == 0 && n + 3 < N) {
-                        typedef _Float16 half4 __attribute__((ext_vector_type(4)));
-                        half4 h;
+                            for (int b = 0; b < 4; ++b)
+                                hv[b] = (_Float16)A[4 * a4 + b];
+                            *reinterpret_cast<half4 *>(o) = hv;
+                        } else {
 #pragma unroll
-                        for (int b = 0; b < 4; ++b)
-                            h[b] = (_Float16)acc[tt][4 * a4 + b];
-                        *reinterpret_cast<half4 *>(o) = h;
-                    } else {
-#pragma unroll
-                        for (int b = 0; b < 4; ++b)
-                            if (n + b < N)
-                                o[b] = (_Float16)acc[tt][4 * a4 + b];
+                            for (int b = 0; b < 4; ++b)
+                                if (n + b < N)
+                                    o[b] = (_Float16)A[4 * a4 + b];
+                        }
                     }
                 }
             }
@@ -497,18 +550,16 @@ __device__ __attribute__((always_inline)) void dispatch_q(const TileParams &P, c
 }
 
 template <int KIND>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) tile_kernel(TileParams P)
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) tile_kernel(TileParams P)
 {
-    __shared__ __attribute__((aligned(16))) char smem[kLutBytes + kStages * kStageBytes];
+    __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
     Tile T;
-    if (!resolve_tile(P, reinterpret_cast<int *>(smem + kXBase), T))
+    if (!resolve_tile(P, reinterpret_cast<int *>(smem + kLdsBytes - kThreads * sizeof(int)), T))
         return;
     __syncthreads();  // the scan scratch is reused as a token stage
     const DevBlock blk = P.table[2 * T.e + P.kind];
-    const int ntt = (T.M + 31) / 32;
-    if (ntt > 4)
-        dispatch_q<8>(P, blk, T, smem);
-    else if (ntt > 2)
+    const int ntt = (T.M + 31) / 32;  // token tiles of the tile (two halves of at most 4)
+    if (ntt > 2)
         dispatch_q<4>(P, blk, T, smem);
     else if (ntt > 1)
         dispatch_q<2>(P, blk, T, smem);
