@@ -110,6 +110,36 @@ __device__ inline void load_x_group(u32x4 (&xg)[4], __amdgpu_buffer_rsrc_t rx, u
 }
 
 // 4 MFMAs over one 32-column word of each needed plane: unpack, LUT gather, multiply.
+// q = 3, two weights per lookup: the transpose input is the 3 plane words and the
+// same words shifted down one column, so output byte b of d[j] (j even) holds the
+// transposed codes of columns 8b+j (bits 0..2) and 8b+j+1 (bits 3..5) -- an index
+// into the pair table of LUT_3 (entry = two fp16, the even column's in the low half).
+// One ds_read_b32 per pair yields two A-operand elements with no repacking.
+template <int W>
+__device__ inline void group_product_pair3(const u32x2 (&w)[3], const u32x4 (&xg)[4], uint32_t lut_base,
+                                           uint32_t lane_const, float16v &acc)
+{
+    uint32_t d[8];
+#pragma unroll
+    for (int p = 0; p < 3; ++p) {
+        d[p] = w[p][W];
+        d[3 + p] = w[p][W] >> 1;
+    }
+    d[6] = d[7] = 0u;
+    transpose8x8(d);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        u32x4 a;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const uint32_t addr = __builtin_amdgcn_perm(d[2 * jj], lane_const, 0x0C0C0000u | ((4u + b) << 8));
+            a[jj] = *reinterpret_cast<const __attribute__((address_space(3))) uint32_t *>((uintptr_t)(lut_base + addr));
+        }
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, a), __builtin_bit_cast(half8, xg[b]), acc,
+                                                     0, 0, 0);
+    }
+}
+
 template <int Q, int W>
 __device__ inline void group_product(const u32x2 (&w)[Q], const u32x4 (&xg)[4], uint32_t lut_base,
                                      uint32_t lane_const, float16v &acc)
@@ -164,52 +194,75 @@ __device__ void gemm_block(const GemmParams &P, const DevBlock &blk, int rb, int
     const __amdgpu_buffer_rsrc_t rl = make_rsrc(blk.lut, (uint32_t)N << (Q + 1));
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(P.in, P.in_bytes);
 
-    // ---- LUT level Q of rows n0..n0+63: 16-byte loads (8 entries of one row),
-    //      lane -> row so that one wave touches 64 rows ----------------------------
-    constexpr int kLutU4 = (kRows << Q) / 8;
-    constexpr int kPer = (kLutU4 + kThreads - 1) / kThreads;
-    constexpr int kBatch = kPer < 4 ? kPer : 4;  // loads in flight per batch (register budget)
     u32x2 wc[Q];
-#pragma unroll
-    for (int j0 = 0; j0 < kPer; j0 += kBatch) {
-        u32x4 lv[kBatch];
-#pragma unroll
-        for (int jj = 0; jj < kBatch; ++jj) {
-            const int idx = tid + (j0 + jj) * kThreads;
-            const int nl = idx % kRows, ch = idx / kRows;
-            const bool ok = idx < kLutU4 && n0 + nl < N;
-            lv[jj] = ok ? __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                              rl, (int)((((uint32_t)(n0 + nl) << Q) + 8u * ch) * 2u), 0, 0))
-                        : u32x4{0, 0, 0, 0};
-        }
-        // first step's planes are requested before the LUT lands in LDS
-        if (j0 == 0 && has_steps)
+    if constexpr (Q == 3) {
+        // ---- pair table of LUT_3 for rows n0..n0+63: entry (row 32t+i, pair code v)
+        //      at v*256 + 128t + 4i; thread -> row tid % 64, pair codes 16(tid/64) .. +15
+        const int nl = tid % kRows, part = tid / kRows;
+        const u32x4 lv = n0 + nl < N ? __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                               rl, (int)(((uint32_t)(n0 + nl) << 3) * 2u), 0, 0))
+                                     : u32x4{0, 0, 0, 0};
+        if (has_steps)
             load_planes<Q>(wc, rs, lane_word);
+        const uint32_t slot = (uint32_t)(128 * (nl >> 5) + 4 * (nl & 31));
 #pragma unroll
-        for (int jj = 0; jj < kBatch; ++jj) {
-            const int idx = tid + (j0 + jj) * kThreads;
-            if (idx >= kLutU4)
-                break;
-            const int nl = idx % kRows, ch = idx / kRows;
-            const int il = nl & 31, tl = nl >> 5;
+        for (int kk = 0; kk < 16; ++kk) {
+            const uint32_t v = (uint32_t)(16 * part + kk);
+            const uint32_t ce = bitrev(v & 7u, 3), co = bitrev(v >> 3, 3);  // codes of the even / odd column
+            const uint32_t lo = (lv[ce >> 1] >> (16 * (ce & 1))) & 0xFFFFu;
+            const uint32_t hi = (lv[co >> 1] >> (16 * (co & 1))) & 0xFFFFu;
+            *reinterpret_cast<uint32_t *>(smem + v * 256 + slot) = lo | (hi << 16);
+        }
+    } else {
+        // ---- LUT level Q of rows n0..n0+63: 16-byte loads (8 entries of one row),
+        //      lane -> row so that one wave touches 64 rows ----------------------------
+        constexpr int kLutU4 = (kRows << Q) / 8;
+        constexpr int kPer = (kLutU4 + kThreads - 1) / kThreads;
+        constexpr int kBatch = kPer < 4 ? kPer : 4;  // loads in flight per batch (register budget)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint16_t v = (uint16_t)(lv[jj][e >> 1] >> (16 * (e & 1)));
-                const uint32_t vp = bitrev((uint32_t)(8 * ch + e), Q);
-                if (Q < 8) {
-                    *reinterpret_cast<uint16_t *>(smem + vp * 256 + 4 * il + 2 * tl) = v;
-                    *reinterpret_cast<uint16_t *>(smem + vp * 256 + 4 * (32 + il) + 2 * tl) = v;
-                } else {
-                    *reinterpret_cast<uint16_t *>(smem + vp * 128 + 4 * il + 2 * tl) = v;
+        for (int j0 = 0; j0 < kPer; j0 += kBatch) {
+            u32x4 lv[kBatch];
+#pragma unroll
+            for (int jj = 0; jj < kBatch; ++jj) {
+                const int idx = tid + (j0 + jj) * kThreads;
+                const int nl = idx % kRows, ch = idx / kRows;
+                const bool ok = idx < kLutU4 && n0 + nl < N;
+                lv[jj] = ok ? __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                  rl, (int)((((uint32_t)(n0 + nl) << Q) + 8u * ch) * 2u), 0, 0))
+                            : u32x4{0, 0, 0, 0};
+            }
+            // first step's planes are requested before the LUT lands in LDS
+            if (j0 == 0 && has_steps)
+                load_planes<Q>(wc, rs, lane_word);
+#pragma unroll
+            for (int jj = 0; jj < kBatch; ++jj) {
+                const int idx = tid + (j0 + jj) * kThreads;
+                if (idx >= kLutU4)
+                    break;
+                const int nl = idx % kRows, ch = idx / kRows;
+                const int il = nl & 31, tl = nl >> 5;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint16_t v = (uint16_t)(lv[jj][e >> 1] >> (16 * (e & 1)));
+                    const uint32_t vp = bitrev((uint32_t)(8 * ch + e), Q);
+                    if (Q < 8) {
+                        *reinterpret_cast<uint16_t *>(smem + vp * 256 + 4 * il + 2 * tl) = v;
+                        *reinterpret_cast<uint16_t *>(smem + vp * 256 + 4 * (32 + il) + 2 * tl) = v;
+                    } else {
+                        *reinterpret_cast<uint16_t *>(smem + vp * 128 + 4 * il + 2 * tl) = v;
+                    }
                 }
             }
         }
+
     }
     __syncthreads();
 
     // LDS byte address of the region (a compile-time constant for the static array)
     const uint32_t lds_base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char *)smem);
-    const uint32_t lane_const = (Q < 8) ? (uint32_t)(4 * (32 * g + i) + 2 * t) : (uint32_t)(4 * i + 2 * t);
+    const uint32_t lane_const = Q == 3  ? (uint32_t)(128 * t + 4 * i)
+                                : Q < 8 ? (uint32_t)(4 * (32 * g + i) + 2 * t)
+                                        : (uint32_t)(4 * i + 2 * t);
     float *red = reinterpret_cast<float *>(smem + kLutBytes);
 
     for (int tp = 0; tp < Me; tp += kTokTile) {
@@ -234,13 +287,24 @@ __device__ void gemm_block(const GemmParams &P, const DevBlock &blk, int rb, int
         for (int step = half; step < nsteps; step += 2) {
             const bool more = step + 2 < nsteps;
             u32x2 wn[Q];
+            // Vector-memory requests complete in issue order: the B group used later in
+            // this step goes first, so waiting for it leaves the next step's plane words
+            // in flight for a whole step.
+            load_x_group(xb, rx, xoff + 64);
+            __builtin_amdgcn_sched_barrier(0);
             word += more ? kNextWords : 0u;
             load_planes<Q>(wn, rs, word);
-            load_x_group(xb, rx, xoff + 64);
-            group_product<Q, 0>(wc, xa, lds_base, lane_const, acc);
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (Q == 3)
+                group_product_pair3<0>(wc, xa, lds_base, lane_const, acc);
+            else
+                group_product<Q, 0>(wc, xa, lds_base, lane_const, acc);
             xoff += more ? 2 * kStepCols * 2 : 0;  // this wave's next step: 256 columns on
             load_x_group(xa, rx, xoff);
-            group_product<Q, 1>(wc, xb, lds_base, lane_const, acc);
+            if constexpr (Q == 3)
+                group_product_pair3<1>(wc, xb, lds_base, lane_const, acc);
+            else
+                group_product<Q, 1>(wc, xb, lds_base, lane_const, acc);
 #pragma unroll
             for (int p = 0; p < Q; ++p)
                 wc[p] = wn[p];
