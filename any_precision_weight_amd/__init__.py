@@ -25,7 +25,8 @@ EXPORTED = [
     "apmoe_status_string", "apmoe_last_error", "apmoe_version", "apmoe_create", "apmoe_destroy",
     "apmoe_block_bytes", "apmoe_table_create", "apmoe_table_destroy", "apmoe_table_set_block",
     "apmoe_table_set_bits", "apmoe_table_set_plane", "apmoe_table_validate", "apmoe_table_committed_bits",
-    "apmoe_table_commit", "apmoe_lut_build", "apmoe_tiled_plane_words", "apmoe_tile_planes", "apmoe_pack_planes", "apmoe_route", "apmoe_gemm", "apmoe_act",
+    "apmoe_table_commit", "apmoe_lut_build", "apmoe_tiled_plane_words", "apmoe_tile_planes", "apmoe_pack_planes", "apmoe_route", "apmoe_route_stats", "apmoe_gemm",
+    "apmoe_act",
     "apmoe_combine", "apmoe_moe_workspace", "apmoe_moe_forward",
 ]
 
@@ -90,6 +91,7 @@ def _declare(L):
         "apmoe_tile_planes": (S, [P, P, I32, I32, P, P]),
         "apmoe_pack_planes": (S, [P, P, I32, I32, P, P]),
         "apmoe_route": (S, [P, P, P, P, I32, I32, I32, I32, I32, P, P, P, P, P, P, P]),
+        "apmoe_route_stats": (S, [P, P, P, P, I32, I32, I32, P, P, P, P]),
         "apmoe_gemm": (S, [P, P, I32, I32, P, I32, P, P, I32, I32, P, I32, P]),
         "apmoe_act": (S, [P, P, I32, I32, P, P]),
         "apmoe_combine": (S, [P, P, I32, P, P, I32, I32, I32, P, P]),
@@ -238,6 +240,14 @@ def route(ctx: Context, x, w_router, bias, T: int, H: int, E: int, topk: int, re
     _check(lib().apmoe_route(ctx.handle, ptr(x), ptr(w_router), ptr(bias), T, H, E, topk, int(renormalize),
                              ptr(topk_ids), ptr(topk_w), ptr(counts), ptr(offsets), ptr(perm), ptr(inv_perm),
                              stream_handle(stream)), "apmoe_route")
+
+
+def route_stats(ctx: Context, topk_w, perm, offsets, T: int, topk: int, E: int, mass, total, selections,
+                stream=None) -> None:
+    """Add one routed batch to the routing-statistics accumulators (Eq. 1):
+    mass[E] fp64, total[1] fp64, selections[E] int64, all device memory."""
+    _check(lib().apmoe_route_stats(ctx.handle, ptr(topk_w), ptr(perm), ptr(offsets), T, topk, E, ptr(mass),
+                                   ptr(total), ptr(selections), stream_handle(stream)), "apmoe_route_stats")
 
 
 def gemm(ctx: Context, table: Table, layer: int, kind: int, inp, gather: bool, perm, offsets, T: int, topk: int,

@@ -514,6 +514,35 @@ apmoe_status apmoe_route(apmoe_ctx *ctx, const uint16_t *x, const uint16_t *w_ro
     return ok();
 }
 
+apmoe_status apmoe_route_stats(apmoe_ctx *ctx, const float *topk_w, const int32_t *perm, const int32_t *offsets,
+                               int32_t T, int32_t topk, int32_t E, double *mass, double *total, int64_t *selections,
+                               void *stream)
+{
+    apmoe_status s = check_ctx(ctx);
+    if (s != APMOE_OK)
+        return s;
+    if (T < 0)
+        return fail(APMOE_INVALID_ARG, "T=%d", T);
+    if (E < 1 || E > APMOE_MAX_EXPERTS)
+        return fail(APMOE_INVALID_ARG, "E=%d outside 1..%d", E, APMOE_MAX_EXPERTS);
+    if (topk < 1 || topk > E || topk > APMOE_MAX_TOPK)
+        return fail(APMOE_INVALID_ARG, "topk=%d (need 1..min(E,%d))", topk, APMOE_MAX_TOPK);
+    if ((int64_t)T * topk > (int64_t)1 << 30)
+        return fail(APMOE_INVALID_ARG, "T*topk too large");
+    if (!mass || !total || !selections)
+        return fail(APMOE_INVALID_ARG, "mass / total / selections is NULL");
+    if (T == 0)
+        return ok();
+    if (!topk_w || !perm || !offsets)
+        return fail(APMOE_INVALID_ARG, "topk_w / perm / offsets is NULL");
+    if ((reinterpret_cast<uintptr_t>(mass) | reinterpret_cast<uintptr_t>(total) |
+         reinterpret_cast<uintptr_t>(selections)) % 8 != 0)
+        return fail(APMOE_INVALID_ARG, "accumulators not 8-byte aligned");
+    hipError_t e = apmoe::launch_route_stats(topk_w, perm, offsets, E, mass, total, selections,
+                                             reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ok() : hip_fail(e, "route_stats launch");
+}
+
 static apmoe_status layer_shape(const apmoe_table *t, int layer, int kind, int *N, int *K, int *max_q)
 {
     *N = *K = -1;

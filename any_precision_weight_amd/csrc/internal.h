@@ -35,6 +35,8 @@ hipError_t launch_route_topk(const uint16_t *x, const uint16_t *wr, const float 
                              int renormalize, int32_t *ids, float *w, hipStream_t s);
 hipError_t launch_route_sort(const int32_t *ids, int R, int E, int32_t *counts, int32_t *offsets, int32_t *perm,
                              int32_t *inv_perm, hipStream_t s);
+hipError_t launch_route_stats(const float *w, const int32_t *perm, const int32_t *offsets, int E, double *mass,
+                              double *total, int64_t *selections, hipStream_t s);
 
 // table points at the (layer) slice: entry for expert e and kind u is table[2*e + u].
 // in_bytes: size of `in` (rows x K fp16); must be below 2^31.

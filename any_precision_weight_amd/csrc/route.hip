@@ -202,6 +202,48 @@ __global__ void __launch_bounds__(kSortThreads) route_sort_kernel(const int32_t 
     }
 }
 
+
+// Routing statistics (PagedWeight, Section 2.1, Eq. 1 and Section 3.2 "Routing
+// statistics"): per expert, the sum of the routing weights of the assignments it
+// received and the number of those assignments, plus the sum of all routing
+// weights, accumulated into caller-owned fp64 / int64 arrays across calls (the
+// routing mass of expert e is mass[e] / total).  One workgroup walks the experts in
+// order; each expert's contiguous perm segment is reduced with a fixed thread-strided
+// partial sum and a fixed tree, so every call is deterministic.
+constexpr int kStatsThreads = 256;
+
+__global__ void __launch_bounds__(kStatsThreads) route_stats_kernel(const float *__restrict__ w,
+                                                                    const int32_t *__restrict__ perm,
+                                                                    const int32_t *__restrict__ offsets, int E,
+                                                                    double *__restrict__ mass, double *__restrict__ total,
+                                                                    int64_t *__restrict__ selections)
+{
+    __shared__ double part[kStatsThreads];
+    const int tid = threadIdx.x;
+    double batch_total = 0.0;  // thread 0 only
+    for (int e = 0; e < E; ++e) {
+        const int r0 = offsets[e], r1 = offsets[e + 1];
+        double s = 0.0;
+        for (int r = r0 + tid; r < r1; r += kStatsThreads)
+            s += (double)w[perm[r]];
+        part[tid] = s;
+        __syncthreads();
+        for (int h = kStatsThreads / 2; h > 0; h >>= 1) {
+            if (tid < h)
+                part[tid] += part[tid + h];
+            __syncthreads();
+        }
+        if (tid == 0) {
+            mass[e] += part[0];
+            selections[e] += (int64_t)(r1 - r0);
+            batch_total += part[0];
+        }
+        __syncthreads();
+    }
+    if (tid == 0)
+        total[0] += batch_total;
+}
+
 }  // namespace
 
 hipError_t launch_route_topk(const uint16_t *x, const uint16_t *wr, const float *bias, int T, int H, int E, int topk,
@@ -211,6 +253,14 @@ hipError_t launch_route_topk(const uint16_t *x, const uint16_t *wr, const float 
         return hipSuccess;
     hipLaunchKernelGGL(route_topk_kernel, dim3(T), dim3(kRouteThreads), 0, s, x, wr, bias, T, H, E, topk,
                        renormalize, ids, w);
+    return hipGetLastError();
+}
+
+hipError_t launch_route_stats(const float *w, const int32_t *perm, const int32_t *offsets, int E, double *mass,
+                              double *total, int64_t *selections, hipStream_t s)
+{
+    hipLaunchKernelGGL(route_stats_kernel, dim3(1), dim3(kStatsThreads), 0, s, w, perm, offsets, E, mass, total,
+                       selections);
     return hipGetLastError();
 }
 

@@ -213,6 +213,24 @@ apmoe_status apmoe_route(apmoe_ctx *ctx, const uint16_t *x, const uint16_t *w_ro
                          int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv_perm, void *stream);
 
 /*
+ * Online routing statistics (Section 2.1, Eq. 1: the routing mass of expert e is
+ * the sum of the routing weights of its selections over the sum of all routing
+ * weights; Section 3.2 "Routing statistics": collected during serving).  Adds this
+ * batch's contribution to caller-owned device accumulators:
+ *   mass[e]       += sum of topk_w[t][j] over assignments routed to e   (fp64)
+ *   selections[e] += number of assignments routed to e                  (int64)
+ *   total[0]      += sum of all topk_w[t][j]                             (fp64)
+ * topk_w, perm and offsets are the outputs of apmoe_route for the same batch
+ * (perm groups the assignments by expert).  The caller zeroes the accumulators
+ * once and reads mass[e] / total[0].  Sums are fp64 with a fixed reduction order:
+ * repeated calls give identical bits.  Calls that overlap on the same
+ * accumulators race.  Limits as apmoe_route; T = 0 adds nothing.
+ */
+apmoe_status apmoe_route_stats(apmoe_ctx *ctx, const float *topk_w, const int32_t *perm, const int32_t *offsets,
+                               int32_t T, int32_t topk, int32_t E, double *mass, double *total, int64_t *selections,
+                               void *stream);
+
+/*
  * Any-precision product of every expert of one (layer, kind) in one launch.
  * For expert e, rows r in [offsets[e], offsets[e+1]) of the output:
  *   out[r][n] = sum_c in_row(r)[c] * LUT_q[n][code_q(n, c)],   fp32 accumulation,

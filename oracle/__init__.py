@@ -275,6 +275,27 @@ def moe_forward(x, wr, bias, topk: int, planes_gu, lutp_gu, q_gu, planes_dn, lut
     return res
 
 
+def route_stats(ids: np.ndarray, w: np.ndarray, E: int):
+    """Eq. 1 (Section 2.1) terms of one batch, in fp64: for every expert e the sum of
+    the routing weights r_tk of the selections z_tk = e (numerator), the number of
+    those selections, and the sum of all routing weights (denominator).  Plain loops
+    over tokens t and choices k, in that order."""
+    ids = np.asarray(ids)
+    w = np.asarray(w)
+    num = np.zeros(E, np.float64)
+    cnt = np.zeros(E, np.int64)
+    den = 0.0
+    T, K = ids.shape
+    for t in range(T):
+        for k in range(K):
+            e = int(ids[t, k])
+            r = float(w[t, k])
+            num[e] += r
+            cnt[e] += 1
+            den += r
+    return num, cnt, den
+
+
 def routing_mass(ids: np.ndarray, w: np.ndarray, E: int) -> np.ndarray:
     """Eq. 1 (Section 2.1): m_e = sum_t sum_k r_tk [z_tk = e] / sum_t sum_k r_tk."""
     ids = np.asarray(ids)

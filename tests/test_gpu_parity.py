@@ -61,6 +61,45 @@ def test_route_parity(case):
     check_route(o, r)
 
 
+@pytest.mark.parametrize("case", ROUTE_CASES[:3], ids=lambda c: f"T{c[0]}H{c[1]}E{c[2]}k{c[3]}")
+def test_route_stats_accumulate(case):
+    """Eq. 1 terms accumulated over two calls: selection counts exact; with dyadic
+    weights every fp64 sum is exact whatever the order, so the masses match bit for
+    bit; with the router's own weights they match within the fp64 summation bound."""
+    T, H, E, k, use_bias, renorm, seed = case
+    x = synth.fp16_normal(100 + seed, 1, T * H, 1.0).reshape(T, H)
+    wr = synth.fp16_normal(100 + seed, 2, E * H, 0.02).reshape(E, H)
+    R = T * k
+    o = dict(ids=torch.empty((T, k), dtype=torch.int32, device="cuda"),
+             w=torch.empty((T, k), dtype=torch.float32, device="cuda"),
+             counts=torch.empty(E, dtype=torch.int32, device="cuda"),
+             offsets=torch.empty(E + 1, dtype=torch.int32, device="cuda"),
+             perm=torch.empty(max(R, 1), dtype=torch.int32, device="cuda"),
+             inv_perm=torch.empty(max(R, 1), dtype=torch.int32, device="cuda"))
+    apw.route(ctx(), dev(x), dev(wr), None, T, H, E, k, renorm, o["ids"], o["w"], o["counts"], o["offsets"],
+              o["perm"], o["inv_perm"])
+    mass = torch.zeros(E, dtype=torch.float64, device="cuda")
+    total = torch.zeros(1, dtype=torch.float64, device="cuda")
+    sel = torch.zeros(E, dtype=torch.int64, device="cuda")
+    for _ in range(2):
+        apw.route_stats(ctx(), o["w"], o["perm"], o["offsets"], T, k, E, mass, total, sel)
+    torch.cuda.synchronize()
+    ids, w = host(o["ids"]), host(o["w"])
+    num, cnt, den = oracle.route_stats(ids, w, E)
+    assert np.array_equal(host(sel), 2 * cnt)
+    bound = 2 * R * 2.0 ** -52 * (2 * den) + 1e-300
+    assert np.all(np.abs(host(mass) - 2 * num) <= bound)
+    assert abs(float(host(total)[0]) - 2 * den) <= bound
+    # dyadic weights: exact in any summation order
+    wd = (RNG.integers(1, 1024, (T, k)) / 1024.0).astype(np.float32)
+    mass.zero_(), total.zero_(), sel.zero_()
+    apw.route_stats(ctx(), dev(wd), o["perm"], o["offsets"], T, k, E, mass, total, sel)
+    torch.cuda.synchronize()
+    num, cnt, den = oracle.route_stats(ids, wd, E)
+    assert np.array_equal(host(mass), num) and float(host(total)[0]) == den
+    assert np.array_equal(host(sel), cnt)
+
+
 def test_route_ties_lower_index():
     T, H, E, k = 40, 256, 8, 2
     x = synth.fp16_normal(9, 1, T * H, 1.0).reshape(T, H)

@@ -264,6 +264,20 @@ def test_routing_mass_eq1():
     assert np.allclose(m, brute, rtol=1e-13, atol=1e-16)
 
 
+def test_route_stats_eq1_terms():
+    """Eq. 1 numerator, selection count and denominator on a hand example whose
+    weights are dyadic (every sum exact): experts 0, 1, 2 receive 0.75+0.125,
+    0.5 and 0.25+0.5+0.875 of a total 3."""
+    ids = np.array([[0, 2], [2, 1], [0, 2]], np.int32)
+    w = np.array([[0.75, 0.25], [0.5, 0.5], [0.125, 0.875]], np.float32)
+    num, cnt, den = oracle.route_stats(ids, w, 4)
+    assert num.tolist() == [0.875, 0.5, 1.625, 0.0]
+    assert cnt.tolist() == [2, 1, 3, 0]
+    assert den == 3.0
+    # and the normalised form is the routing mass of Eq. 1
+    assert np.array_equal(num / den, oracle.routing_mass(ids, w, 4))
+
+
 # ---------------------------------------------------------------- layer -------
 
 def _tiny_layer(T=5, H=64, F=64, E=4, k=2, seed=31, qs=None):
