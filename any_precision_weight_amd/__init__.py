@@ -27,7 +27,7 @@ EXPORTED = [
     "apmoe_table_set_bits", "apmoe_table_set_plane", "apmoe_table_validate", "apmoe_table_committed_bits",
     "apmoe_table_commit", "apmoe_lut_build", "apmoe_tiled_plane_words", "apmoe_tile_planes", "apmoe_pack_planes", "apmoe_route", "apmoe_route_stats", "apmoe_gemm",
     "apmoe_act",
-    "apmoe_combine", "apmoe_moe_workspace", "apmoe_moe_forward",
+    "apmoe_combine", "apmoe_moe_workspace", "apmoe_moe_forward", "apmoe_page_out", "apmoe_page_in",
 ]
 
 
@@ -97,6 +97,8 @@ def _declare(L):
         "apmoe_combine": (S, [P, P, I32, P, P, I32, I32, I32, P, P]),
         "apmoe_moe_workspace": (S, [P, I32, I32, I32, ctypes.POINTER(SZ)]),
         "apmoe_moe_forward": (S, [P, P, I32, P, P, P, I32, I32, I32, P, SZ, P, P]),
+        "apmoe_page_out": (S, [P, P, I32, I32, I32, I32, ctypes.POINTER(P), P, P, P]),
+        "apmoe_page_in": (S, [P, P, I32, I32, I32, I32, ctypes.POINTER(P), ctypes.POINTER(P), P, P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -276,3 +278,40 @@ def moe_forward(ctx: Context, table: Table, layer: int, x, w_router, bias, T: in
     _check(lib().apmoe_moe_forward(ctx.handle, table.handle, layer, ptr(x), ptr(w_router), ptr(bias), T, topk,
                                    int(renormalize), ptr(ws), ws_bytes, ptr(out), stream_handle(stream)),
            "apmoe_moe_forward")
+
+
+# --------------------------------------------------------------------------- page movement
+
+def _plane_array(planes):
+    arr = (ctypes.c_void_p * PLANES)()
+    for p, t in enumerate(planes if planes is not None else []):
+        if p < PLANES:
+            arr[p] = ptr(t)
+    return arr
+
+
+def _event_handle(ev, stream) -> int:
+    """Raw hipEvent_t of a torch.cuda.Event (recorded once on `stream` so that the
+    handle exists; the library records it again)."""
+    ev.record(stream)
+    return ev.cuda_event
+
+
+def page_out(ctx: Context, table: Table, layer: int, expert: int, kind: int, q_new: int, host_planes,
+             stream, copy_stream, done_event) -> None:
+    """Lower (layer, expert, kind) to q_new and copy planes q_new.. to host_planes[p]
+    (8-entry list; pinned tensors).  done_event (torch.cuda.Event) completes once the
+    device planes may be freed."""
+    _check(lib().apmoe_page_out(ctx.handle, table.handle, layer, expert, kind, q_new, _plane_array(host_planes),
+                                stream_handle(stream), stream_handle(copy_stream),
+                                _event_handle(done_event, copy_stream)), "apmoe_page_out")
+
+
+def page_in(ctx: Context, table: Table, layer: int, expert: int, kind: int, q_new: int, host_planes, dev_planes,
+            stream, copy_stream, copied_event) -> None:
+    """Copy host_planes[p] to dev_planes[p] for the planes above the current bitwidth,
+    then raise (layer, expert, kind) to q_new with a commit on `stream` that waits for
+    the copies."""
+    _check(lib().apmoe_page_in(ctx.handle, table.handle, layer, expert, kind, q_new, _plane_array(host_planes),
+                               _plane_array(dev_planes), stream_handle(stream), stream_handle(copy_stream),
+                               _event_handle(copied_event, copy_stream)), "apmoe_page_in")

@@ -514,6 +514,132 @@ apmoe_status apmoe_route(apmoe_ctx *ctx, const uint16_t *x, const uint16_t *w_ro
     return ok();
 }
 
+// ---- page movement ----------------------------------------------------------------
+
+static apmoe_status page_common(apmoe_ctx *ctx, apmoe_table *t, int32_t layer, int32_t expert, int32_t kind,
+                                size_t *idx)
+{
+    apmoe_status s = check_ctx(ctx);
+    if (s != APMOE_OK)
+        return s;
+    s = check_index(t, layer, expert, kind);
+    if (s != APMOE_OK)
+        return s;
+    if (!t->committed_once)
+        return fail(APMOE_NOT_RESIDENT, "table was never committed");
+    if (t->device != ctx->device)
+        return fail(APMOE_INVALID_ARG, "table lives on device %d, ctx on %d", t->device, ctx->device);
+    const size_t i = t->index(layer, expert, kind);
+    if (!t->staged_present[i] || !t->cpresent[i])
+        return fail(APMOE_INVALID_ARG, "block (%d,%d,%d) was never committed", layer, expert, kind);
+    if (t->staged[i].q != t->cq[i])
+        return fail(APMOE_INVALID_ARG, "block (%d,%d,%d) has an uncommitted bitwidth change", layer, expert, kind);
+    *idx = i;
+    return APMOE_OK;
+}
+
+apmoe_status apmoe_page_out(apmoe_ctx *ctx, apmoe_table *t, int32_t layer, int32_t expert, int32_t kind,
+                            int32_t q_new, void *const *host_planes, void *stream, void *copy_stream,
+                            void *done_event)
+{
+    size_t i = 0;
+    apmoe_status s = page_common(ctx, t, layer, expert, kind, &i);
+    if (s != APMOE_OK)
+        return s;
+    apmoe_block_desc &d = t->staged[i];
+    const int q_old = d.q;
+    if (q_new < APMOE_MIN_BITS || q_new >= q_old)
+        return fail(APMOE_INVALID_ARG, "page-out to q=%d from q=%d (need %d <= q_new < q_old)", q_new, q_old,
+                    APMOE_MIN_BITS);
+    if (!host_planes || !done_event)
+        return fail(APMOE_INVALID_ARG, "host_planes / done_event is NULL");
+    for (int p = q_new; p < q_old; ++p)
+        if (!host_planes[p] || !d.plane[p])
+            return fail(APMOE_INVALID_ARG, "plane %d: host buffer or device plane is NULL", p);
+    // lower q first (stream-ordered commit): launches after it never read planes >= q_new
+    const apmoe_block_desc saved = d;
+    d.q = q_new;
+    s = apmoe_table_commit(ctx, t, stream);
+    if (s != APMOE_OK) {
+        d = saved;
+        return s;
+    }
+    const size_t bytes = apmoe::tiled_plane_words(d.n, d.k) * 4;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream), cs = reinterpret_cast<hipStream_t>(copy_stream);
+    hipEvent_t done = reinterpret_cast<hipEvent_t>(done_event);
+    // The copies start at the commit point of `stream` (every earlier write to the
+    // planes and every launch that may read them have finished) and overlap the
+    // launches enqueued after it; done is recorded after the copies.
+    hipError_t e = hipEventRecord(done, st);
+    if (e == hipSuccess)
+        e = hipStreamWaitEvent(cs, done, 0);
+    for (int p = q_new; p < q_old && e == hipSuccess; ++p)
+        e = hipMemcpyAsync(host_planes[p], d.plane[p], bytes, hipMemcpyDeviceToHost, cs);
+    if (e == hipSuccess)
+        e = hipEventRecord(done, cs);
+    if (e != hipSuccess)
+        return hip_fail(e, "page-out copies");
+    for (int p = q_new; p < q_old; ++p) {  // no longer resident once `done` has passed
+        d.plane[p] = nullptr;
+        d.resident_mask &= ~(1u << p);
+    }
+    return ok();
+}
+
+apmoe_status apmoe_page_in(apmoe_ctx *ctx, apmoe_table *t, int32_t layer, int32_t expert, int32_t kind,
+                           int32_t q_new, void *const *host_planes, uint32_t *const *dev_planes, void *stream,
+                           void *copy_stream, void *copied_event)
+{
+    size_t i = 0;
+    apmoe_status s = page_common(ctx, t, layer, expert, kind, &i);
+    if (s != APMOE_OK)
+        return s;
+    apmoe_block_desc &d = t->staged[i];
+    const int q_old = d.q;
+    if (q_new <= q_old || q_new > APMOE_MAX_BITS)
+        return fail(APMOE_INVALID_ARG, "page-in to q=%d from q=%d (need q_old < q_new <= %d)", q_new, q_old,
+                    APMOE_MAX_BITS);
+    if (!host_planes || !dev_planes || !copied_event)
+        return fail(APMOE_INVALID_ARG, "host_planes / dev_planes / copied_event is NULL");
+    for (int p = q_old; p < q_new; ++p) {
+        if (!host_planes[p] || !dev_planes[p])
+            return fail(APMOE_INVALID_ARG, "plane %d: host buffer or device plane is NULL", p);
+        if (!aligned16(dev_planes[p]))
+            return fail(APMOE_INVALID_ARG, "device plane %d not 16-byte aligned", p);
+    }
+    // stage the new planes and q, and check the result before anything is enqueued
+    const apmoe_block_desc saved = d;
+    for (int p = q_old; p < q_new; ++p) {
+        d.plane[p] = dev_planes[p];
+        d.resident_mask |= 1u << p;
+    }
+    d.q = q_new;
+    s = validate_table(t);
+    if (s != APMOE_OK) {
+        d = saved;
+        return s;
+    }
+    const size_t bytes = apmoe::tiled_plane_words(d.n, d.k) * 4;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream), cs = reinterpret_cast<hipStream_t>(copy_stream);
+    hipEvent_t copied = reinterpret_cast<hipEvent_t>(copied_event);
+    hipError_t e = hipSuccess;
+    for (int p = q_old; p < q_new && e == hipSuccess; ++p)
+        e = hipMemcpyAsync(dev_planes[p], host_planes[p], bytes, hipMemcpyHostToDevice, cs);
+    // raise q last: the commit on `stream` waits for the copies
+    if (e == hipSuccess)
+        e = hipEventRecord(copied, cs);
+    if (e == hipSuccess)
+        e = hipStreamWaitEvent(st, copied, 0);
+    if (e != hipSuccess) {
+        d = saved;
+        return hip_fail(e, "page-in copies");
+    }
+    s = apmoe_table_commit(ctx, t, stream);
+    if (s != APMOE_OK)
+        d = saved;
+    return s;
+}
+
 apmoe_status apmoe_route_stats(apmoe_ctx *ctx, const float *topk_w, const int32_t *perm, const int32_t *offsets,
                                int32_t T, int32_t topk, int32_t E, double *mass, double *total, int64_t *selections,
                                void *stream)

@@ -192,6 +192,44 @@ apmoe_status apmoe_pack_planes(apmoe_ctx *ctx, const uint8_t *codes, int32_t n, 
                                void *stream);
 
 /* ---------------------------------------------------------------------------
+ * Page movement (Section 3.1: each bit-plane of a linear-block is a page, and
+ * dropping the top planes lowers its bitwidth; Section 3.3 and Figure 4: pages
+ * move asynchronously, a bitwidth is lowered before its pages are offloaded and
+ * raised only after they are reloaded, and changes are committed only at safe
+ * boundaries).  Both calls are asynchronous; copies run on copy_stream, the
+ * commit on stream.  Plane buffers hold one tiled plane each
+ * (apmoe_tiled_plane_words(n, k) * 4 bytes); host buffers should be pinned.
+ * ------------------------------------------------------------------------ */
+
+/*
+ * Page-out: lower committed block (layer, expert, kind) from q_old to q_new and
+ * copy its planes q_new .. q_old-1 to host_planes[p].  The bitwidth change is
+ * committed on `stream` first, so launches enqueued after this call never read
+ * those planes.  The copies start once `stream` has passed that commit (every
+ * launch that may read the planes has finished) and overlap the launches enqueued
+ * after it.  done_event (a caller-created hipEvent_t) completes after the copies;
+ * then the device planes may be freed or reused.
+ * The staged entry then lists those planes as not resident.  Errors (nothing
+ * enqueued, nothing changed): INVALID_ARG unless 3 <= q_new < q_old, the block was
+ * committed with no pending bitwidth change, and every needed pointer is set.
+ */
+apmoe_status apmoe_page_out(apmoe_ctx *ctx, apmoe_table *tbl, int32_t layer, int32_t expert, int32_t kind,
+                            int32_t q_new, void *const *host_planes /*[8]*/, void *stream, void *copy_stream,
+                            void *done_event);
+
+/*
+ * Page-in: copy host_planes[p] to dev_planes[p] (caller-allocated device memory)
+ * for p = q_old .. q_new-1 on copy_stream, make `stream` wait for the copies
+ * (copied_event, a caller-created hipEvent_t, is recorded after them), then stage
+ * the planes and q_new and commit on `stream`: launches enqueued after this call
+ * use q_new.  LUT level q_new must be in the block's descriptor.  Errors as for
+ * page-out, with q_old < q_new <= 8 and 16-byte aligned device planes.
+ */
+apmoe_status apmoe_page_in(apmoe_ctx *ctx, apmoe_table *tbl, int32_t layer, int32_t expert, int32_t kind,
+                           int32_t q_new, void *const *host_planes /*[8]*/, uint32_t *const *dev_planes /*[8]*/,
+                           void *stream, void *copy_stream, void *copied_event);
+
+/* ---------------------------------------------------------------------------
  * Layer steps
  * ------------------------------------------------------------------------ */
 
