@@ -90,13 +90,13 @@ def _declare(L):
         "apmoe_tiled_plane_words": (I64, [I32, I32]),
         "apmoe_tile_planes": (S, [P, P, I32, I32, P, P]),
         "apmoe_pack_planes": (S, [P, P, I32, I32, P, P]),
-        "apmoe_route": (S, [P, P, P, P, I32, I32, I32, I32, I32, P, P, P, P, P, P, P]),
+        "apmoe_route": (S, [P, P, P, P, I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, P]),
         "apmoe_route_stats": (S, [P, P, P, P, I32, I32, I32, P, P, P, P]),
         "apmoe_gemm": (S, [P, P, I32, I32, P, I32, P, P, I32, I32, P, I32, P]),
         "apmoe_act": (S, [P, P, I32, I32, P, P]),
         "apmoe_combine": (S, [P, P, I32, P, P, I32, I32, I32, P, P]),
-        "apmoe_moe_workspace": (S, [P, I32, I32, I32, ctypes.POINTER(SZ)]),
-        "apmoe_moe_forward": (S, [P, P, I32, P, P, P, I32, I32, I32, P, SZ, P, P]),
+        "apmoe_moe_workspace": (S, [P, I32, I32, I32, I32, ctypes.POINTER(SZ)]),
+        "apmoe_moe_forward": (S, [P, P, I32, P, P, P, I32, I32, I32, I32, P, SZ, P, P]),
         "apmoe_page_out": (S, [P, P, I32, I32, I32, I32, ctypes.POINTER(P), P, P, P]),
         "apmoe_page_in": (S, [P, P, I32, I32, I32, I32, ctypes.POINTER(P), ctypes.POINTER(P), P, P, P]),
     }
@@ -238,8 +238,11 @@ def pack_planes(ctx: Context, codes, n: int, k: int, planes, stream=None) -> Non
 
 
 def route(ctx: Context, x, w_router, bias, T: int, H: int, E: int, topk: int, renormalize: bool, topk_ids,
-          topk_w, counts, offsets, perm, inv_perm, stream=None) -> None:
-    _check(lib().apmoe_route(ctx.handle, ptr(x), ptr(w_router), ptr(bias), T, H, E, topk, int(renormalize),
+          topk_w, counts, offsets, perm, inv_perm, stream=None, n_shared: int = 0) -> None:
+    """Top-k routing over E routed experts; with n_shared > 0 each token's row of
+    topk_ids / topk_w (stride topk + n_shared) ends with the shared experts
+    E .. E + n_shared - 1 at weight 1, and counts / offsets cover E + n_shared experts."""
+    _check(lib().apmoe_route(ctx.handle, ptr(x), ptr(w_router), ptr(bias), T, H, E, topk, n_shared, int(renormalize),
                              ptr(topk_ids), ptr(topk_w), ptr(counts), ptr(offsets), ptr(perm), ptr(inv_perm),
                              stream_handle(stream)), "apmoe_route")
 
@@ -267,15 +270,17 @@ def combine(ctx: Context, y, y_dtype: int, topk_w, inv_perm, T: int, topk: int, 
                                stream_handle(stream)), "apmoe_combine")
 
 
-def moe_workspace(table: Table, layer: int, T: int, topk: int) -> int:
+def moe_workspace(table: Table, layer: int, T: int, topk: int, n_shared: int = 0) -> int:
     n = ctypes.c_size_t()
-    _check(lib().apmoe_moe_workspace(table.handle, layer, T, topk, ctypes.byref(n)), "apmoe_moe_workspace")
+    _check(lib().apmoe_moe_workspace(table.handle, layer, T, topk, n_shared, ctypes.byref(n)), "apmoe_moe_workspace")
     return n.value
 
 
 def moe_forward(ctx: Context, table: Table, layer: int, x, w_router, bias, T: int, topk: int, renormalize: bool,
-                ws, ws_bytes: int, out, stream=None) -> None:
+                ws, ws_bytes: int, out, stream=None, n_shared: int = 0) -> None:
+    """Whole layer; the table's last n_shared experts of the layer are shared ones."""
     _check(lib().apmoe_moe_forward(ctx.handle, table.handle, layer, ptr(x), ptr(w_router), ptr(bias), T, topk,
+                                   n_shared,
                                    int(renormalize), ptr(ws), ws_bytes, ptr(out), stream_handle(stream)),
            "apmoe_moe_forward")
 

@@ -484,8 +484,9 @@ apmoe_status apmoe_pack_planes(apmoe_ctx *ctx, const uint8_t *codes, int32_t n, 
 // ----------------------------------------------------------------------------
 
 apmoe_status apmoe_route(apmoe_ctx *ctx, const uint16_t *x, const uint16_t *w_router, const float *bias, int32_t T,
-                         int32_t H, int32_t E, int32_t topk, int32_t renormalize, int32_t *topk_ids, float *topk_w,
-                         int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv_perm, void *stream)
+                         int32_t H, int32_t E, int32_t topk, int32_t n_shared, int32_t renormalize,
+                         int32_t *topk_ids, float *topk_w, int32_t *counts, int32_t *offsets, int32_t *perm,
+                         int32_t *inv_perm, void *stream)
 {
     apmoe_status s = check_ctx(ctx);
     if (s != APMOE_OK)
@@ -496,19 +497,24 @@ apmoe_status apmoe_route(apmoe_ctx *ctx, const uint16_t *x, const uint16_t *w_ro
         return fail(APMOE_INVALID_ARG, "E=%d outside 1..%d", E, APMOE_MAX_EXPERTS);
     if (topk < 1 || topk > E || topk > APMOE_MAX_TOPK)
         return fail(APMOE_INVALID_ARG, "topk=%d (need 1..min(E,%d))", topk, APMOE_MAX_TOPK);
+    if (n_shared < 0 || n_shared > APMOE_MAX_SHARED || E + n_shared > APMOE_MAX_EXPERTS)
+        return fail(APMOE_INVALID_ARG, "n_shared=%d (need 0..%d and E + n_shared <= %d)", n_shared, APMOE_MAX_SHARED,
+                    APMOE_MAX_EXPERTS);
     if (!counts || !offsets)
         return fail(APMOE_INVALID_ARG, "counts / offsets is NULL");
     if (T > 0 && (!x || !w_router || !topk_ids || !topk_w || !perm || !inv_perm))
         return fail(APMOE_INVALID_ARG, "a required pointer is NULL");
     if (T > 0 && (!aligned16(x) || !aligned16(w_router)))
         return fail(APMOE_INVALID_ARG, "x / w_router not 16-byte aligned");
-    if ((int64_t)T * topk > (int64_t)1 << 30)
+    const int kt = topk + n_shared;
+    if ((int64_t)T * kt > (int64_t)1 << 30)
         return fail(APMOE_INVALID_ARG, "T*topk too large");
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    hipError_t e = apmoe::launch_route_topk(x, w_router, bias, T, H, E, topk, renormalize, topk_ids, topk_w, st);
+    hipError_t e =
+        apmoe::launch_route_topk(x, w_router, bias, T, H, E, topk, n_shared, renormalize, topk_ids, topk_w, st);
     if (e != hipSuccess)
         return hip_fail(e, "route_topk launch");
-    e = apmoe::launch_route_sort(topk_ids, T * topk, E, counts, offsets, perm, inv_perm, st);
+    e = apmoe::launch_route_sort(topk_ids, T * kt, E + n_shared, counts, offsets, perm, inv_perm, st);
     if (e != hipSuccess)
         return hip_fail(e, "route_sort launch");
     return ok();
@@ -651,8 +657,8 @@ apmoe_status apmoe_route_stats(apmoe_ctx *ctx, const float *topk_w, const int32_
         return fail(APMOE_INVALID_ARG, "T=%d", T);
     if (E < 1 || E > APMOE_MAX_EXPERTS)
         return fail(APMOE_INVALID_ARG, "E=%d outside 1..%d", E, APMOE_MAX_EXPERTS);
-    if (topk < 1 || topk > E || topk > APMOE_MAX_TOPK)
-        return fail(APMOE_INVALID_ARG, "topk=%d (need 1..min(E,%d))", topk, APMOE_MAX_TOPK);
+    if (topk < 1 || topk > APMOE_MAX_ASSIGN)
+        return fail(APMOE_INVALID_ARG, "topk=%d (need 1..%d)", topk, APMOE_MAX_ASSIGN);
     if ((int64_t)T * topk > (int64_t)1 << 30)
         return fail(APMOE_INVALID_ARG, "T*topk too large");
     if (!mass || !total || !selections)
@@ -701,7 +707,7 @@ apmoe_status apmoe_gemm(apmoe_ctx *ctx, const apmoe_table *tbl, int32_t layer, i
         return fail(APMOE_NOT_RESIDENT, "table was never committed");
     if (tbl->device != ctx->device)
         return fail(APMOE_INVALID_ARG, "table lives on device %d, ctx on %d", tbl->device, ctx->device);
-    if (T < 0 || topk < 1 || topk > APMOE_MAX_TOPK)
+    if (T < 0 || topk < 1 || topk > APMOE_MAX_ASSIGN)
         return fail(APMOE_INVALID_ARG, "T=%d topk=%d", T, topk);
     if (out_dtype != APMOE_F16 && out_dtype != APMOE_F32)
         return fail(APMOE_UNSUPPORTED, "out_dtype %d", out_dtype);
@@ -748,7 +754,7 @@ apmoe_status apmoe_combine(apmoe_ctx *ctx, const void *y, int32_t y_dtype, const
     apmoe_status s = check_ctx(ctx);
     if (s != APMOE_OK)
         return s;
-    if (T < 0 || topk < 1 || topk > APMOE_MAX_TOPK || H < 8 || H % 8 != 0)
+    if (T < 0 || topk < 1 || topk > APMOE_MAX_ASSIGN || H < 8 || H % 8 != 0)
         return fail(APMOE_INVALID_ARG, "T=%d topk=%d H=%d", T, topk, H);
     if (y_dtype != APMOE_F16 && y_dtype != APMOE_F32)
         return fail(APMOE_UNSUPPORTED, "y_dtype %d", y_dtype);
@@ -798,13 +804,14 @@ WsLayout ws_layout(int T, int topk, int E, int H, int F)
 }
 }  // namespace
 
-apmoe_status apmoe_moe_workspace(const apmoe_table *tbl, int32_t layer, int32_t T, int32_t topk, size_t *bytes)
+apmoe_status apmoe_moe_workspace(const apmoe_table *tbl, int32_t layer, int32_t T, int32_t topk, int32_t n_shared,
+                                 size_t *bytes)
 {
     apmoe_status s = check_index(tbl, layer, 0, 0);
     if (s != APMOE_OK)
         return s;
-    if (!bytes || T < 0 || topk < 1)
-        return fail(APMOE_INVALID_ARG, "bytes NULL or T/topk invalid");
+    if (!bytes || T < 0 || topk < 1 || n_shared < 0 || n_shared >= tbl->E)
+        return fail(APMOE_INVALID_ARG, "bytes NULL or T/topk/n_shared invalid");
     int N0, K0, q0, N1, K1, q1;
     s = layer_shape(tbl, layer, APMOE_GATE_UP, &N0, &K0, &q0);
     if (s != APMOE_OK)
@@ -812,13 +819,14 @@ apmoe_status apmoe_moe_workspace(const apmoe_table *tbl, int32_t layer, int32_t 
     s = layer_shape(tbl, layer, APMOE_DOWN, &N1, &K1, &q1);
     if (s != APMOE_OK)
         return s;
-    *bytes = ws_layout(T, topk, tbl->E, K0, K1).total;
+    *bytes = ws_layout(T, topk + n_shared, tbl->E, K0, K1).total;
     return ok();
 }
 
 apmoe_status apmoe_moe_forward(apmoe_ctx *ctx, const apmoe_table *tbl, int32_t layer, const uint16_t *x,
                                const uint16_t *w_router, const float *bias, int32_t T, int32_t topk,
-                               int32_t renormalize, void *ws, size_t ws_bytes, uint16_t *out, void *stream)
+                               int32_t n_shared, int32_t renormalize, void *ws, size_t ws_bytes, uint16_t *out,
+                               void *stream)
 {
     apmoe_status s = check_ctx(ctx);
     if (s != APMOE_OK)
@@ -837,7 +845,10 @@ apmoe_status apmoe_moe_forward(apmoe_ctx *ctx, const apmoe_table *tbl, int32_t l
     if (N0 != 2 * F || N1 != H)
         return fail(APMOE_INVALID_ARG, "layer %d shapes: gate_up %dx%d, down %dx%d are not [2F x H], [H x F]",
                     layer, N0, K0, N1, K1);
-    const WsLayout L = ws_layout(T, topk, tbl->E, H, F);
+    if (n_shared < 0 || n_shared >= tbl->E)
+        return fail(APMOE_INVALID_ARG, "n_shared=%d with %d experts in the table", n_shared, tbl->E);
+    const int kt = topk + n_shared;  // assignments per token
+    const WsLayout L = ws_layout(T, kt, tbl->E, H, F);
     if (!ws || ws_bytes < L.total || ((uintptr_t)ws & 255u))
         return fail(APMOE_INVALID_ARG, "workspace NULL, unaligned or smaller than %zu bytes", L.total);
     if (T > 0 && (!out || !aligned16(out)))
@@ -852,20 +863,20 @@ apmoe_status apmoe_moe_forward(apmoe_ctx *ctx, const apmoe_table *tbl, int32_t l
     uint16_t *h = reinterpret_cast<uint16_t *>(w + L.h);
     uint16_t *a = reinterpret_cast<uint16_t *>(w + L.a);
     float *y = reinterpret_cast<float *>(w + L.y);
-    s = apmoe_route(ctx, x, w_router, bias, T, H, tbl->E, topk, renormalize, ids, tw, counts, offsets, perm, inv,
-                    stream);
+    s = apmoe_route(ctx, x, w_router, bias, T, H, tbl->E - n_shared, topk, n_shared, renormalize, ids, tw, counts,
+                    offsets, perm, inv, stream);
     if (s != APMOE_OK || T == 0)
         return s;
-    s = apmoe_gemm(ctx, tbl, layer, APMOE_GATE_UP, x, 1, perm, offsets, T, topk, h, APMOE_F16, stream);
+    s = apmoe_gemm(ctx, tbl, layer, APMOE_GATE_UP, x, 1, perm, offsets, T, kt, h, APMOE_F16, stream);
     if (s != APMOE_OK)
         return s;
-    s = apmoe_act(ctx, h, T * topk, F, a, stream);
+    s = apmoe_act(ctx, h, T * kt, F, a, stream);
     if (s != APMOE_OK)
         return s;
-    s = apmoe_gemm(ctx, tbl, layer, APMOE_DOWN, a, 0, perm, offsets, T, topk, y, APMOE_F32, stream);
+    s = apmoe_gemm(ctx, tbl, layer, APMOE_DOWN, a, 0, perm, offsets, T, kt, y, APMOE_F32, stream);
     if (s != APMOE_OK)
         return s;
-    return apmoe_combine(ctx, y, APMOE_F32, tw, inv, T, topk, H, out, stream);
+    return apmoe_combine(ctx, y, APMOE_F32, tw, inv, T, kt, H, out, stream);
 }
 
 }  // extern "C"

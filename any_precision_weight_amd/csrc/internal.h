@@ -32,7 +32,7 @@ constexpr int kTileTokens = 256;
 inline size_t tiled_plane_words(int n, int k) { return (size_t)((n + 31) / 32) * (k / 128) * 128; }
 
 hipError_t launch_route_topk(const uint16_t *x, const uint16_t *wr, const float *bias, int T, int H, int E, int topk,
-                             int renormalize, int32_t *ids, float *w, hipStream_t s);
+                             int n_shared, int renormalize, int32_t *ids, float *w, hipStream_t s);
 hipError_t launch_route_sort(const int32_t *ids, int R, int E, int32_t *counts, int32_t *offsets, int32_t *perm,
                              int32_t *inv_perm, hipStream_t s);
 hipError_t launch_route_stats(const float *w, const int32_t *perm, const int32_t *offsets, int E, double *mass,

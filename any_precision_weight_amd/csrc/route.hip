@@ -30,7 +30,7 @@ constexpr int kRouteThreads = 256;
 __global__ void __launch_bounds__(kRouteThreads) route_topk_kernel(const uint16_t *__restrict__ x,
                                                                    const uint16_t *__restrict__ wr,
                                                                    const float *__restrict__ bias, int T, int H,
-                                                                   int E, int topk, int renormalize,
+                                                                   int E, int topk, int n_shared, int renormalize,
                                                                    int32_t *__restrict__ ids,
                                                                    float *__restrict__ wout)
 {
@@ -114,9 +114,14 @@ __global__ void __launch_bounds__(kRouteThreads) route_topk_kernel(const uint16_
             for (int e = 0; e < E; ++e)
                 den += exp(zs[e] - zmax);
         }
+        const int kt = topk + n_shared;  // row: routed choices, then the shared experts (weight 1)
         for (int j = 0; j < topk; ++j) {
-            ids[(size_t)t * topk + j] = esel[j];
-            wout[(size_t)t * topk + j] = (float)(exp(zsel[j] - zmax) / den);
+            ids[(size_t)t * kt + j] = esel[j];
+            wout[(size_t)t * kt + j] = (float)(exp(zsel[j] - zmax) / den);
+        }
+        for (int s = 0; s < n_shared; ++s) {
+            ids[(size_t)t * kt + topk + s] = E + s;
+            wout[(size_t)t * kt + topk + s] = 1.0f;
         }
     }
 }
@@ -247,12 +252,12 @@ __global__ void __launch_bounds__(kStatsThreads) route_stats_kernel(const float 
 }  // namespace
 
 hipError_t launch_route_topk(const uint16_t *x, const uint16_t *wr, const float *bias, int T, int H, int E, int topk,
-                             int renormalize, int32_t *ids, float *w, hipStream_t s)
+                             int n_shared, int renormalize, int32_t *ids, float *w, hipStream_t s)
 {
     if (T <= 0)
         return hipSuccess;
     hipLaunchKernelGGL(route_topk_kernel, dim3(T), dim3(kRouteThreads), 0, s, x, wr, bias, T, H, E, topk,
-                       renormalize, ids, w);
+                       n_shared, renormalize, ids, w);
     return hipGetLastError();
 }
 

@@ -78,7 +78,7 @@ def algorithmic_bytes(cfg, counts, qmap, kind):
 
 def layer_bytes(cfg, counts, qmap):
     """Whole-layer algorithmic bytes: active weights + x + router + out + routing metadata."""
-    T, H, E, k = cfg.tokens, cfg.hidden, cfg.experts, cfg.topk
+    T, H, E, k = cfg.tokens, cfg.hidden, cfg.experts, cfg.assign
     w = 0
     for kind in (0, 1):
         N, K = cfg.block_shape(kind)
@@ -119,7 +119,7 @@ class BenchLayer:
         self.cfg = cfg
         self.ctx = apw.Context(0)
         self.copies = copies
-        E = cfg.experts
+        E = cfg.weight_experts
         self.q = synth.gen_qmap(cfg, 0)
         if uniform_q:
             self.q[:] = uniform_q
@@ -143,7 +143,7 @@ class BenchLayer:
         dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
         self.x_d, self.wr_d = dev(self.x), dev(self.wr)
         self.bias_d = None if self.bias is None else dev(self.bias)
-        T, k, H, F = cfg.tokens, cfg.topk, cfg.hidden, cfg.ffn
+        T, k, H, F = cfg.tokens, cfg.assign, cfg.hidden, cfg.ffn
         R = T * k
         z = lambda shape, dt: torch.empty(shape, dtype=dt, device="cuda")
         self.b = dict(ids=z((T, k), torch.int32), w=z((T, k), torch.float32), counts=z(E, torch.int32),
@@ -153,9 +153,9 @@ class BenchLayer:
 
     def step(self, slot, ev=None):
         apw, b, cfg, c = self.apw, self.b, self.cfg, self.ctx
-        T, k, H, F, E = cfg.tokens, cfg.topk, cfg.hidden, cfg.ffn, cfg.experts
-        apw.route(c, self.x_d, self.wr_d, self.bias_d, T, H, E, k, cfg.renormalize, b["ids"], b["w"], b["counts"],
-                  b["offsets"], b["perm"], b["inv"])
+        T, k, H, F, E = cfg.tokens, cfg.assign, cfg.hidden, cfg.ffn, cfg.experts
+        apw.route(c, self.x_d, self.wr_d, self.bias_d, T, H, E, cfg.topk, cfg.renormalize, b["ids"], b["w"],
+                  b["counts"], b["offsets"], b["perm"], b["inv"], n_shared=cfg.shared)
         if ev:
             ev[0].record()
         apw.gemm(c, self.rw.table, slot, apw.GATE_UP, self.x_d, True, b["perm"], b["offsets"], T, k, b["h"], apw.F16)
@@ -171,11 +171,12 @@ class BenchLayer:
 
     def oracle(self):
         import oracle
-        E = self.cfg.experts
+        E = self.cfg.weight_experts
         return oracle.moe_forward(self.x, self.wr, self.bias, self.cfg.topk,
                                   [self.planes[(e, 0)] for e in range(E)], [self.parent[(e, 0)] for e in range(E)],
                                   self.q[:, 0], [self.planes[(e, 1)] for e in range(E)],
-                                  [self.parent[(e, 1)] for e in range(E)], self.q[:, 1])
+                                  [self.parent[(e, 1)] for e in range(E)], self.q[:, 1],
+                                  renormalize=self.cfg.renormalize, n_shared=self.cfg.shared)
 
 
 def main() -> int:
@@ -238,7 +239,7 @@ def main() -> int:
     lb = layer_bytes(cfg, counts, L.q)
     gu_gbs = gu_bytes / (gu_ms * 1e-3) / 1e9
     tokens_per_s = cfg.tokens / (ms * 1e-3)
-    flops = 2 * cfg.tokens * cfg.topk * 3 * cfg.hidden * cfg.ffn + 2 * cfg.tokens * cfg.experts * cfg.hidden
+    flops = 2 * cfg.tokens * cfg.assign * 3 * cfg.hidden * cfg.ffn + 2 * cfg.tokens * cfg.experts * cfg.hidden
     tflops = flops / (ms * 1e-3) / 1e12
     print(f"[bench] {cfg.name}: {tflops:.1f} TFLOP/s  "
           f"step {ms * 1e3:.1f} us  gate_up {gu_ms * 1e3:.1f} us ({gu_gbs:.0f} GB/s)  "
@@ -259,8 +260,9 @@ def main() -> int:
         "dtype": "fp16 (fp32 accumulate; fp64 router)",
         "data": "synthetic (seeded bit-planes, sorted N(0,0.02) fp16 LUTs, N(0,1) fp16 activations)",
         "config": {"workload": cfg.name, "tokens": cfg.tokens, "hidden": cfg.hidden, "ffn": cfg.ffn,
-                   "experts": cfg.experts, "topk": cfg.topk, "qmap_mean_bits": float(L.q.mean()),
-                   "counts": [int(c) for c in counts], "weight_copies": args.copies},
+                   "experts": cfg.experts, "shared_experts": cfg.shared, "topk": cfg.topk,
+                   "qmap_mean_bits": float(L.q.mean()), "counts": [int(c) for c in counts],
+                   "weight_copies": args.copies},
         "layer_gbps": round(lb / (ms * 1e-3) / 1e9, 1),
         "layer_hbm_frac": round(lb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "kernels_us": {"gate_up": round(gu_ms * 1e3, 2), "down": round(dn_ms * 1e3, 2)},
@@ -269,7 +271,7 @@ def main() -> int:
     }
     # the gate_up product is the dominant kernel; it is HBM-bound below the ridge point
     # (peak FLOP/s over peak bytes/s) and MFMA-bound above it
-    gu_flops = 2 * cfg.tokens * cfg.topk * 2 * cfg.ffn * cfg.hidden
+    gu_flops = 2 * cfg.tokens * cfg.assign * 2 * cfg.ffn * cfg.hidden
     sources = ["gemm.hip", "gemm_tile.hip"]
     if gu_flops / gu_bytes > MFMA_F16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
         tf = gu_flops / (gu_ms * 1e-3) / 1e12

@@ -74,6 +74,8 @@ typedef int32_t apmoe_status;
 #define APMOE_PLANES 8
 #define APMOE_MAX_EXPERTS 256
 #define APMOE_MAX_TOPK 8
+#define APMOE_MAX_SHARED 8 /* shared experts per layer */
+#define APMOE_MAX_ASSIGN (APMOE_MAX_TOPK + APMOE_MAX_SHARED) /* assignments per token */
 
 typedef struct apmoe_ctx apmoe_ctx;
 typedef struct apmoe_table apmoe_table;
@@ -235,20 +237,26 @@ apmoe_status apmoe_page_in(apmoe_ctx *ctx, apmoe_table *tbl, int32_t layer, int3
 
 /*
  * Router (Section 2.1: the router weights E experts and keeps the top K).
- *   x [T][H] fp16, w_router [E][H] fp16, bias [E] fp32 or NULL.
+ *   x [T][H] fp16, w_router [E][H] fp16 (E routed experts), bias [E] fp32 or NULL.
  *   logit z[t][e] = sum_h x*w in fp64 (exact fp16 products), then + bias[e].
  *   topk_ids [T][topk] : experts by descending logit, ties to the lower index.
  *   topk_w   [T][topk] : fp32; renormalize != 0: softmax over the selected
  *                        logits; else the full softmax over E, at the selected.
- *   counts [E], offsets [E+1] (offsets[E] = T*topk), perm [T*topk]: assignment
- *   ids a = t*topk + j grouped by expert ascending, ascending a inside a
- *   group; inv_perm [T*topk]: inv_perm[perm[r]] = r.
- * Limits: 1 <= E <= 256, 1 <= topk <= min(E, 8), T >= 0 (T = 0 writes counts
- * and offsets only), H % 8 == 0.
+ *   Shared experts (Table 1 lists "+4" / "+1" experts visited by every token):
+ *   experts E .. E+n_shared-1 have no router row; the pages give no gate for them,
+ *   so they follow the topk routed experts in every token's row with weight 1.
+ *   With kt = topk + n_shared and Et = E + n_shared:
+ *   topk_ids, topk_w [T][kt]; counts [Et], offsets [Et+1] (offsets[Et] = T*kt),
+ *   perm [T*kt]: assignment ids a = t*kt + j grouped by expert ascending,
+ *   ascending a inside a group; inv_perm [T*kt]: inv_perm[perm[r]] = r.
+ *   The later steps take kt as their topk and Et as the layer's expert count.
+ * Limits: 1 <= E, E + n_shared <= 256, 1 <= topk <= min(E, 8), 0 <= n_shared <= 8,
+ * T >= 0 (T = 0 writes counts and offsets only), H % 8 == 0.
  */
 apmoe_status apmoe_route(apmoe_ctx *ctx, const uint16_t *x, const uint16_t *w_router, const float *bias, int32_t T,
-                         int32_t H, int32_t E, int32_t topk, int32_t renormalize, int32_t *topk_ids, float *topk_w,
-                         int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv_perm, void *stream);
+                         int32_t H, int32_t E, int32_t topk, int32_t n_shared, int32_t renormalize,
+                         int32_t *topk_ids, float *topk_w, int32_t *counts, int32_t *offsets, int32_t *perm,
+                         int32_t *inv_perm, void *stream);
 
 /*
  * Online routing statistics (Section 2.1, Eq. 1: the routing mass of expert e is
@@ -257,12 +265,15 @@ apmoe_status apmoe_route(apmoe_ctx *ctx, const uint16_t *x, const uint16_t *w_ro
  * batch's contribution to caller-owned device accumulators:
  *   mass[e]       += sum of topk_w[t][j] over assignments routed to e   (fp64)
  *   selections[e] += number of assignments routed to e                  (int64)
- *   total[0]      += sum of all topk_w[t][j]                             (fp64)
- * topk_w, perm and offsets are the outputs of apmoe_route for the same batch
- * (perm groups the assignments by expert).  The caller zeroes the accumulators
- * once and reads mass[e] / total[0].  Sums are fp64 with a fixed reduction order:
+ *   total[0]      += sum of the topk_w[t][j] of experts 0 .. E-1         (fp64)
+ * for e = 0 .. E-1.  topk_w, perm and offsets are the outputs of apmoe_route for
+ * the same batch (perm groups the assignments by expert); topk is their row
+ * stride.  With shared experts pass topk + n_shared as topk and the routed E:
+ * the statistics then cover the routed choices only, as Eq. 1 does (shared
+ * experts have no routing weight).  The caller zeroes the accumulators once and
+ * reads mass[e] / total[0].  Sums are fp64 with a fixed reduction order:
  * repeated calls give identical bits.  Calls that overlap on the same
- * accumulators race.  Limits as apmoe_route; T = 0 adds nothing.
+ * accumulators race.  Limits: 1 <= E <= 256, 1 <= topk <= 16; T = 0 adds nothing.
  */
 apmoe_status apmoe_route_stats(apmoe_ctx *ctx, const float *topk_w, const int32_t *perm, const int32_t *offsets,
                                int32_t T, int32_t topk, int32_t E, double *mass, double *total, int64_t *selections,
@@ -295,17 +306,21 @@ apmoe_status apmoe_combine(apmoe_ctx *ctx, const void *y, int32_t y_dtype, const
                            const int32_t *inv_perm, int32_t T, int32_t topk, int32_t H, uint16_t *out, void *stream);
 
 /* Device workspace bytes needed by apmoe_moe_forward for one layer of tbl. */
-apmoe_status apmoe_moe_workspace(const apmoe_table *tbl, int32_t layer, int32_t T, int32_t topk, size_t *bytes);
+apmoe_status apmoe_moe_workspace(const apmoe_table *tbl, int32_t layer, int32_t T, int32_t topk, int32_t n_shared,
+                                 size_t *bytes);
 
 /*
  * Whole layer: route, gate_up (gather, fp16 h), act, down (fp32 y), combine.
+ * The table's experts of the layer are the routed ones (w_router rows) followed by
+ * n_shared shared experts.
  * ws is caller-owned device memory of at least apmoe_moe_workspace bytes, 256-byte
  * aligned; it holds ids, weights, counts, offsets, perm, inv_perm, h, a and y.
  * out fp16 [T][H].
  */
 apmoe_status apmoe_moe_forward(apmoe_ctx *ctx, const apmoe_table *tbl, int32_t layer, const uint16_t *x,
                                const uint16_t *w_router, const float *bias, int32_t T, int32_t topk,
-                               int32_t renormalize, void *ws, size_t ws_bytes, uint16_t *out, void *stream);
+                               int32_t n_shared, int32_t renormalize, void *ws, size_t ws_bytes, uint16_t *out,
+                               void *stream);
 
 #ifdef __cplusplus
 }

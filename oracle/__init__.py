@@ -63,13 +63,13 @@ def _declare(L):
     L.apo_lut_level.argtypes = [P, I64, I32, P]
     L.apo_block_bytes.restype = I64
     L.apo_block_bytes.argtypes = [I64, I64, I32]
-    L.apo_route.argtypes = [P, P, P, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, P, P]
+    L.apo_route.argtypes = [P, P, P, I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, P, P]
     L.apo_block_gemm.argtypes = [P, P, I32, I64, I64, P, I64, P]
     L.apo_dequant_block.argtypes = [P, P, I32, I64, I64, P]
     L.apo_act.argtypes = [P, I64, I64, P]
     L.apo_combine.argtypes = [P, P, P, I32, I32, I64, P]
     L.apo_moe_forward.restype = I32
-    L.apo_moe_forward.argtypes = [P, P, P, I32, I32, I32, I32, I32, I32,
+    L.apo_moe_forward.argtypes = [P, P, P, I32, I32, I32, I32, I32, I32, I32,
                                   P, P, P, P, P, P, P, I32,
                                   P, P, P, P, P, P, P, P, P, P, P, P]
     L.apo_num_threads.restype = I32
@@ -148,26 +148,30 @@ def block_bytes(N: int, K: int, b: int) -> int:
 
 # -- route ------------------------------------------------------------------
 
-def route(x, wr, bias, topk: int, renormalize: bool = True, want_absdot: bool = False):
+def route(x, wr, bias, topk: int, renormalize: bool = True, want_absdot: bool = False, n_shared: int = 0):
+    """Router of Section 2.1 (see apo_route); with n_shared > 0 the shared experts
+    E .. E+n_shared-1 follow the topk routed ones in every token's row, weight 1."""
     x = _c(x, np.float16).view(np.uint16)
     wr = _c(wr, np.float16).view(np.uint16)
     T, H = x.shape
     E = wr.shape[0]
-    assert E <= 1024 and 1 <= topk <= E
+    assert E <= 1024 and 1 <= topk <= E and n_shared >= 0
     b = None if bias is None else _c(bias, np.float32)
-    R = T * topk
+    kt, Et = topk + n_shared, E + n_shared
+    R = T * kt
     out = dict(
         logits=np.empty((T, E), np.float64),
-        ids=np.empty((T, topk), np.int32),
-        w64=np.empty((T, topk), np.float64),
-        w32=np.empty((T, topk), np.float32),
-        counts=np.empty(E, np.int32),
-        offsets=np.empty(E + 1, np.int32),
+        ids=np.empty((T, kt), np.int32),
+        w64=np.empty((T, kt), np.float64),
+        w32=np.empty((T, kt), np.float32),
+        counts=np.empty(Et, np.int32),
+        offsets=np.empty(Et + 1, np.int32),
         perm=np.empty(R, np.int32),
         inv_perm=np.empty(R, np.int32),
     )
     absdot = np.empty((T, E), np.float64) if want_absdot else None
-    lib().apo_route(_p(x), _p(wr), _p(b), T, H, E, topk, int(renormalize), _p(out["logits"]), _p(out["ids"]),
+    lib().apo_route(_p(x), _p(wr), _p(b), T, H, E, topk, n_shared, int(renormalize), _p(out["logits"]),
+                    _p(out["ids"]),
                     _p(out["w64"]), _p(out["w32"]), _p(out["counts"]), _p(out["offsets"]), _p(out["perm"]),
                     _p(out["inv_perm"]), _p(absdot))
     if want_absdot:
@@ -225,13 +229,17 @@ def combine(y: np.ndarray, w: np.ndarray, inv_perm: np.ndarray, topk: int) -> np
 # -- whole layer --------------------------------------------------------------
 
 def moe_forward(x, wr, bias, topk: int, planes_gu, lutp_gu, q_gu, planes_dn, lutp_dn, q_dn,
-                renormalize: bool = True, eval_tokens=None, intermediates: bool = False):
+                renormalize: bool = True, eval_tokens=None, intermediates: bool = False, n_shared: int = 0):
     """One MoE layer in fp64.  planes_* / lutp_* are lists over experts of uint32
-    [8][N][K/32] planes and fp16 [N][256] parent LUTs; q_* are int arrays [E]."""
+    [8][N][K/32] planes and fp16 [N][256] parent LUTs; q_* are int arrays.  The
+    lists cover the E routed experts (router rows) followed by n_shared shared
+    experts."""
     x = _c(x, np.float16).view(np.uint16)
     wr = _c(wr, np.float16).view(np.uint16)
     T, H = x.shape
-    E = wr.shape[0]
+    Er = wr.shape[0]
+    E = Er + n_shared  # experts with weights
+    assert len(planes_gu) == E
     F = planes_dn[0].shape[2] * 32
     b = None if bias is None else _c(bias, np.float32)
     keep = []
@@ -247,14 +255,15 @@ def moe_forward(x, wr, bias, topk: int, planes_gu, lutp_gu, q_gu, planes_dn, lut
     ld = ptr_array([np.asarray(a, np.float16).view(np.uint16) for a in lutp_dn], np.uint16)
     qg = _c(q_gu, np.int32)
     qd = _c(q_dn, np.int32)
-    R = T * topk
+    kt = topk + n_shared
+    R = T * kt
     ev = None if eval_tokens is None else _c(eval_tokens, np.int32)
     n_eval = T if ev is None else ev.size
     res = dict(
-        ids=np.empty((T, topk), np.int32), w64=np.empty((T, topk), np.float64),
-        w32=np.empty((T, topk), np.float32), counts=np.empty(E, np.int32),
+        ids=np.empty((T, kt), np.int32), w64=np.empty((T, kt), np.float64),
+        w32=np.empty((T, kt), np.float32), counts=np.empty(E, np.int32),
         offsets=np.empty(E + 1, np.int32), perm=np.empty(R, np.int32), inv_perm=np.empty(R, np.int32),
-        logits=np.empty((T, E), np.float64), out=np.empty((n_eval, H), np.float64),
+        logits=np.empty((T, Er), np.float64), out=np.empty((n_eval, H), np.float64),
     )
     h = a = y = None
     if intermediates:
@@ -263,7 +272,7 @@ def moe_forward(x, wr, bias, topk: int, planes_gu, lutp_gu, q_gu, planes_dn, lut
         a = np.zeros((R, F), np.float64)
         y = np.zeros((R, H), np.float64)
     rc = lib().apo_moe_forward(
-        _p(x), _p(wr), _p(b), T, H, F, E, topk, int(renormalize),
+        _p(x), _p(wr), _p(b), T, H, F, Er, topk, n_shared, int(renormalize),
         ctypes.cast(pg, P), ctypes.cast(lg, P), _p(qg), ctypes.cast(pd, P), ctypes.cast(ld, P), _p(qd),
         _p(ev), n_eval, _p(res["ids"]), _p(res["w64"]), _p(res["w32"]), _p(res["counts"]),
         _p(res["offsets"]), _p(res["perm"]), _p(res["inv_perm"]), _p(res["logits"]), _p(res["out"]),

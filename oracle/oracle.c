@@ -183,11 +183,18 @@ int64_t apo_block_bytes(int64_t N, int64_t K, int b)
  * assignments a = t*k + j grouped by expert (e ascending), inside an expert by
  * a ascending; inv_perm[perm[r]] = r.
  * absdot[t][e] (optional) = sum |x*Wr| + |bias|, for rounding-error bounds.
+ * Shared experts (n_shared >= 0, the "+4" / "+1" experts of the models in Table 1):
+ * experts E .. E+n_shared-1 have no router row and are visited by every token.  The
+ * pages give no gate for them; they are appended to every token's assignments after
+ * the k routed ones, with weight 1 (their outputs add to the routed mixture).  Rows
+ * of ids / w then hold kt = k + n_shared entries, and counts / offsets / perm cover
+ * the E + n_shared experts.
  */
 void apo_route(const uint16_t *x, const uint16_t *wr, const float *bias, int T, int H, int E, int k,
-               int renormalize, double *logits, int32_t *ids, double *w64, float *w32, int32_t *counts,
-               int32_t *offsets, int32_t *perm, int32_t *inv_perm, double *absdot)
+               int n_shared, int renormalize, double *logits, int32_t *ids, double *w64, float *w32,
+               int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv_perm, double *absdot)
 {
+    const int kt = k + n_shared;
 #pragma omp parallel for schedule(static)
     for (int t = 0; t < T; ++t) {
         for (int e = 0; e < E; ++e) {
@@ -218,33 +225,38 @@ void apo_route(const uint16_t *x, const uint16_t *wr, const float *bias, int T, 
                     best = e;
             }
             taken[best] = 1;
-            ids[(int64_t)t * k + j] = best;
+            ids[(int64_t)t * kt + j] = best;
         }
-        double zmax = z[ids[(int64_t)t * k]];
+        double zmax = z[ids[(int64_t)t * kt]];
         double den = 0.0;
         if (renormalize) {
             for (int j = 0; j < k; ++j)
-                den += exp(z[ids[(int64_t)t * k + j]] - zmax);
+                den += exp(z[ids[(int64_t)t * kt + j]] - zmax);
         } else {
             for (int e = 0; e < E; ++e)
                 den += exp(z[e] - zmax);
         }
         for (int j = 0; j < k; ++j) {
-            double w = exp(z[ids[(int64_t)t * k + j]] - zmax) / den;
-            w64[(int64_t)t * k + j] = w;
-            w32[(int64_t)t * k + j] = (float)w;
+            double w = exp(z[ids[(int64_t)t * kt + j]] - zmax) / den;
+            w64[(int64_t)t * kt + j] = w;
+            w32[(int64_t)t * kt + j] = (float)w;
+        }
+        for (int s = 0; s < n_shared; ++s) {
+            ids[(int64_t)t * kt + k + s] = E + s;
+            w64[(int64_t)t * kt + k + s] = 1.0;
+            w32[(int64_t)t * kt + k + s] = 1.0f;
         }
     }
-    const int R = T * k;
-    for (int e = 0; e < E; ++e)
+    const int R = T * kt, Et = E + n_shared;
+    for (int e = 0; e < Et; ++e)
         counts[e] = 0;
     for (int a = 0; a < R; ++a)
         counts[ids[a]]++;
     offsets[0] = 0;
-    for (int e = 0; e < E; ++e)
+    for (int e = 0; e < Et; ++e)
         offsets[e + 1] = offsets[e] + counts[e];
     int r = 0;
-    for (int e = 0; e < E; ++e)
+    for (int e = 0; e < Et; ++e)
         for (int a = 0; a < R; ++a)
             if (ids[a] == e)
                 perm[r++] = a;
@@ -329,17 +341,21 @@ void apo_combine(const double *y, const double *w, const int32_t *inv_perm, int 
  * Only assignments of tokens listed in eval_tokens (n_eval of them, NULL = all)
  * are carried through the experts; out is [n_eval][H].  Route outputs are for all
  * T tokens.  If h_out / a_out / y_out are non-NULL (all tokens only) they receive
- * the intermediates in expert-grouped row order: [T*k][2F], [T*k][F], [T*k][H].
+ * the intermediates in expert-grouped row order: [T*kt][2F], [T*kt][F], [T*kt][H].
+ * E routed experts (router rows) plus n_shared shared experts (see apo_route); the
+ * plane / LUT / q arrays cover all E + n_shared experts, kt = k + n_shared.
  */
 int apo_moe_forward(const uint16_t *x, const uint16_t *wr, const float *bias, int T, int H, int F, int E, int k,
-                    int renormalize, const uint32_t *const *planes_gu, const uint16_t *const *lutp_gu,
+                    int n_shared, int renormalize, const uint32_t *const *planes_gu, const uint16_t *const *lutp_gu,
                     const int32_t *q_gu, const uint32_t *const *planes_dn, const uint16_t *const *lutp_dn,
                     const int32_t *q_dn, const int32_t *eval_tokens, int n_eval, int32_t *ids, double *w64,
                     float *w32, int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv_perm, double *logits,
                     double *out, double *h_out, double *a_out, double *y_out)
 {
-    const int R = T * k;
-    apo_route(x, wr, bias, T, H, E, k, renormalize, logits, ids, w64, w32, counts, offsets, perm, inv_perm, NULL);
+    const int kt = k + n_shared, Et = E + n_shared;
+    const int R = T * kt;
+    apo_route(x, wr, bias, T, H, E, k, n_shared, renormalize, logits, ids, w64, w32, counts, offsets, perm, inv_perm,
+              NULL);
 
     unsigned char *want = (unsigned char *)calloc((size_t)T, 1);
     if (!want)
@@ -357,12 +373,12 @@ int apo_moe_forward(const uint16_t *x, const uint16_t *wr, const float *bias, in
         free(want);
         return 1;
     }
-    for (int e = 0; e < E; ++e) {
+    for (int e = 0; e < Et; ++e) {
         /* rows of expert e whose token is evaluated */
         int M = 0;
         int *rows = (int *)malloc(sizeof(int) * (size_t)(counts[e] + 1));
         for (int r = offsets[e]; r < offsets[e + 1]; ++r)
-            if (want[perm[r] / k])
+            if (want[perm[r] / kt])
                 rows[M++] = r;
         if (M == 0) {
             free(rows);
@@ -376,7 +392,7 @@ int apo_moe_forward(const uint16_t *x, const uint16_t *wr, const float *bias, in
 
         double *xin = (double *)malloc(sizeof(double) * (size_t)M * H);
         for (int m = 0; m < M; ++m) {
-            const int t = perm[rows[m]] / k;
+            const int t = perm[rows[m]] / kt;
             for (int c = 0; c < H; ++c)
                 xin[(size_t)m * H + c] = apo_h2d(x[(int64_t)t * H + c]);
         }
@@ -408,8 +424,8 @@ int apo_moe_forward(const uint16_t *x, const uint16_t *wr, const float *bias, in
         const int t = eval_tokens ? eval_tokens[n_i] : n_i;
         for (int n = 0; n < H; ++n) {
             double s = 0.0;
-            for (int j = 0; j < k; ++j)
-                s += w64[t * k + j] * y[(size_t)inv_perm[t * k + j] * H + n];
+            for (int j = 0; j < kt; ++j)
+                s += w64[t * kt + j] * y[(size_t)inv_perm[t * kt + j] * H + n];
             out[(size_t)n_i * H + n] = s;
         }
     }

@@ -117,11 +117,22 @@ class MoEConfig:
     zipf_s: float | None = None
     qmode: str = "u38"
     renormalize: bool = True
+    shared: int = 0
     note: str = field(default="", compare=False)
 
     @property
+    def assign(self) -> int:
+        """Expert rows per token: the topk routed ones, then every shared expert."""
+        return self.topk + self.shared
+
+    @property
+    def weight_experts(self) -> int:
+        """Experts holding weights: the `experts` routed ones, then the shared ones."""
+        return self.experts + self.shared
+
+    @property
     def rows(self) -> int:
-        return self.tokens * self.topk
+        return self.tokens * self.assign
 
     def block_shape(self, kind: int) -> tuple[int, int]:
         """(N, K) of a linear-block: gate_up is [2F x H], down is [H x F]."""
@@ -142,6 +153,18 @@ CONFIGS = [
     MoEConfig("mixtral8x7b_32layer_decode_t32", tokens=32, hidden=4096, ffn=14336, experts=8,
               topk=2, seed=4, layers=32, qmode="maps",
               note="32 layers x 8 experts resident, decode batch 32, q map switch"),
+    # Many small experts plus shared experts.  The expert counts and top-k are the
+    # two fine-grained models the paper evaluates; their hidden and expert FFN sizes
+    # are not given there, so the ones below are chosen (fine-grained scale).
+    MoEConfig("qwen_60r4s_top4_decode_t64", tokens=64, hidden=2048, ffn=1408, experts=60, topk=4,
+              seed=5, shared=4, renormalize=False,
+              note="60 routed + 4 shared experts, top-4, decode batch 64; H=2048, F=1408 chosen"),
+    MoEConfig("gemma_128r1s_top8_decode_t64", tokens=64, hidden=2048, ffn=768, experts=128, topk=8,
+              seed=6, shared=1,
+              note="128 routed + 1 shared expert, top-8, decode batch 64; H=2048, F=768 chosen"),
+    MoEConfig("qwen_60r4s_top4_prefill_t2048", tokens=2048, hidden=2048, ffn=1408, experts=60, topk=4,
+              seed=7, shared=4, renormalize=False,
+              note="60 routed + 4 shared experts, top-4, prefill 2048 tokens; H=2048, F=1408 chosen"),
 ]
 
 
@@ -236,11 +259,12 @@ def gen_parent_lut_shape(seed: int, layer: int, expert: int, kind: int, N: int) 
 
 
 def gen_qmap(cfg: MoEConfig, layer: int = 0, which: int = 0) -> np.ndarray:
-    """Committed bitwidths q[e][kind] (kind 0 gate_up, 1 down) of one layer.
+    """Committed bitwidths q[e][kind] (kind 0 gate_up, 1 down) of one layer, for
+    the routed experts followed by the shared ones.
 
     which selects map A (0) or map B (1) for the "maps" workload.
     """
-    E = cfg.experts
+    E = cfg.weight_experts
     u = u64(cfg.seed, tensor_id(TID.QMAP, layer, 0, which), np.arange(2 * E)).reshape(E, 2)
     if cfg.qmode == "u38":
         return (3 + (u % np.uint64(6))).astype(np.int32)

@@ -51,7 +51,7 @@ class Layer:
         self.wr = synth.gen_router(cfg, layer)
         self.bias = synth.gen_bias(cfg, layer)
         self.q = synth.gen_qmap(cfg, layer) if qmap is None else np.asarray(qmap, np.int32)
-        E = cfg.experts
+        E = cfg.weight_experts
         self.planes = {}
         self.parent = {}
         own = resident is None
@@ -73,14 +73,14 @@ class Layer:
     # ------------------------------------------------------------------ GPU run
     def run(self, stream=None) -> dict:
         """Route, gate_up (fp16 h), act, down (fp32 y), combine -- each via the C ABI."""
-        cfg, T, k = self.cfg, self.T, self.cfg.topk
-        H, F, E = cfg.hidden, cfg.ffn, cfg.experts
-        R = T * k
+        cfg, T, k, kt = self.cfg, self.T, self.cfg.topk, self.cfg.assign
+        H, F, E, Et = cfg.hidden, cfg.ffn, cfg.experts, cfg.weight_experts
+        R = T * kt
         o = dict(
-            ids=torch.empty((T, k), dtype=torch.int32, device="cuda"),
-            w=torch.empty((T, k), dtype=torch.float32, device="cuda"),
-            counts=torch.empty(E, dtype=torch.int32, device="cuda"),
-            offsets=torch.empty(E + 1, dtype=torch.int32, device="cuda"),
+            ids=torch.empty((T, kt), dtype=torch.int32, device="cuda"),
+            w=torch.empty((T, kt), dtype=torch.float32, device="cuda"),
+            counts=torch.empty(Et, dtype=torch.int32, device="cuda"),
+            offsets=torch.empty(Et + 1, dtype=torch.int32, device="cuda"),
             perm=torch.empty(R, dtype=torch.int32, device="cuda"),
             inv_perm=torch.empty(R, dtype=torch.int32, device="cuda"),
             h=torch.empty((R, 2 * F), dtype=torch.float16, device="cuda"),
@@ -90,34 +90,35 @@ class Layer:
         )
         c = ctx()
         apw.route(c, self.x_d, self.wr_d, self.bias_d, T, H, E, k, cfg.renormalize, o["ids"], o["w"], o["counts"],
-                  o["offsets"], o["perm"], o["inv_perm"], stream)
-        apw.gemm(c, self.rw.table, self.layer, apw.GATE_UP, self.x_d, True, o["perm"], o["offsets"], T, k, o["h"],
+                  o["offsets"], o["perm"], o["inv_perm"], stream, n_shared=cfg.shared)
+        apw.gemm(c, self.rw.table, self.layer, apw.GATE_UP, self.x_d, True, o["perm"], o["offsets"], T, kt, o["h"],
                  apw.F16, stream)
         apw.act(c, o["h"], R, F, o["a"], stream)
-        apw.gemm(c, self.rw.table, self.layer, apw.DOWN, o["a"], False, o["perm"], o["offsets"], T, k, o["y"],
+        apw.gemm(c, self.rw.table, self.layer, apw.DOWN, o["a"], False, o["perm"], o["offsets"], T, kt, o["y"],
                  apw.F32, stream)
-        apw.combine(c, o["y"], apw.F32, o["w"], o["inv_perm"], T, k, H, o["out"], stream)
+        apw.combine(c, o["y"], apw.F32, o["w"], o["inv_perm"], T, kt, H, o["out"], stream)
         return o
 
     def run_fused_call(self, stream=None) -> torch.Tensor:
         """The same layer through apmoe_moe_forward."""
         cfg = self.cfg
-        nbytes = apw.moe_workspace(self.rw.table, self.layer, self.T, cfg.topk)
+        nbytes = apw.moe_workspace(self.rw.table, self.layer, self.T, cfg.topk, cfg.shared)
         ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
         out = torch.empty((self.T, cfg.hidden), dtype=torch.float16, device="cuda")
         apw.moe_forward(ctx(), self.rw.table, self.layer, self.x_d, self.wr_d, self.bias_d, self.T, cfg.topk,
-                        cfg.renormalize, ws, nbytes, out, stream)
+                        cfg.renormalize, ws, nbytes, out, stream, n_shared=cfg.shared)
         return out
 
     # ------------------------------------------------------------------ oracle
     def oracle(self, eval_tokens=None, intermediates=False, qmap=None) -> dict:
-        E = self.cfg.experts
+        E = self.cfg.weight_experts
         q = self.q if qmap is None else qmap
         return oracle.moe_forward(
             self.x, self.wr, self.bias, self.cfg.topk,
             [self.planes[(e, 0)] for e in range(E)], [self.parent[(e, 0)] for e in range(E)], q[:, 0],
             [self.planes[(e, 1)] for e in range(E)], [self.parent[(e, 1)] for e in range(E)], q[:, 1],
-            renormalize=self.cfg.renormalize, eval_tokens=eval_tokens, intermediates=intermediates)
+            renormalize=self.cfg.renormalize, eval_tokens=eval_tokens, intermediates=intermediates,
+            n_shared=self.cfg.shared)
 
 
 def check_route(o_gpu: dict, r: dict) -> None:

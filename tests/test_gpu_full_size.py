@@ -5,6 +5,9 @@
 - 32 Mixtral-8x7B layers resident (45 GB of planes), decode batch 32, with the q map
   switched between two committed maps at a launch boundary (PagedWeight, Section 3.3:
   commits only at safe boundaries).
+- Many small experts plus shared experts (the fine-grained models of Table 1: 60
+  routed + 4 shared top-4, 128 routed + 1 shared top-8; hidden and FFN sizes chosen),
+  decode and prefill.
 
 Bars: routing bit-exact for all tokens; sampled outputs within max-abs 1e-2 and
 relative L2 2e-3 of the oracle.
@@ -24,12 +27,12 @@ pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
 
 def _run_layer(rw, layer, x_d, wr_d, bias_d, cfg, T):
-    k, H, F, E = cfg.topk, cfg.hidden, cfg.ffn, cfg.experts
+    k, H, F, E, Et = cfg.assign, cfg.hidden, cfg.ffn, cfg.experts, cfg.weight_experts
     R = T * k
     o = dict(ids=torch.empty((T, k), dtype=torch.int32, device="cuda"),
              w=torch.empty((T, k), dtype=torch.float32, device="cuda"),
-             counts=torch.empty(E, dtype=torch.int32, device="cuda"),
-             offsets=torch.empty(E + 1, dtype=torch.int32, device="cuda"),
+             counts=torch.empty(Et, dtype=torch.int32, device="cuda"),
+             offsets=torch.empty(Et + 1, dtype=torch.int32, device="cuda"),
              perm=torch.empty(R, dtype=torch.int32, device="cuda"),
              inv_perm=torch.empty(R, dtype=torch.int32, device="cuda"),
              h=torch.empty((R, 2 * F), dtype=torch.float16, device="cuda"),
@@ -37,8 +40,8 @@ def _run_layer(rw, layer, x_d, wr_d, bias_d, cfg, T):
              y=torch.empty((R, H), dtype=torch.float32, device="cuda"),
              out=torch.empty((T, H), dtype=torch.float16, device="cuda"))
     c = ctx()
-    apw.route(c, x_d, wr_d, bias_d, T, H, E, k, cfg.renormalize, o["ids"], o["w"], o["counts"], o["offsets"],
-              o["perm"], o["inv_perm"])
+    apw.route(c, x_d, wr_d, bias_d, T, H, E, cfg.topk, cfg.renormalize, o["ids"], o["w"], o["counts"],
+              o["offsets"], o["perm"], o["inv_perm"], n_shared=cfg.shared)
     apw.gemm(c, rw.table, layer, apw.GATE_UP, x_d, True, o["perm"], o["offsets"], T, k, o["h"], apw.F16)
     apw.act(c, o["h"], R, F, o["a"])
     apw.gemm(c, rw.table, layer, apw.DOWN, o["a"], False, o["perm"], o["offsets"], T, k, o["y"], apw.F32)
@@ -48,26 +51,27 @@ def _run_layer(rw, layer, x_d, wr_d, bias_d, cfg, T):
 
 def _upload_layer_gpu(rw, cfg, gen_layer, slot, q):
     """Blocks generated on the device (bit-identical to synth.gen), tiled, LUT levels built."""
-    for e in range(cfg.experts):
+    for e in range(cfg.weight_experts):
         for u in (0, 1):
             rw.add_block(slot, e, u, synth.gpu.planes(cfg, gen_layer, e, u), synth.gpu.parent_lut(cfg, gen_layer, e, u),
                          int(q[e, u]))
 
 
 def _oracle_layer(cfg, layer, q, eval_tokens):
-    E = cfg.experts
+    E = cfg.weight_experts
     x, wr, bias = synth.gen_x(cfg, layer), synth.gen_router(cfg, layer), synth.gen_bias(cfg, layer)
     pg = [synth.gen_planes(cfg, layer, e, 0) for e in range(E)]
     pd = [synth.gen_planes(cfg, layer, e, 1) for e in range(E)]
     lg = [synth.gen_parent_lut(cfg, layer, e, 0) for e in range(E)]
     ld = [synth.gen_parent_lut(cfg, layer, e, 1) for e in range(E)]
-    r = oracle.moe_forward(x, wr, bias, cfg.topk, pg, lg, q[:, 0], pd, ld, q[:, 1], eval_tokens=eval_tokens)
+    r = oracle.moe_forward(x, wr, bias, cfg.topk, pg, lg, q[:, 0], pd, ld, q[:, 1], eval_tokens=eval_tokens,
+                           renormalize=cfg.renormalize, n_shared=cfg.shared)
     return r, x, wr, bias
 
 
 def _single_layer_case(cfg, eval_tokens):
     q = synth.gen_qmap(cfg)
-    rw = ResidentWeights(ctx(), 1, cfg.experts)
+    rw = ResidentWeights(ctx(), 1, cfg.weight_experts)
     _upload_layer_gpu(rw, cfg, 0, 0, q)
     rw.commit()
     x, wr, bias = synth.gen_x(cfg), synth.gen_router(cfg), synth.gen_bias(cfg)
@@ -126,3 +130,15 @@ def test_32_layers_resident_with_map_switch():
             ma, rl = check_out(host(outs[layer]["out"])[ev], r["out"])
             print(f"layer {layer} mean q {q.mean():.2f}: max-abs {ma:.3e} rel-L2 {rl:.3e}", flush=True)
     rw.close()
+
+
+@pytest.mark.parametrize("name,tokens", [("qwen_60r4s_top4_decode_t64", [0, 31, 63]),
+                                         ("gemma_128r1s_top8_decode_t64", [0, 40, 63]),
+                                         ("qwen_60r4s_top4_prefill_t2048", [0, 1000, 2047])])
+def test_shared_expert_workloads(name, tokens):
+    cfg = synth.config_by_name(name)
+    r, q = _single_layer_case(cfg, tokens)
+    T, k, E = cfg.tokens, cfg.topk, cfg.experts
+    # every token's row ends with the shared experts at weight 1; each holds all T rows
+    assert np.array_equal(r["ids"][:, k:], np.tile(np.arange(E, E + cfg.shared, dtype=np.int32), (T, 1)))
+    assert np.all(r["counts"][E:] == T)

@@ -100,6 +100,69 @@ def test_route_stats_accumulate(case):
     assert np.array_equal(host(sel), cnt)
 
 
+SHARED_ROUTE_CASES = [
+    # T, H, E routed, k, shared, bias, renormalize, seed
+    (37, 256, 12, 3, 2, False, True, 11),
+    (64, 512, 60, 4, 4, True, False, 12),
+    (5, 256, 128, 8, 1, False, True, 13),
+    (16, 256, 248, 8, 8, False, True, 14),  # E + shared = 256 experts, the most shared experts
+    (0, 256, 8, 2, 3, False, True, 15),
+    (9, 256, 4, 4, 2, False, False, 16),  # every routed expert chosen
+]
+
+
+@pytest.mark.parametrize("case", SHARED_ROUTE_CASES, ids=lambda c: f"T{c[0]}E{c[2]}k{c[3]}s{c[4]}")
+def test_route_shared_parity(case):
+    """Shared experts: each token's row is its top-k routed experts, then the shared
+    ones at weight 1; the sort groups all E + shared experts."""
+    T, H, E, k, S, use_bias, renorm, seed = case
+    x = synth.fp16_normal(200 + seed, 1, T * H, 1.0).reshape(T, H)
+    wr = synth.fp16_normal(200 + seed, 2, E * H, 0.02).reshape(E, H)
+    bias = synth.fp16_normal(200 + seed, 3, E, 1.0).astype(np.float32) if use_bias else None
+    if T > 0:
+        assert topk_margin_ok(x, wr, bias, k)
+    r = oracle.route(x, wr, bias, k, renorm, n_shared=S)
+    kt, R = k + S, T * (k + S)
+    o = dict(ids=torch.empty((T, kt), dtype=torch.int32, device="cuda"),
+             w=torch.empty((T, kt), dtype=torch.float32, device="cuda"),
+             counts=torch.full((E + S,), -1, dtype=torch.int32, device="cuda"),
+             offsets=torch.full((E + S + 1,), -1, dtype=torch.int32, device="cuda"),
+             perm=torch.empty(max(R, 1), dtype=torch.int32, device="cuda"),
+             inv_perm=torch.empty(max(R, 1), dtype=torch.int32, device="cuda"))
+    xd = dev(x) if T > 0 else torch.empty((1, H), dtype=torch.float16, device="cuda")
+    apw.route(ctx(), xd, dev(wr), None if bias is None else dev(bias), T, H, E, k, renorm, o["ids"], o["w"],
+              o["counts"], o["offsets"], o["perm"], o["inv_perm"], n_shared=S)
+    torch.cuda.synchronize()
+    o["perm"], o["inv_perm"] = o["perm"][:R], o["inv_perm"][:R]
+    check_route(o, r)
+    assert np.all(host(o["counts"])[E:] == T)
+    if T == 0:
+        return
+    # Eq. 1 statistics over the routed choices only: routed E, row stride k + shared
+    mass = torch.zeros(E, dtype=torch.float64, device="cuda")
+    total = torch.zeros(1, dtype=torch.float64, device="cuda")
+    sel = torch.zeros(E, dtype=torch.int64, device="cuda")
+    apw.route_stats(ctx(), o["w"], o["perm"], o["offsets"], T, kt, E, mass, total, sel)
+    torch.cuda.synchronize()
+    num, cnt, den = oracle.route_stats(r["ids"][:, :k], r["w32"][:, :k], E)
+    assert np.array_equal(host(sel), cnt)
+    bound = R * 2.0 ** -52 * den + 1e-300
+    assert np.all(np.abs(host(mass) - num) <= bound)
+    assert abs(float(host(total)[0]) - den) <= bound
+
+
+def test_route_shared_rejected():
+    H, E = 256, 250
+    x = dev(synth.fp16_normal(7, 1, 4 * H, 1.0).reshape(4, H))
+    wr = dev(synth.fp16_normal(7, 2, E * H, 0.02).reshape(E, H))
+    buf = torch.empty(4096, dtype=torch.int32, device="cuda")
+    wbuf = torch.empty(4096, dtype=torch.float32, device="cuda")
+    for S in (-1, 7, 9):  # 7: E + S above 256 experts; 9: above the shared-expert limit
+        with pytest.raises(apw.ApmoeError) as ex:
+            apw.route(ctx(), x, wr, None, 4, H, E, 2, True, buf, wbuf, buf, buf, buf, buf, n_shared=S)
+        assert ex.value.status == apw.INVALID_ARG
+
+
 def test_route_ties_lower_index():
     T, H, E, k = 40, 256, 8, 2
     x = synth.fp16_normal(9, 1, T * H, 1.0).reshape(T, H)
@@ -381,6 +444,29 @@ def test_layer_tiny_parity():
         acc = H * 2.0 ** -24 * S
         tol = 0.5 * ulp16(np.abs(r["h"][s:t]) + acc) + acc
         assert np.all(np.abs(h[s:t] - r["h"][s:t]) <= tol), e
+
+
+TINY_SHARED = synth.MoEConfig("tiny_shared", tokens=48, hidden=256, ffn=384, experts=12, topk=3, seed=21,
+                              shared=2, note="12 routed + 2 shared experts, top-3")
+
+
+@pytest.mark.parametrize("T,renorm", [(48, True), (48, False), (7, True), (150, False)])
+def test_layer_shared_experts(T, renorm):
+    """Shared experts run every token (T rows each: the tile product once T > 32,
+    the decode product below); routed ones get few rows.  Step-by-step calls and
+    the one-call layer agree bit for bit, both within the bar of the oracle."""
+    import dataclasses
+    cfg = dataclasses.replace(TINY_SHARED, renormalize=renorm)
+    L = Layer(cfg, T=T)
+    assert topk_margin_ok(L.x, L.wr, L.bias, cfg.topk)
+    o = L.run()
+    fused = L.run_fused_call()
+    torch.cuda.synchronize()
+    r = L.oracle()
+    check_route(o, r)
+    assert np.all(r["counts"][cfg.experts:] == T)
+    check_out(host(o["out"]), r["out"])
+    assert np.array_equal(host(fused).view(np.uint16), host(o["out"]).view(np.uint16))
 
 
 @pytest.mark.parametrize("T", [1, 5, 13])

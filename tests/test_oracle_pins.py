@@ -376,3 +376,29 @@ def test_uniform_q_is_apl_style_baseline():
         r = oracle.moe_forward(x, wr, None, cfg.topk, pg, lg, q[:, 0], pd, ld, q[:, 1])
         ref = _brute_layer(x, wr, cfg.topk, pg, pd, lg, ld, q)
         assert np.allclose(r["out"], ref, rtol=1e-10, atol=1e-13)
+
+
+def test_shared_experts_add_their_ffn():
+    """Shared experts (the "+4" / "+1" experts of Table 1): every token visits
+    them with weight 1 after its routed top-k, so the layer equals the routed-only
+    layer plus each shared expert's FFN of x, computed here from the block product
+    and the activation directly."""
+    T, H, F, E, k, S = 6, 64, 64, 4, 2, 2
+    cfg, x, wr, pg, pd, lg, ld, q = _tiny_layer(T=T, H=H, F=F, E=E + S, k=k, seed=37)
+    wr_routed = wr[:E]
+    with_shared = oracle.moe_forward(x, wr_routed, None, k, pg, lg, q[:, 0], pd, ld, q[:, 1], n_shared=S)
+    routed = oracle.moe_forward(x, wr_routed, None, k, pg[:E], lg[:E], q[:E, 0], pd[:E], ld[:E], q[:E, 1])
+    ref = routed["out"].copy()
+    xin = x.astype(np.float64)
+    for s_ in range(S):
+        e = E + s_
+        h = oracle.block_gemm(pg[e], oracle.lut_level(lg[e], int(q[e, 0])), int(q[e, 0]), xin)
+        a = oracle.act(h)
+        ref += oracle.block_gemm(pd[e], oracle.lut_level(ld[e], int(q[e, 1])), int(q[e, 1]), a)
+    assert np.allclose(with_shared["out"], ref, rtol=1e-12, atol=1e-12)
+    # routing: the shared experts follow the routed ones in every row, weight 1
+    assert np.array_equal(with_shared["ids"][:, :k], routed["ids"])
+    assert np.all(with_shared["ids"][:, k:] == np.arange(E, E + S))
+    assert np.all(with_shared["w64"][:, k:] == 1.0)
+    assert with_shared["counts"][E:].tolist() == [T] * S
+
