@@ -19,12 +19,15 @@
 // to MFMA k-slots is free as long as A and B agree.  Plane words of the next step
 // and B fragments of the next word are requested ahead of use.
 //
-// LDS LUT layout (bank-conflict-free gathers): the transposed code byte v has
-// bit p = plane p's bit, i.e. v is the q-bit code with its bits reversed; entry
-// LUT_q[n][code] is stored at v*256 + 4*(32*g + i) + 2*t for q <= 7, where i is
-// the row within the 32-row tile t and g the lane half (two copies, so the 64
-// lanes of a wave read 64 distinct banks).  For q = 8 one copy at v*128 + 4*i +
-// 2*t keeps the region at 32 KB.
+// LDS LUT layout: the transposed code byte v has bit p = plane p's bit, i.e. v is
+// the q-bit code with its bits reversed; entry LUT_q[n][code] is stored at
+// v*256 + 4*(32*g + i) + 2*t for q <= 7, where i is the row within the 32-row tile
+// t and g the lane half.  The 256-byte stride lets one v_perm place v above the
+// lane's constant byte to form the address; the second copy fills the rest of
+// each 256-byte row.  Gathers are conflict-free: the LDS serves a wave in two
+// halves of 32 lanes (lanes 0-31, 32-63), and within a half the 32 rows i fall in
+// 32 distinct banks.  For q = 8 one copy at v*128 + 4*i + 2*t keeps the region at
+// 32 KB (two instructions per address).
 #include "internal.h"
 
 namespace apmoe {
@@ -165,6 +168,72 @@ __device__ inline void group_product(const u32x2 (&w)[Q], const u32x4 (&xg)[4], 
     }
 }
 
+// LUT level Q of rows n0 .. n0+63 into LDS (layouts in the file header; q = 3 as the
+// pair table).  first_loads() runs once the LUT requests are out and before their data
+// is written, so the caller's first weight requests overlap the LUT's latency.
+template <int Q, typename F>
+__device__ __attribute__((always_inline)) inline void stage_lut(const __amdgpu_buffer_rsrc_t rl, int n0, int N,
+                                                                int tid, char *smem, F &&first_loads)
+{
+    if constexpr (Q == 3) {
+        // pair table of LUT_3: entry (row 32t+i, pair code v) at v*256 + 128t + 4i;
+        // thread -> row tid % 64, pair codes 16(tid/64) .. +15
+        const int nl = tid % kRows, part = tid / kRows;
+        const u32x4 lv = n0 + nl < N ? __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                               rl, (int)(((uint32_t)(n0 + nl) << 3) * 2u), 0, 0))
+                                     : u32x4{0, 0, 0, 0};
+        first_loads();
+        const uint32_t slot = (uint32_t)(128 * (nl >> 5) + 4 * (nl & 31));
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk) {
+            const uint32_t v = (uint32_t)(16 * part + kk);
+            const uint32_t ce = bitrev(v & 7u, 3), co = bitrev(v >> 3, 3);  // codes of the even / odd column
+            const uint32_t lo = (lv[ce >> 1] >> (16 * (ce & 1))) & 0xFFFFu;
+            const uint32_t hi = (lv[co >> 1] >> (16 * (co & 1))) & 0xFFFFu;
+            *reinterpret_cast<uint32_t *>(smem + v * 256 + slot) = lo | (hi << 16);
+        }
+    } else {
+        // 16-byte loads (8 entries of one row), lane -> row so that one wave touches 64 rows
+        constexpr int kLutU4 = (kRows << Q) / 8;
+        constexpr int kPer = (kLutU4 + kThreads - 1) / kThreads;
+        constexpr int kBatch = kPer < 4 ? kPer : 4;  // loads in flight per batch (register budget)
+#pragma unroll
+        for (int j0 = 0; j0 < kPer; j0 += kBatch) {
+            u32x4 lv[kBatch];
+#pragma unroll
+            for (int jj = 0; jj < kBatch; ++jj) {
+                const int idx = tid + (j0 + jj) * kThreads;
+                const int nl = idx % kRows, ch = idx / kRows;
+                const bool ok = idx < kLutU4 && n0 + nl < N;
+                lv[jj] = ok ? __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                  rl, (int)((((uint32_t)(n0 + nl) << Q) + 8u * ch) * 2u), 0, 0))
+                            : u32x4{0, 0, 0, 0};
+            }
+            if (j0 == 0)
+                first_loads();
+#pragma unroll
+            for (int jj = 0; jj < kBatch; ++jj) {
+                const int idx = tid + (j0 + jj) * kThreads;
+                if (idx >= kLutU4)
+                    break;
+                const int nl = idx % kRows, ch = idx / kRows;
+                const int il = nl & 31, tl = nl >> 5;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint16_t v = (uint16_t)(lv[jj][e >> 1] >> (16 * (e & 1)));
+                    const uint32_t vp = bitrev((uint32_t)(8 * ch + e), Q);
+                    if (Q < 8) {
+                        *reinterpret_cast<uint16_t *>(smem + vp * 256 + 4 * il + 2 * tl) = v;
+                        *reinterpret_cast<uint16_t *>(smem + vp * 256 + 4 * (32 + il) + 2 * tl) = v;
+                    } else {
+                        *reinterpret_cast<uint16_t *>(smem + vp * 128 + 4 * il + 2 * tl) = v;
+                    }
+                }
+            }
+        }
+    }
+}
+
 template <int Q>
 __device__ void gemm_block(const GemmParams &P, const DevBlock &blk, int rb, int r0, int Me, char *smem)
 {
@@ -195,67 +264,10 @@ __device__ void gemm_block(const GemmParams &P, const DevBlock &blk, int rb, int
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(P.in, P.in_bytes);
 
     u32x2 wc[Q];
-    if constexpr (Q == 3) {
-        // ---- pair table of LUT_3 for rows n0..n0+63: entry (row 32t+i, pair code v)
-        //      at v*256 + 128t + 4i; thread -> row tid % 64, pair codes 16(tid/64) .. +15
-        const int nl = tid % kRows, part = tid / kRows;
-        const u32x4 lv = n0 + nl < N ? __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                               rl, (int)(((uint32_t)(n0 + nl) << 3) * 2u), 0, 0))
-                                     : u32x4{0, 0, 0, 0};
+    stage_lut<Q>(rl, n0, N, tid, smem, [&] {
         if (has_steps)
             load_planes<Q>(wc, rs, lane_word);
-        const uint32_t slot = (uint32_t)(128 * (nl >> 5) + 4 * (nl & 31));
-#pragma unroll
-        for (int kk = 0; kk < 16; ++kk) {
-            const uint32_t v = (uint32_t)(16 * part + kk);
-            const uint32_t ce = bitrev(v & 7u, 3), co = bitrev(v >> 3, 3);  // codes of the even / odd column
-            const uint32_t lo = (lv[ce >> 1] >> (16 * (ce & 1))) & 0xFFFFu;
-            const uint32_t hi = (lv[co >> 1] >> (16 * (co & 1))) & 0xFFFFu;
-            *reinterpret_cast<uint32_t *>(smem + v * 256 + slot) = lo | (hi << 16);
-        }
-    } else {
-        // ---- LUT level Q of rows n0..n0+63: 16-byte loads (8 entries of one row),
-        //      lane -> row so that one wave touches 64 rows ----------------------------
-        constexpr int kLutU4 = (kRows << Q) / 8;
-        constexpr int kPer = (kLutU4 + kThreads - 1) / kThreads;
-        constexpr int kBatch = kPer < 4 ? kPer : 4;  // loads in flight per batch (register budget)
-#pragma unroll
-        for (int j0 = 0; j0 < kPer; j0 += kBatch) {
-            u32x4 lv[kBatch];
-#pragma unroll
-            for (int jj = 0; jj < kBatch; ++jj) {
-                const int idx = tid + (j0 + jj) * kThreads;
-                const int nl = idx % kRows, ch = idx / kRows;
-                const bool ok = idx < kLutU4 && n0 + nl < N;
-                lv[jj] = ok ? __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                  rl, (int)((((uint32_t)(n0 + nl) << Q) + 8u * ch) * 2u), 0, 0))
-                            : u32x4{0, 0, 0, 0};
-            }
-            // first step's planes are requested before the LUT lands in LDS
-            if (j0 == 0 && has_steps)
-                load_planes<Q>(wc, rs, lane_word);
-#pragma unroll
-            for (int jj = 0; jj < kBatch; ++jj) {
-                const int idx = tid + (j0 + jj) * kThreads;
-                if (idx >= kLutU4)
-                    break;
-                const int nl = idx % kRows, ch = idx / kRows;
-                const int il = nl & 31, tl = nl >> 5;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const uint16_t v = (uint16_t)(lv[jj][e >> 1] >> (16 * (e & 1)));
-                    const uint32_t vp = bitrev((uint32_t)(8 * ch + e), Q);
-                    if (Q < 8) {
-                        *reinterpret_cast<uint16_t *>(smem + vp * 256 + 4 * il + 2 * tl) = v;
-                        *reinterpret_cast<uint16_t *>(smem + vp * 256 + 4 * (32 + il) + 2 * tl) = v;
-                    } else {
-                        *reinterpret_cast<uint16_t *>(smem + vp * 128 + 4 * il + 2 * tl) = v;
-                    }
-                }
-            }
-        }
-
-    }
+    });
     __syncthreads();
 
     // LDS byte address of the region (a compile-time constant for the static array)
@@ -268,10 +280,12 @@ __device__ void gemm_block(const GemmParams &P, const DevBlock &blk, int rb, int
     for (int tp = 0; tp < Me; tp += kTokTile) {
         const int j = lane & 31;  // token of this lane in the B operand
         const bool tok_ok = tp + j < Me;
-        // lanes past the last token read the last token's row: their D columns are discarded
+        // lanes past the last token keep a valid row index; their D columns are discarded
         const int r = r0 + min(tp + j, Me - 1);
         const int src = P.gather ? P.perm[r] / P.topk : r;
-        uint32_t xoff = ((uint32_t)src * (uint32_t)K + (uint32_t)(half * kStepCols + 64 * g)) * 2u;  // bytes
+        // lanes past the last token request an offset beyond the buffer: zeros, no cache traffic
+        uint32_t xoff = tok_ok ? ((uint32_t)src * (uint32_t)K + (uint32_t)(half * kStepCols + 64 * g)) * 2u  // bytes
+                               : 0x80000000u;
         if (tp > 0 && has_steps)
             load_planes<Q>(wc, rs, lane_word);
         float16v acc;
