@@ -26,7 +26,7 @@ EXPORTED = [
     "apmoe_block_bytes", "apmoe_table_create", "apmoe_table_destroy", "apmoe_table_set_block",
     "apmoe_table_set_bits", "apmoe_table_set_plane", "apmoe_table_validate", "apmoe_table_committed_bits",
     "apmoe_table_commit", "apmoe_lut_build", "apmoe_tiled_plane_words", "apmoe_tile_planes", "apmoe_pack_planes", "apmoe_route", "apmoe_route_stats", "apmoe_gemm",
-    "apmoe_act",
+    "apmoe_gemm_act", "apmoe_act",
     "apmoe_combine", "apmoe_moe_workspace", "apmoe_moe_forward", "apmoe_page_out", "apmoe_page_in",
 ]
 
@@ -93,6 +93,7 @@ def _declare(L):
         "apmoe_route": (S, [P, P, P, P, I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, P]),
         "apmoe_route_stats": (S, [P, P, P, P, I32, I32, I32, P, P, P, P]),
         "apmoe_gemm": (S, [P, P, I32, I32, P, I32, P, P, I32, I32, P, I32, P]),
+        "apmoe_gemm_act": (S, [P, P, I32, P, I32, P, P, I32, I32, P, P]),
         "apmoe_act": (S, [P, P, I32, I32, P, P]),
         "apmoe_combine": (S, [P, P, I32, P, P, I32, I32, I32, P, P]),
         "apmoe_moe_workspace": (S, [P, I32, I32, I32, I32, ctypes.POINTER(SZ)]),
@@ -259,6 +260,13 @@ def gemm(ctx: Context, table: Table, layer: int, kind: int, inp, gather: bool, p
          out, out_dtype: int, stream=None) -> None:
     _check(lib().apmoe_gemm(ctx.handle, table.handle, layer, kind, ptr(inp), int(gather), ptr(perm), ptr(offsets),
                             T, topk, ptr(out), out_dtype, stream_handle(stream)), "apmoe_gemm")
+
+
+def gemm_act(ctx: Context, table: Table, layer: int, x, gather: bool, perm, offsets, T: int, topk: int, a,
+             stream=None) -> None:
+    """gate_up product with SiLU(gate) * up in its epilogue: fp16 a [T*topk][F]."""
+    _check(lib().apmoe_gemm_act(ctx.handle, table.handle, layer, ptr(x), int(gather), ptr(perm), ptr(offsets), T,
+                                topk, ptr(a), stream_handle(stream)), "apmoe_gemm_act")
 
 
 def act(ctx: Context, h, R: int, F: int, a, stream=None) -> None:

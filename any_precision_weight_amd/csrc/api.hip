@@ -693,9 +693,9 @@ static apmoe_status layer_shape(const apmoe_table *t, int layer, int kind, int *
     return ok();
 }
 
-apmoe_status apmoe_gemm(apmoe_ctx *ctx, const apmoe_table *tbl, int32_t layer, int32_t kind, const uint16_t *in,
-                        int32_t gather, const int32_t *perm, const int32_t *offsets, int32_t T, int32_t topk,
-                        void *out, int32_t out_dtype, void *stream)
+static apmoe_status gemm_common(apmoe_ctx *ctx, const apmoe_table *tbl, int32_t layer, int32_t kind,
+                                const uint16_t *in, int32_t gather, const int32_t *perm, const int32_t *offsets,
+                                int32_t T, int32_t topk, void *out, int32_t out_dtype, int act, void *stream)
 {
     apmoe_status s = check_ctx(ctx);
     if (s != APMOE_OK)
@@ -723,6 +723,8 @@ apmoe_status apmoe_gemm(apmoe_ctx *ctx, const apmoe_table *tbl, int32_t layer, i
     s = layer_shape(tbl, layer, kind, &N, &K, &max_q);
     if (s != APMOE_OK)
         return s;
+    if (act && (N % 128 != 0))
+        return fail(APMOE_INVALID_ARG, "gate_up has %d rows: the fused activation needs F = N/2 a multiple of 64", N);
     const size_t in_rows = gather ? (size_t)T : (size_t)T * topk;
     const size_t in_bytes = in_rows * (size_t)K * 2;
     const size_t plane_bytes = apmoe::tiled_plane_words(N, K) * 4;
@@ -731,8 +733,23 @@ apmoe_status apmoe_gemm(apmoe_ctx *ctx, const apmoe_table *tbl, int32_t layer, i
                     in_bytes, plane_bytes);
     const DevBlock *slice = tbl->d_table + tbl->index(layer, 0, 0);
     hipError_t e = apmoe::launch_gemm(slice, kind, tbl->E, N, K, max_q, in, in_bytes, gather, perm, offsets, topk,
-                                      T * topk, out, out_dtype == APMOE_F32, reinterpret_cast<hipStream_t>(stream));
+                                      T * topk, out, out_dtype == APMOE_F32, act,
+                                      reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? ok() : hip_fail(e, "gemm launch");
+}
+
+apmoe_status apmoe_gemm(apmoe_ctx *ctx, const apmoe_table *tbl, int32_t layer, int32_t kind, const uint16_t *in,
+                        int32_t gather, const int32_t *perm, const int32_t *offsets, int32_t T, int32_t topk,
+                        void *out, int32_t out_dtype, void *stream)
+{
+    return gemm_common(ctx, tbl, layer, kind, in, gather, perm, offsets, T, topk, out, out_dtype, 0, stream);
+}
+
+apmoe_status apmoe_gemm_act(apmoe_ctx *ctx, const apmoe_table *tbl, int32_t layer, const uint16_t *x,
+                            int32_t gather, const int32_t *perm, const int32_t *offsets, int32_t T, int32_t topk,
+                            uint16_t *a, void *stream)
+{
+    return gemm_common(ctx, tbl, layer, APMOE_GATE_UP, x, gather, perm, offsets, T, topk, a, APMOE_F16, 1, stream);
 }
 
 apmoe_status apmoe_act(apmoe_ctx *ctx, const uint16_t *h, int32_t R, int32_t F, uint16_t *a, void *stream)
@@ -771,7 +788,7 @@ apmoe_status apmoe_combine(apmoe_ctx *ctx, const void *y, int32_t y_dtype, const
 
 namespace {
 struct WsLayout {
-    size_t ids, w, counts, offsets, perm, inv_perm, h, a, y, total;
+    size_t ids, w, counts, offsets, perm, inv_perm, a, y, total;
 };
 
 size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -793,8 +810,6 @@ WsLayout ws_layout(int T, int topk, int E, int H, int F)
     o = up256(o + R * 4);
     L.inv_perm = o;
     o = up256(o + R * 4);
-    L.h = o;
-    o = up256(o + R * 2 * F * 2);
     L.a = o;
     o = up256(o + R * F * 2);
     L.y = o;
@@ -860,17 +875,14 @@ apmoe_status apmoe_moe_forward(apmoe_ctx *ctx, const apmoe_table *tbl, int32_t l
     int32_t *offsets = reinterpret_cast<int32_t *>(w + L.offsets);
     int32_t *perm = reinterpret_cast<int32_t *>(w + L.perm);
     int32_t *inv = reinterpret_cast<int32_t *>(w + L.inv_perm);
-    uint16_t *h = reinterpret_cast<uint16_t *>(w + L.h);
     uint16_t *a = reinterpret_cast<uint16_t *>(w + L.a);
     float *y = reinterpret_cast<float *>(w + L.y);
     s = apmoe_route(ctx, x, w_router, bias, T, H, tbl->E - n_shared, topk, n_shared, renormalize, ids, tw, counts,
                     offsets, perm, inv, stream);
     if (s != APMOE_OK || T == 0)
         return s;
-    s = apmoe_gemm(ctx, tbl, layer, APMOE_GATE_UP, x, 1, perm, offsets, T, kt, h, APMOE_F16, stream);
-    if (s != APMOE_OK)
-        return s;
-    s = apmoe_act(ctx, h, T * kt, F, a, stream);
+    // gate_up with SiLU(gate) * up in its epilogue (F = K of down is a multiple of 128)
+    s = apmoe_gemm_act(ctx, tbl, layer, x, 1, perm, offsets, T, kt, a, stream);
     if (s != APMOE_OK)
         return s;
     s = apmoe_gemm(ctx, tbl, layer, APMOE_DOWN, a, 0, perm, offsets, T, kt, y, APMOE_F32, stream);

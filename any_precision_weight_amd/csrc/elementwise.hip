@@ -22,8 +22,7 @@ __global__ void __launch_bounds__(256) act_kernel(const uint16_t *__restrict__ h
     half8 o;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const float z = (float)g[i];
-        o[i] = (_Float16)(z / (1.0f + __expf(-z)) * (float)u[i]);
+        o[i] = silu_mul(g[i], u[i]);
     }
     *reinterpret_cast<uint4 *>(a + r * F + f) = __builtin_bit_cast(uint4, o);
 }

@@ -88,6 +88,7 @@ struct GemmParams {
     const int32_t *offsets;
     void *out;
     int kind, E, N, K, topk, gather, out_f32, row_blocks;
+    int act;               // gate_up with the activation fused: out = a [rows][N/2] fp16
     int max_rows;          // experts with more rows belong to the tile product
     uint32_t in_bytes;     // bytes of `in` (buffer range of the B-operand loads)
     uint32_t plane_bytes;  // bytes of one tiled plane
@@ -168,20 +169,22 @@ __device__ inline void group_product(const u32x2 (&w)[Q], const u32x4 (&xg)[4], 
     }
 }
 
-// LUT level Q of rows n0 .. n0+63 into LDS (layouts in the file header; q = 3 as the
-// pair table).  first_loads() runs once the LUT requests are out and before their data
-// is written, so the caller's first weight requests overlap the LUT's latency.
+// LUT level Q of the block's two 32-row tiles (first rows nA, nB) into LDS (layouts
+// in the file header; q = 3 as the pair table).  first_loads() runs once the LUT
+// requests are out and before their data is written, so the caller's first weight
+// requests overlap the LUT's latency.
 template <int Q, typename F>
-__device__ __attribute__((always_inline)) inline void stage_lut(const __amdgpu_buffer_rsrc_t rl, int n0, int N,
-                                                                int tid, char *smem, F &&first_loads)
+__device__ __attribute__((always_inline)) inline void stage_lut(const __amdgpu_buffer_rsrc_t rl, int nA, int nB,
+                                                                int N, int tid, char *smem, F &&first_loads)
 {
     if constexpr (Q == 3) {
         // pair table of LUT_3: entry (row 32t+i, pair code v) at v*256 + 128t + 4i;
         // thread -> row tid % 64, pair codes 16(tid/64) .. +15
         const int nl = tid % kRows, part = tid / kRows;
-        const u32x4 lv = n0 + nl < N ? __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                               rl, (int)(((uint32_t)(n0 + nl) << 3) * 2u), 0, 0))
-                                     : u32x4{0, 0, 0, 0};
+        const int n = (nl < 32 ? nA : nB) + (nl & 31);
+        const u32x4 lv = n < N ? __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                         rl, (int)(((uint32_t)n << 3) * 2u), 0, 0))
+                               : u32x4{0, 0, 0, 0};
         first_loads();
         const uint32_t slot = (uint32_t)(128 * (nl >> 5) + 4 * (nl & 31));
 #pragma unroll
@@ -204,9 +207,10 @@ __device__ __attribute__((always_inline)) inline void stage_lut(const __amdgpu_b
             for (int jj = 0; jj < kBatch; ++jj) {
                 const int idx = tid + (j0 + jj) * kThreads;
                 const int nl = idx % kRows, ch = idx / kRows;
-                const bool ok = idx < kLutU4 && n0 + nl < N;
+                const int n = (nl < 32 ? nA : nB) + (nl & 31);
+                const bool ok = idx < kLutU4 && n < N;
                 lv[jj] = ok ? __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                  rl, (int)((((uint32_t)(n0 + nl) << Q) + 8u * ch) * 2u), 0, 0))
+                                  rl, (int)((((uint32_t)n << Q) + 8u * ch) * 2u), 0, 0))
                             : u32x4{0, 0, 0, 0};
             }
             if (j0 == 0)
@@ -243,17 +247,19 @@ __device__ void gemm_block(const GemmParams &P, const DevBlock &blk, int rb, int
     const int t = wave & 1, half = wave >> 1;
     const int i = lane & 31, g = lane >> 5;
     const int N = P.N, K = P.K;
-    const int n0 = rb * kRows;
+    // first rows of the block's two 32-row tiles: consecutive, or with the activation
+    // fused, gate rows 32rb.. and the matching up rows F + 32rb..
+    const int nA = P.act ? 32 * rb : rb * kRows;
+    const int nB = P.act ? (N >> 1) + 32 * rb : rb * kRows + 32;
+    const int nt = t ? nB : nA;  // this wave's tile
     const int nsteps = K / kStepCols;  // K % 128 == 0
     // half 1 has no step when K == 128: it must not touch planes or token rows at all
     const bool has_steps = half < nsteps;
-    const int n_row = n0 + 32 * t + i;
-    const bool row_ok = n_row < N;
     // tiled planes: tile (rt, kt) = rows 32rt.., columns 128kt.., 128 words; this lane
     // reads words 2*lane, 2*lane+1 of each tile.  A row tile past the end (N % 64 in
     // (0, 32]) reads tile row 0; its outputs are not written.
     const int RT = (N + 31) / 32, KT = K / kStepCols;
-    const int rt = 2 * rb + t;
+    const int rt = nt / 32;
     const uint32_t lane_word = ((uint32_t)(rt < RT ? rt : 0) * (uint32_t)KT + (uint32_t)half) * 128u + 2u * lane;
     constexpr uint32_t kNextWords = 2 * 128;  // this wave's next step: two tiles on
     __amdgpu_buffer_rsrc_t rs[Q];
@@ -264,7 +270,7 @@ __device__ void gemm_block(const GemmParams &P, const DevBlock &blk, int rb, int
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(P.in, P.in_bytes);
 
     u32x2 wc[Q];
-    stage_lut<Q>(rl, n0, N, tid, smem, [&] {
+    stage_lut<Q>(rl, nA, nB, N, tid, smem, [&] {
         if (has_steps)
             load_planes<Q>(wc, rs, lane_word);
     });
@@ -335,19 +341,44 @@ __device__ void gemm_block(const GemmParams &P, const DevBlock &blk, int rb, int
 #pragma unroll
             for (int v = 0; v < 16; ++v)
                 acc[v] += red[(t * 16 + v) * kWave + lane];
-            if (tok_ok) {
-                const size_t orow = (size_t)(r0 + tp + j) * N;
+        }
+        // D layout of the 32x32 MFMA: column j = lane%32, row = 8*(v/4) + 4*(lane/32) + v%4
+        if (!P.act) {
+            if (half == 0 && tok_ok) {
+                // rows nt + 4g + 8(v/4) + v%4 of token row r0 + tp + j: one base, constant offsets
+                const size_t o0 = (size_t)(r0 + tp + j) * N + (size_t)(nt + 4 * g);
+                const int nleft = N - (nt + 4 * g);
+                float *of = reinterpret_cast<float *>(P.out) + o0;
+                _Float16 *oh = reinterpret_cast<_Float16 *>(P.out) + o0;
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
-                    // D layout of the 32x32 MFMA: column j = lane%32, row = 8*(v/4) + 4*(lane/32) + v%4
-                    const int row = 8 * (v >> 2) + 4 * g + (v & 3);
-                    const int n = n0 + 32 * t + row;
-                    if (n < N) {
+                    const int d = 8 * (v >> 2) + (v & 3);
+                    if (d < nleft) {
                         if (P.out_f32)
-                            reinterpret_cast<float *>(P.out)[orow + n] = acc[v];
+                            of[d] = acc[v];
                         else
-                            reinterpret_cast<_Float16 *>(P.out)[orow + n] = (_Float16)acc[v];
+                            oh[d] = (_Float16)acc[v];
                     }
+                }
+            }
+        } else {
+            // the up wave hands its fp16-rounded rows to the gate wave of the same lanes
+            // through its own reduction slots (already read by it; only it touches them);
+            // the gate wave writes a = SiLU(gate) * up
+            if (half == 0 && t == 1) {
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    red[(16 + v) * kWave + lane] = (float)(_Float16)acc[v];
+            }
+            __syncthreads();
+            if (half == 0 && t == 0 && tok_ok) {
+                // rows f = nA + 4g + 8(v/4) + v%4 < F of token row r0 + tp + j
+                _Float16 *oa = reinterpret_cast<_Float16 *>(P.out) + (size_t)(r0 + tp + j) * (size_t)(N >> 1) +
+                               (size_t)(nA + 4 * g);
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const _Float16 up = (_Float16)red[(16 + v) * kWave + lane];
+                    oa[8 * (v >> 2) + (v & 3)] = silu_mul((_Float16)acc[v], up);
                 }
             }
         }
@@ -382,7 +413,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
 
 hipError_t launch_gemm(const DevBlock *table, int kind, int E, int N, int K, int max_q, const uint16_t *in,
                        size_t in_bytes, int gather, const int32_t *perm, const int32_t *offsets, int topk, int R,
-                       void *out, int out_f32, hipStream_t s)
+                       void *out, int out_f32, int act, hipStream_t s)
 {
     (void)max_q;
     GemmParams P;
@@ -398,7 +429,9 @@ hipError_t launch_gemm(const DevBlock *table, int kind, int E, int N, int K, int
     P.topk = topk;
     P.gather = gather;
     P.out_f32 = out_f32;
-    P.row_blocks = (N + kRows - 1) / kRows;
+    P.act = act;
+    // with the activation fused a block covers 32 gate rows and the matching 32 up rows
+    P.row_blocks = act ? (N / 2) / 32 : (N + kRows - 1) / kRows;
     P.in_bytes = (uint32_t)in_bytes;
     P.plane_bytes = (uint32_t)(tiled_plane_words(N, K) * 4);
     P.max_rows = kDecodeMaxRows;
@@ -409,7 +442,7 @@ hipError_t launch_gemm(const DevBlock *table, int kind, int E, int N, int K, int
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || R <= kDecodeMaxRows)
         return err;  // no expert can have more rows than the decode product takes
-    return launch_gemm_tile(table, kind, E, N, K, in, in_bytes, gather, perm, offsets, topk, out, out_f32, R, s);
+    return launch_gemm_tile(table, kind, E, N, K, in, in_bytes, gather, perm, offsets, topk, out, out_f32, act, R, s);
 }
 
 }  // namespace apmoe

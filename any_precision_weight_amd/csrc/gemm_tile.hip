@@ -112,6 +112,7 @@ struct TileParams {
     const int32_t *offsets;
     void *out;
     int kind, E, N, K, topk, gather, out_f32, NT, min_rows;
+    int act;               // gate_up with the activation fused: out = a [rows][N/2] fp16
     uint32_t in_bytes;     // bytes of `in`
     uint32_t plane_bytes;  // bytes of one tiled plane
 };
@@ -332,6 +333,10 @@ __device__ __attribute__((always_inline)) void tile_block(const TileParams &P, c
     const int KT2 = (KT + 1) & ~1;  // steps rounded up to even (the pipeline runs two per loop)
     const int nst = 2 * KT;         // token stages (one per plane word)
     const uint32_t base = lds_addr(smem);
+    // first rows of the tile's two 64-row halves: consecutive, or with the activation
+    // fused, gate rows 64nt.. and the matching up rows F + 64nt..
+    const int rowA0 = P.act ? (T.n0 >> 1) : T.n0;
+    const int rowB0 = P.act ? (N >> 1) + (T.n0 >> 1) : T.n0 + 64;
 
     // ---- LUT level Q of the tile's rows -> LDS (row pairs nl, nl+64 share a word;
     //      lane -> row pair, so the writes of a wave hit distinct banks) ----------------
@@ -345,7 +350,7 @@ __device__ __attribute__((always_inline)) void tile_block(const TileParams &P, c
             const int pc = tid + jj * kThreads;
             if (pc < kPairChunks) {
                 const int pr = pc % 64, ch = pc / 64;
-                const int na = T.n0 + pr, nb = T.n0 + pr + 64;
+                const int na = rowA0 + pr, nb = rowB0 + pr;
                 const u32x4 za = {0, 0, 0, 0};
                 const u32x4 la = na < N ? __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                                                      rl, (int)((((uint32_t)na << Q) + 8u * ch) * 2u), 0, 0))
@@ -367,7 +372,7 @@ __device__ __attribute__((always_inline)) void tile_block(const TileParams &P, c
     if (producer) {
         // ---------------------------------------------------------------- producer
         const int RT = (N + 31) / 32;
-        const int rt = T.n0 / 32 + pw;
+        const int rt = (pw < 2 ? rowA0 + 32 * pw : rowB0 + 32 * (pw - 2)) / 32;
         const uint32_t lane_word = (uint32_t)(rt < RT ? rt : 0) * (uint32_t)KT * 128u + 2u * lane;
         auto step_word = [&](int st) -> uint32_t { return lane_word + 128u * (uint32_t)(st < KT ? st : KT - 1); };
         __amdgpu_buffer_rsrc_t rs[Q];
@@ -442,6 +447,8 @@ __device__ __attribute__((always_inline)) void tile_block(const TileParams &P, c
             produce_a<Q, 0>(pa, lane_const, a_dst);
             phase_barrier<kWaitEven>();
         }
+        if (P.act)
+            __syncthreads();  // the consumers' activation exchange: every wave takes part
         return;
     }
 
@@ -485,12 +492,54 @@ __device__ __attribute__((always_inline)) void tile_block(const TileParams &P, c
             consume<TTN>(a_stage + kAStageBytes, a_lane, xsrc(n + 3), bo, acc);
         phase_barrier<0>();
     }
+    const int j = i;
+    if (P.act) {
+        // ---- activation fused: consumer c (odd, up rows) hands its fp16-rounded
+        //      accumulators to consumer c - 1 (even, the matching gate rows) through the
+        //      A buffers, idle after the last phase; the gate consumer writes
+        //      a = SiLU(gate) * up for rows f = rowA0 + 32h + 8(v/4) + 4g + v%4 ---------
+        _Float16 *xch = reinterpret_cast<_Float16 *>(smem + L::kA);
+        auto xi = [&](int h, int tt, int v) { return ((((c >> 1) * 2 + h) * TTN + tt) * 16 + v) * kWave + lane; };
+        if (active && (c & 1)) {
+#pragma unroll
+            for (int tt = 0; tt < TTN; ++tt)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v)
+                        xch[xi(h, tt, v)] = (_Float16)acc[h][tt][v];
+        }
+        __syncthreads();
+        if (active && !(c & 1)) {
+            const int F = N >> 1;
+#pragma unroll
+            for (int tt = 0; tt < TTN; ++tt) {
+                const int tok = 128 * (c >> 1) + 32 * tt + j;
+                if (tok < T.M) {
+                    const size_t orow = (size_t)(T.r0 + T.m0 + tok) * F;
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+                        for (int a4 = 0; a4 < 4; ++a4) {
+                            typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+                            half4 hv;
+#pragma unroll
+                            for (int b = 0; b < 4; ++b)
+                                hv[b] = silu_mul((_Float16)acc[h][tt][4 * a4 + b], xch[xi(h, tt, 4 * a4 + b)]);
+                            const int f = rowA0 + 32 * h + 8 * a4 + 4 * g;
+                            *reinterpret_cast<half4 *>(reinterpret_cast<_Float16 *>(P.out) + orow + f) = hv;
+                        }
+                    }
+                }
+            }
+        }
+        return;
+    }
     if (!active)
         return;
 
     // ---- write: acc[h][tt][v] is token 128(c/2) + 32tt + (lane % 32), weight row
     //      64(c%2) + 32h + 8(v/4) + 4g + v%4; four consecutive rows per store ----------
-    const int j = i;
 #pragma unroll
     for (int tt = 0; tt < TTN; ++tt) {
         const int tok = 128 * (c >> 1) + 32 * tt + j;
@@ -500,7 +549,7 @@ __device__ __attribute__((always_inline)) void tile_block(const TileParams &P, c
             for (int h = 0; h < 2; ++h) {
 #pragma unroll
                 for (int a4 = 0; a4 < 4; ++a4) {
-                    const int n = T.n0 + 64 * (c & 1) + 32 * h + 8 * a4 + 4 * g;
+                    const int n = (c & 1 ? rowB0 : rowA0) + 32 * h + 8 * a4 + 4 * g;
                     const float16v &A = acc[h][tt];
                     if (P.out_f32) {
                         float *o = reinterpret_cast<float *>(P.out) + orow + n;
@@ -581,7 +630,7 @@ int tile_grid(int N, int E, int R)
 
 hipError_t launch_gemm_tile(const DevBlock *table, int kind, int E, int N, int K, const uint16_t *in, size_t in_bytes,
                             int gather, const int32_t *perm, const int32_t *offsets, int topk, void *out, int out_f32,
-                            int R, hipStream_t s)
+                            int act, int R, hipStream_t s)
 {
     TileParams P;
     P.table = table;
@@ -596,7 +645,8 @@ hipError_t launch_gemm_tile(const DevBlock *table, int kind, int E, int N, int K
     P.topk = topk;
     P.gather = gather;
     P.out_f32 = out_f32;
-    P.NT = (N + kBN - 1) / kBN;
+    P.act = act;
+    P.NT = (N + kBN - 1) / kBN;  // with the activation fused: F / 64 tiles of 64 gate + 64 up rows
     P.min_rows = kDecodeMaxRows;
     P.in_bytes = (uint32_t)in_bytes;
     P.plane_bytes = (uint32_t)(tiled_plane_words(N, K) * 4);

@@ -25,6 +25,15 @@ constexpr int kGemmRowsPerBlock = 64;
 // Experts with at most this many rows use the decode product (one pass of 32 token
 // columns); larger ones use the MFMA tile product.
 constexpr int kDecodeMaxRows = 32;
+
+// Expert activation of one (gate, up) pair of fp16 values: SiLU(g) * u with
+// SiLU(z) = z / (1 + e^-z), fp32 math, fp16 result (RNE).  The activation launch
+// and the products' fused epilogue both call this, so the two give identical bits.
+__device__ __attribute__((always_inline)) inline _Float16 silu_mul(_Float16 g, _Float16 u)
+{
+    const float z = (float)g;
+    return (_Float16)(z / (1.0f + __expf(-z)) * (float)u);
+}
 // Token rows per tile of the MFMA tile product.
 constexpr int kTileTokens = 256;
 
@@ -42,12 +51,14 @@ hipError_t launch_route_stats(const float *w, const int32_t *perm, const int32_t
 // in_bytes: size of `in` (rows x K fp16); must be below 2^31.
 // R = T * topk rows in total; experts are split between the decode and the tile
 // product by their row count (read on the device).
+// act = 1 (gate_up only, F = N/2 a multiple of 64): the epilogue applies silu_mul to
+// the fp16-rounded gate row f and up row F + f and writes fp16 a[R][F] to out.
 hipError_t launch_gemm(const DevBlock *table, int kind, int E, int N, int K, int max_q, const uint16_t *in,
                        size_t in_bytes, int gather, const int32_t *perm, const int32_t *offsets, int topk, int R,
-                       void *out, int out_f32, hipStream_t s);
+                       void *out, int out_f32, int act, hipStream_t s);
 hipError_t launch_gemm_tile(const DevBlock *table, int kind, int E, int N, int K, const uint16_t *in, size_t in_bytes,
                             int gather, const int32_t *perm, const int32_t *offsets, int topk, void *out, int out_f32,
-                            int R, hipStream_t s);
+                            int act, int R, hipStream_t s);
 
 hipError_t launch_act(const uint16_t *h, int R, int F, uint16_t *a, hipStream_t s);
 hipError_t launch_combine(const void *y, int y_f32, const float *w, const int32_t *inv_perm, int T, int topk, int H,

@@ -61,7 +61,7 @@ def profiled_traffic(workload, sources):
 def algorithmic_bytes(cfg, counts, qmap, kind):
     """Bytes one product launch must move: the q needed planes and LUT level q of
     every active expert (Eq. 3 of the paper), the input rows it reads and the
-    output rows it writes."""
+    output rows it writes (gate_up writes the activation a, fp16 [rows][F])."""
     N, K = cfg.block_shape(kind)
     w = 0
     rows = 0
@@ -72,7 +72,7 @@ def algorithmic_bytes(cfg, counts, qmap, kind):
         w += N * q * K // 8 + N * (1 << q) * 2
         rows += int(c)
     in_bytes = rows * K * 2
-    out_bytes = rows * N * (2 if kind == 0 else 4)
+    out_bytes = rows * (N // 2) * 2 if kind == 0 else rows * N * 4
     return w + in_bytes + out_bytes, w
 
 
@@ -148,7 +148,7 @@ class BenchLayer:
         z = lambda shape, dt: torch.empty(shape, dtype=dt, device="cuda")
         self.b = dict(ids=z((T, k), torch.int32), w=z((T, k), torch.float32), counts=z(E, torch.int32),
                       offsets=z(E + 1, torch.int32), perm=z(R, torch.int32), inv=z(R, torch.int32),
-                      h=z((R, 2 * F), torch.float16), a=z((R, F), torch.float16), y=z((R, H), torch.float32),
+                      a=z((R, F), torch.float16), y=z((R, H), torch.float32),
                       out=z((T, H), torch.float16))
 
     def step(self, slot, ev=None):
@@ -158,11 +158,10 @@ class BenchLayer:
                   b["counts"], b["offsets"], b["perm"], b["inv"], n_shared=cfg.shared)
         if ev:
             ev[0].record()
-        apw.gemm(c, self.rw.table, slot, apw.GATE_UP, self.x_d, True, b["perm"], b["offsets"], T, k, b["h"], apw.F16)
+        # gate_up with SiLU(gate) * up in its epilogue: a [R][F] directly
+        apw.gemm_act(c, self.rw.table, slot, self.x_d, True, b["perm"], b["offsets"], T, k, b["a"])
         if ev:
             ev[1].record()
-        apw.act(c, b["h"], T * k, F, b["a"])
-        if ev:
             ev[2].record()
         apw.gemm(c, self.rw.table, slot, apw.DOWN, b["a"], False, b["perm"], b["offsets"], T, k, b["y"], apw.F32)
         if ev:

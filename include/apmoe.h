@@ -300,6 +300,21 @@ apmoe_status apmoe_gemm(apmoe_ctx *ctx, const apmoe_table *tbl, int32_t layer, i
  * h fp16 [R][2F], a fp16 [R][F], F % 8 == 0. */
 apmoe_status apmoe_act(apmoe_ctx *ctx, const uint16_t *h, int32_t R, int32_t F, uint16_t *a, void *stream);
 
+/*
+ * gate_up product with the expert activation in its epilogue (Section 3.3: the MoE
+ * kernel covers the expert computation, activation included, in its launches):
+ *   a[r][f] = SiLU(h16[r][f]) * h16[r][F + f],   h16 = fp16 (RNE) of the gate_up rows,
+ * in fp32, stored fp16 -- bit for bit what apmoe_gemm(APMOE_GATE_UP, .., APMOE_F16)
+ * followed by apmoe_act gives, without writing or reading h.
+ *   x : fp16 [T][H] (gather != 0) or [T*topk][H];  a : fp16 [T*topk][F].
+ * Each workgroup computes gate rows and the matching up rows together, so
+ * F = N/2 must be a multiple of 64 (APMOE_INVALID_ARG otherwise); other arguments,
+ * limits and errors as apmoe_gemm with kind = APMOE_GATE_UP.
+ */
+apmoe_status apmoe_gemm_act(apmoe_ctx *ctx, const apmoe_table *tbl, int32_t layer, const uint16_t *x,
+                            int32_t gather, const int32_t *perm, const int32_t *offsets, int32_t T, int32_t topk,
+                            uint16_t *a, void *stream);
+
 /* Output accumulation: out[t][n] = sum_{j < topk} topk_w[t][j] * y[inv_perm[t*topk + j]][n],
  * fp32, summed in j order, stored fp16.  y is [T*topk][H] of y_dtype; H % 8 == 0. */
 apmoe_status apmoe_combine(apmoe_ctx *ctx, const void *y, int32_t y_dtype, const float *topk_w,
@@ -310,11 +325,12 @@ apmoe_status apmoe_moe_workspace(const apmoe_table *tbl, int32_t layer, int32_t 
                                  size_t *bytes);
 
 /*
- * Whole layer: route, gate_up (gather, fp16 h), act, down (fp32 y), combine.
+ * Whole layer in four steps: route, gate_up with the activation fused
+ * (apmoe_gemm_act, fp16 a), down (fp32 y), combine.
  * The table's experts of the layer are the routed ones (w_router rows) followed by
  * n_shared shared experts.
  * ws is caller-owned device memory of at least apmoe_moe_workspace bytes, 256-byte
- * aligned; it holds ids, weights, counts, offsets, perm, inv_perm, h, a and y.
+ * aligned; it holds ids, weights, counts, offsets, perm, inv_perm, a and y.
  * out fp16 [T][H].
  */
 apmoe_status apmoe_moe_forward(apmoe_ctx *ctx, const apmoe_table *tbl, int32_t layer, const uint16_t *x,

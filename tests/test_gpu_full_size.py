@@ -100,6 +100,24 @@ def test_mixtral8x7b_prefill():
     _single_layer_case(cfg, [0, 1234, 4095])
 
 
+def test_mixtral8x7b_prefill_fused_activation():
+    """At full prefill size (tile product), gate_up with the activation fused gives
+    the bits of gate_up to fp16 h plus the activation launch."""
+    cfg = synth.config_by_name("mixtral8x7b_prefill_t4096_zipf")
+    q = synth.gen_qmap(cfg)
+    rw = ResidentWeights(ctx(), 1, cfg.weight_experts)
+    _upload_layer_gpu(rw, cfg, 0, 0, q)
+    rw.commit()
+    x, wr, bias = synth.gen_x(cfg), synth.gen_router(cfg), synth.gen_bias(cfg)
+    x_d = dev(x)
+    o = _run_layer(rw, 0, x_d, dev(wr), None if bias is None else dev(bias), cfg, cfg.tokens)
+    a = torch.empty_like(o["a"])
+    apw.gemm_act(ctx(), rw.table, 0, x_d, True, o["perm"], o["offsets"], cfg.tokens, cfg.assign, a)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(a).view(np.uint16), host(o["a"]).view(np.uint16))
+    rw.close()
+
+
 def test_32_layers_resident_with_map_switch():
     cfg = synth.config_by_name("mixtral8x7b_32layer_decode_t32")
     L, E, T = cfg.layers, cfg.experts, cfg.tokens

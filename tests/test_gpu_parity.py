@@ -469,6 +469,49 @@ def test_layer_shared_experts(T, renorm):
     assert np.array_equal(host(fused).view(np.uint16), host(o["out"]).view(np.uint16))
 
 
+@pytest.mark.parametrize("q", [3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("T", [8, 150])
+def test_gemm_act_matches_two_steps(T, q):
+    """The activation fused into the gate_up epilogue (decode product at T = 8, tile
+    product for experts above 32 rows at T = 150) gives exactly the bits of gate_up to
+    fp16 h followed by the activation launch."""
+    cfg = synth.CONFIGS[0]
+    L = Layer(cfg, T=T, qmap=np.full((cfg.weight_experts, 2), q, np.int32))
+    o = L.run()
+    a = torch.full_like(o["a"], float("nan"))
+    apw.gemm_act(ctx(), L.rw.table, L.layer, L.x_d, True, o["perm"], o["offsets"], T, cfg.assign, a)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(a).view(np.uint16), host(o["a"]).view(np.uint16))
+
+
+def test_gemm_act_shared_experts_and_rejects_odd_f():
+    cfg = TINY_SHARED
+    L = Layer(cfg, T=48)
+    o = L.run()
+    a = torch.empty_like(o["a"])
+    apw.gemm_act(ctx(), L.rw.table, L.layer, L.x_d, True, o["perm"], o["offsets"], 48, cfg.assign, a)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(a).view(np.uint16), host(o["a"]).view(np.uint16))
+    # a gate_up block of 96 rows (F = 48, not a multiple of 64) cannot pair gate and up rows
+    N, K = 96, 128
+    tbl = apw.Table(1, 1)
+    P = synth.gen_planes_shape(71, 0, 0, 0, N, K)
+    Pd = torch.empty((8, apw.tiled_plane_words(N, K)), dtype=torch.int32, device="cuda")
+    apw.tile_planes(ctx(), dev(P), N, K, Pd)
+    luts = {b: dev(np.tile(np.arange(1 << b, dtype=np.float16), (N, 1))) for b in range(3, 9)}
+    tbl.set_block(0, 0, apw.GATE_UP, N, K, 8, [Pd[p] for p in range(8)], luts)
+    tbl.commit(ctx())
+    x = torch.zeros((4, K), dtype=torch.float16, device="cuda")
+    offs = torch.tensor([0, 4], dtype=torch.int32, device="cuda")
+    perm = torch.arange(4, dtype=torch.int32, device="cuda")
+    out = torch.zeros((4, N // 2), dtype=torch.float16, device="cuda")
+    with pytest.raises(apw.ApmoeError) as ex:
+        apw.gemm_act(ctx(), tbl, 0, x, True, perm, offs, 4, 1, out)
+    assert ex.value.status == apw.INVALID_ARG
+    torch.cuda.synchronize()
+    tbl.close()
+
+
 @pytest.mark.parametrize("T", [1, 5, 13])
 def test_layer_tiny_ragged_tokens(T):
     cfg = synth.CONFIGS[0]
