@@ -27,12 +27,13 @@ constexpr int kGemmRowsPerBlock = 64;
 constexpr int kDecodeMaxRows = 32;
 
 // Expert activation of one (gate, up) pair of fp16 values: SiLU(g) * u with
-// SiLU(z) = z / (1 + e^-z), fp32 math, fp16 result (RNE).  The activation launch
-// and the products' fused epilogue both call this, so the two give identical bits.
+// SiLU(z) = z / (1 + e^-z), fp32 math (the hardware reciprocal, 1 ulp, instead of a
+// correctly rounded divide), fp16 result (RNE).  The activation launch and the
+// products' fused epilogue both call this, so the two give identical bits.
 __device__ __attribute__((always_inline)) inline _Float16 silu_mul(_Float16 g, _Float16 u)
 {
     const float z = (float)g;
-    return (_Float16)(z / (1.0f + __expf(-z)) * (float)u);
+    return (_Float16)(z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)) * (float)u);
 }
 // Token rows per tile of the MFMA tile product.
 constexpr int kTileTokens = 256;
