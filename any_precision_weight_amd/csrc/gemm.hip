@@ -95,14 +95,17 @@ struct GemmParams {
 };
 
 // Plane bases are wave-uniform (scalar registers); the per-lane part is a 32-bit
-// word offset into the tiled plane, so each load is one global_load_dwordx2 with a
-// scalar base and a wave reads 512 contiguous bytes per plane.
+// word offset into the tiled plane, so each load is one buffer_load_dwordx2 with a
+// scalar base and a wave reads 512 contiguous bytes per plane.  Plane words are used
+// once: the requests are non-temporal (cache policy NT), so the stream does not push
+// the token rows, which every row block of the expert reads again, out of the caches.
+constexpr int kLoadNT = 2;  // buffer-load cache policy bits: NT
 template <int Q>
 __device__ inline void load_planes(u32x2 (&w)[Q], const __amdgpu_buffer_rsrc_t (&rs)[Q], uint32_t word)
 {
 #pragma unroll
     for (int p = 0; p < Q; ++p)
-        w[p] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs[p], (int)(word * 4u), 0, 0));
+        w[p] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs[p], (int)(word * 4u), 0, kLoadNT));
 }
 
 // 4 B fragments (32 fp16 columns) of this lane's token row, starting at byte `off`.
