@@ -277,10 +277,12 @@ GEMM_QS = [3, 4, 5, 6, 7, 8]
 GEMM_COUNTS = [0, 1, 33, 70, 5, 31]
 
 
-@pytest.mark.parametrize("NK", [(136, 384), (64, 256), (200, 1024)])
+@pytest.mark.parametrize("NK", [(136, 384), (64, 256), (200, 1024), (96, 128), (112, 128), (40, 640)])
 def test_gemm_identity_lut_exact(NK):
     """Identity LUT + integer activations: every partial sum is an integer below
-    2^24, so the fp32 result must equal the integer matmul exactly."""
+    2^24, so the fp32 result must equal the integer matmul exactly.  Shapes include
+    K = 128 (one 128-column step: the second column half of a workgroup has none),
+    an odd number of steps, and N % 64 of 8, 32 and 48 (a partly valid row tile)."""
     N, K = NK
     tbl, keep, P, L, offsets, perm, T = _gemm_setup(GEMM_QS, GEMM_COUNTS, N, K, True, 41)
     x = RNG.integers(-2, 3, (T, K)).astype(np.float16)
@@ -331,6 +333,7 @@ def test_gemm_non_gather_rows():
 # more than one group of 8 weight-row tiles.
 TILE_CASES = [
     (200, 384, [300, 0, 257, 33, 600, 64]),
+    (112, 128, [40, 300, 0, 33, 1, 90]),  # K = 128: one step; N % 128 = 112
     (1280, 256, [40, 300, 1, 31, 500, 32]),
     (64, 1024, [256, 512, 3, 0, 129, 70]),
 ]
