@@ -307,30 +307,35 @@ __device__ void gemm_block(const GemmParams &P, const DevBlock &blk, int rb, int
         if (has_steps)
             load_x_group(xa, rx, xoff);
         uint32_t word = lane_word;
-        for (int step = half; step < nsteps; step += 2) {
+        // one step: requests for the next step go to `nxt` while `cur` is consumed
+        auto step_body = [&](const u32x2 (&cur)[Q], u32x2 (&nxt)[Q], int step) {
             const bool more = step + 2 < nsteps;
-            u32x2 wn[Q];
             // Vector-memory requests complete in issue order: the B group used later in
             // this step goes first, so waiting for it leaves the next step's plane words
             // in flight for a whole step.
             load_x_group(xb, rx, xoff + 64);
             __builtin_amdgcn_sched_barrier(0);
             word += more ? kNextWords : 0u;
-            load_planes<Q>(wn, rs, word);
+            load_planes<Q>(nxt, rs, word);
             __builtin_amdgcn_sched_barrier(0);
             if constexpr (Q == 3)
-                group_product_pair3<0>(wc, xa, lds_base, lane_const, acc);
+                group_product_pair3<0>(cur, xa, lds_base, lane_const, acc);
             else
-                group_product<Q, 0>(wc, xa, lds_base, lane_const, acc);
+                group_product<Q, 0>(cur, xa, lds_base, lane_const, acc);
             xoff += more ? 2 * kStepCols * 2 : 0;  // this wave's next step: 256 columns on
             load_x_group(xa, rx, xoff);
             if constexpr (Q == 3)
-                group_product_pair3<1>(wc, xb, lds_base, lane_const, acc);
+                group_product_pair3<1>(cur, xb, lds_base, lane_const, acc);
             else
-                group_product<Q, 1>(wc, xb, lds_base, lane_const, acc);
-#pragma unroll
-            for (int p = 0; p < Q; ++p)
-                wc[p] = wn[p];
+                group_product<Q, 1>(cur, xb, lds_base, lane_const, acc);
+        };
+        // two steps per iteration with the plane registers in swapped roles: no copies
+        u32x2 wd[Q];
+        for (int step = half; step < nsteps; step += 4) {
+            step_body(wc, wd, step);
+            if (step + 2 >= nsteps)
+                break;
+            step_body(wd, wc, step + 2);
         }
 
         // ---- sum the two column halves, write rows of this pass ------------------
