@@ -58,27 +58,39 @@ __device__ inline uint32_t bitrev(uint32_t c, int q) { return __builtin_bitrever
 
 // In-place transpose of 4 independent 8x8 bit blocks: on input d[p] byte b bit j is
 // plane p, column 8b+j; on output d[j] byte b bit p holds the same bit.
+// Exchange the bits of b under m with the bits of a under m << s.  BFI: two
+// bit-field inserts from the original pair (four instructions); otherwise the xor
+// form (five), which the compiler folds further when some words are known zero.
+template <bool BFI>
 __device__ inline void swap_bits(uint32_t &a, uint32_t &b, int s, uint32_t m)
 {
-    const uint32_t t = ((a >> s) ^ b) & m;
-    b ^= t;
-    a ^= t << s;
+    if constexpr (BFI) {
+        const uint32_t nb = (m & (a >> s)) | (~m & b);
+        const uint32_t na = ((m << s) & (b << s)) | (~(m << s) & a);
+        a = na;
+        b = nb;
+    } else {
+        const uint32_t t = ((a >> s) ^ b) & m;
+        b ^= t;
+        a ^= t << s;
+    }
 }
 
+template <bool BFI>
 __device__ inline void transpose8x8(uint32_t (&d)[8])
 {
-    swap_bits(d[0], d[4], 4, 0x0F0F0F0Fu);
-    swap_bits(d[1], d[5], 4, 0x0F0F0F0Fu);
-    swap_bits(d[2], d[6], 4, 0x0F0F0F0Fu);
-    swap_bits(d[3], d[7], 4, 0x0F0F0F0Fu);
-    swap_bits(d[0], d[2], 2, 0x33333333u);
-    swap_bits(d[1], d[3], 2, 0x33333333u);
-    swap_bits(d[4], d[6], 2, 0x33333333u);
-    swap_bits(d[5], d[7], 2, 0x33333333u);
-    swap_bits(d[0], d[1], 1, 0x55555555u);
-    swap_bits(d[2], d[3], 1, 0x55555555u);
-    swap_bits(d[4], d[5], 1, 0x55555555u);
-    swap_bits(d[6], d[7], 1, 0x55555555u);
+    swap_bits<BFI>(d[0], d[4], 4, 0x0F0F0F0Fu);
+    swap_bits<BFI>(d[1], d[5], 4, 0x0F0F0F0Fu);
+    swap_bits<BFI>(d[2], d[6], 4, 0x0F0F0F0Fu);
+    swap_bits<BFI>(d[3], d[7], 4, 0x0F0F0F0Fu);
+    swap_bits<BFI>(d[0], d[2], 2, 0x33333333u);
+    swap_bits<BFI>(d[1], d[3], 2, 0x33333333u);
+    swap_bits<BFI>(d[4], d[6], 2, 0x33333333u);
+    swap_bits<BFI>(d[5], d[7], 2, 0x33333333u);
+    swap_bits<BFI>(d[0], d[1], 1, 0x55555555u);
+    swap_bits<BFI>(d[2], d[3], 1, 0x55555555u);
+    swap_bits<BFI>(d[4], d[5], 1, 0x55555555u);
+    swap_bits<BFI>(d[6], d[7], 1, 0x55555555u);
 }
 
 struct GemmParams {
@@ -133,7 +145,7 @@ __device__ inline void group_product_pair3(const u32x2 (&w)[3], const u32x4 (&xg
         d[3 + p] = w[p][W] >> 1;
     }
     d[6] = d[7] = 0u;
-    transpose8x8(d);
+    transpose8x8<true>(d);
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
         u32x4 a;
@@ -155,7 +167,7 @@ __device__ inline void group_product(const u32x2 (&w)[Q], const u32x4 (&xg)[4], 
 #pragma unroll
     for (int p = 0; p < 8; ++p)
         d[p] = p < Q ? w[p < Q ? p : 0][W] : 0u;
-    transpose8x8(d);
+    transpose8x8<Q == 8>(d);  // the form with fewer instructions after folding (counted per q)
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
         half8 a;
