@@ -7,9 +7,9 @@
 //   out[r][n] = sum_c in_row(r)[c] * LUT_q[n][code_q(n, c)],  fp32 accumulation,
 //   code_q(n, c) = bits of planes 0..q-1 at column c, plane 0 most significant.
 //
-// Workgroup = 4 waves = 64 weight rows of one expert.  Wave w covers rows
-// 32*(w&1) .. +31 and every other 128-column step (w>>1 picks the half); the two
-// halves are summed through LDS at the end.  Planes are read in the tiled layout
+// Workgroup = 2 x kParts waves = 64 weight rows of one expert.  Wave w covers rows
+// 32*(w&1) .. +31 and every kParts-th 128-column step (w>>1 picks the column part);
+// the parts are summed through LDS at the end in a fixed order.  Planes are read in the tiled layout
 // (32-row x 128-column tiles of 512 bytes, one tile per wave step and plane).  For
 // each step a lane loads, for its row, two words (64 columns) of each of the q
 // needed planes (only planes p < q are touched), turns them into 8-bit codes with an 8x8 bit transpose, looks the
@@ -34,12 +34,13 @@ namespace apmoe {
 namespace {
 
 constexpr int kWave = 64;
-constexpr int kThreads = 256;
+constexpr int kParts = 2;                  // column parts of a workgroup (waves: 2 row tiles x kParts)
+constexpr int kThreads = 2 * kParts * 64;
 constexpr int kRows = kGemmRowsPerBlock;  // 64
 constexpr int kStepCols = 128;            // columns per wave step (2 lane halves x 64)
 constexpr int kTokTile = 32;
 constexpr int kLutBytes = 32 * 1024;                       // LUT region, every q
-constexpr int kRedBytes = 2 * 16 * kWave * sizeof(float);  // column-half reduction
+constexpr int kRedBytes = (kParts - 1) * 2 * 16 * kWave * sizeof(float);  // column-part reduction
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float float16v __attribute__((ext_vector_type(16)));
@@ -194,7 +195,8 @@ __device__ __attribute__((always_inline)) inline void stage_lut(const __amdgpu_b
 {
     if constexpr (Q == 3) {
         // pair table of LUT_3: entry (row 32t+i, pair code v) at v*256 + 128t + 4i;
-        // thread -> row tid % 64, pair codes 16(tid/64) .. +15
+        // thread -> row tid % 64 and kPairsPer of the 64 pair codes
+        constexpr int kPairsPer = 64 / (kThreads / kRows);
         const int nl = tid % kRows, part = tid / kRows;
         const int n = (nl < 32 ? nA : nB) + (nl & 31);
         const u32x4 lv = n < N ? __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
@@ -203,8 +205,8 @@ __device__ __attribute__((always_inline)) inline void stage_lut(const __amdgpu_b
         first_loads();
         const uint32_t slot = (uint32_t)(128 * (nl >> 5) + 4 * (nl & 31));
 #pragma unroll
-        for (int kk = 0; kk < 16; ++kk) {
-            const uint32_t v = (uint32_t)(16 * part + kk);
+        for (int kk = 0; kk < kPairsPer; ++kk) {
+            const uint32_t v = (uint32_t)(kPairsPer * part + kk);
             const uint32_t ce = bitrev(v & 7u, 3), co = bitrev(v >> 3, 3);  // codes of the even / odd column
             const uint32_t lo = (lv[ce >> 1] >> (16 * (ce & 1))) & 0xFFFFu;
             const uint32_t hi = (lv[co >> 1] >> (16 * (co & 1))) & 0xFFFFu;
@@ -259,7 +261,7 @@ __device__ void gemm_block(const GemmParams &P, const DevBlock &blk, int rb, int
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform (scalar)
-    const int t = wave & 1, half = wave >> 1;
+    const int t = wave & 1, part = wave >> 1;  // row tile, column part
     const int i = lane & 31, g = lane >> 5;
     const int N = P.N, K = P.K;
     // first rows of the block's two 32-row tiles: consecutive, or with the activation
@@ -268,15 +270,15 @@ __device__ void gemm_block(const GemmParams &P, const DevBlock &blk, int rb, int
     const int nB = P.act ? (N >> 1) + 32 * rb : rb * kRows + 32;
     const int nt = t ? nB : nA;  // this wave's tile
     const int nsteps = K / kStepCols;  // K % 128 == 0
-    // half 1 has no step when K == 128: it must not touch planes or token rows at all
-    const bool has_steps = half < nsteps;
+    // a part past the last step (K < 128 kParts) must not touch planes or token rows at all
+    const bool has_steps = part < nsteps;
     // tiled planes: tile (rt, kt) = rows 32rt.., columns 128kt.., 128 words; this lane
     // reads words 2*lane, 2*lane+1 of each tile.  A row tile past the end (N % 64 in
     // (0, 32]) reads tile row 0; its outputs are not written.
     const int RT = (N + 31) / 32, KT = K / kStepCols;
     const int rt = nt / 32;
-    const uint32_t lane_word = ((uint32_t)(rt < RT ? rt : 0) * (uint32_t)KT + (uint32_t)half) * 128u + 2u * lane;
-    constexpr uint32_t kNextWords = 2 * 128;  // this wave's next step: two tiles on
+    const uint32_t lane_word = ((uint32_t)(rt < RT ? rt : 0) * (uint32_t)KT + (uint32_t)part) * 128u + 2u * lane;
+    constexpr uint32_t kNextWords = kParts * 128;  // this wave's next step: kParts tiles on
     __amdgpu_buffer_rsrc_t rs[Q];
 #pragma unroll
     for (int p = 0; p < Q; ++p)
@@ -305,7 +307,7 @@ __device__ void gemm_block(const GemmParams &P, const DevBlock &blk, int rb, int
         const int r = r0 + min(tp + j, Me - 1);
         const int src = P.gather ? P.perm[r] / P.topk : r;
         // lanes past the last token request an offset beyond the buffer: zeros, no cache traffic
-        uint32_t xoff = tok_ok ? ((uint32_t)src * (uint32_t)K + (uint32_t)(half * kStepCols + 64 * g)) * 2u  // bytes
+        uint32_t xoff = tok_ok ? ((uint32_t)src * (uint32_t)K + (uint32_t)(part * kStepCols + 64 * g)) * 2u  // bytes
                                : 0x80000000u;
         if (tp > 0 && has_steps)
             load_planes<Q>(wc, rs, lane_word);
@@ -321,7 +323,7 @@ __device__ void gemm_block(const GemmParams &P, const DevBlock &blk, int rb, int
         uint32_t word = lane_word;
         // one step: requests for the next step go to `nxt` while `cur` is consumed
         auto step_body = [&](const u32x2 (&cur)[Q], u32x2 (&nxt)[Q], int step) {
-            const bool more = step + 2 < nsteps;
+            const bool more = step + kParts < nsteps;
             // Vector-memory requests complete in issue order: the B group used later in
             // this step goes first, so waiting for it leaves the next step's plane words
             // in flight for a whole step.
@@ -334,7 +336,7 @@ __device__ void gemm_block(const GemmParams &P, const DevBlock &blk, int rb, int
                 group_product_pair3<0>(cur, xa, lds_base, lane_const, acc);
             else
                 group_product<Q, 0>(cur, xa, lds_base, lane_const, acc);
-            xoff += more ? 2 * kStepCols * 2 : 0;  // this wave's next step: 256 columns on
+            xoff += more ? kParts * kStepCols * 2 : 0;  // this wave's next step: kParts x 128 columns on
             load_x_group(xa, rx, xoff);
             if constexpr (Q == 3)
                 group_product_pair3<1>(cur, xb, lds_base, lane_const, acc);
@@ -343,28 +345,32 @@ __device__ void gemm_block(const GemmParams &P, const DevBlock &blk, int rb, int
         };
         // two steps per iteration with the plane registers in swapped roles: no copies
         u32x2 wd[Q];
-        for (int step = half; step < nsteps; step += 4) {
+        for (int step = part; step < nsteps; step += 2 * kParts) {
             step_body(wc, wd, step);
-            if (step + 2 >= nsteps)
+            if (step + kParts >= nsteps)
                 break;
-            step_body(wd, wc, step + 2);
+            step_body(wd, wc, step + kParts);
         }
 
-        // ---- sum the two column halves, write rows of this pass ------------------
-        if (half == 1) {
+        // ---- sum the column parts (fixed order), write rows of this pass ---------
+        // part p >= 1 of row tile t writes slot (p - 1, t)
+        auto slot = [&](int p, int tt, int v) { return (((p - 1) * 2 + tt) * 16 + v) * kWave + lane; };
+        if (part > 0) {
 #pragma unroll
             for (int v = 0; v < 16; ++v)
-                red[(t * 16 + v) * kWave + lane] = acc[v];
+                red[slot(part, t, v)] = acc[v];
         }
         __syncthreads();
-        if (half == 0) {
+        if (part == 0) {
 #pragma unroll
-            for (int v = 0; v < 16; ++v)
-                acc[v] += red[(t * 16 + v) * kWave + lane];
+            for (int p = 1; p < kParts; ++p)
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    acc[v] += red[slot(p, t, v)];
         }
         // D layout of the 32x32 MFMA: column j = lane%32, row = 8*(v/4) + 4*(lane/32) + v%4
         if (!P.act) {
-            if (half == 0 && tok_ok) {
+            if (part == 0 && tok_ok) {
                 // rows nt + 4g + 8(v/4) + v%4 of token row r0 + tp + j: one base, constant offsets
                 const size_t o0 = (size_t)(r0 + tp + j) * N + (size_t)(nt + 4 * g);
                 const int nleft = N - (nt + 4 * g);
@@ -383,21 +389,21 @@ __device__ void gemm_block(const GemmParams &P, const DevBlock &blk, int rb, int
             }
         } else {
             // the up wave hands its fp16-rounded rows to the gate wave of the same lanes
-            // through its own reduction slots (already read by it; only it touches them);
-            // the gate wave writes a = SiLU(gate) * up
-            if (half == 0 && t == 1) {
+            // through slot (1, up tile) (already read by it; no other wave touches it
+            // after the barrier); the gate wave writes a = SiLU(gate) * up
+            if (part == 0 && t == 1) {
 #pragma unroll
                 for (int v = 0; v < 16; ++v)
-                    red[(16 + v) * kWave + lane] = (float)(_Float16)acc[v];
+                    red[slot(1, 1, v)] = (float)(_Float16)acc[v];
             }
             __syncthreads();
-            if (half == 0 && t == 0 && tok_ok) {
+            if (part == 0 && t == 0 && tok_ok) {
                 // rows f = nA + 4g + 8(v/4) + v%4 < F of token row r0 + tp + j
                 _Float16 *oa = reinterpret_cast<_Float16 *>(P.out) + (size_t)(r0 + tp + j) * (size_t)(N >> 1) +
                                (size_t)(nA + 4 * g);
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
-                    const _Float16 up = (_Float16)red[(16 + v) * kWave + lane];
+                    const _Float16 up = (_Float16)red[slot(1, 1, v)];
                     oa[8 * (v >> 2) + (v & 3)] = silu_mul((_Float16)acc[v], up);
                 }
             }
