@@ -195,12 +195,15 @@ __device__ __attribute__((always_inline)) bool resolve_tile(const TileParams &P,
     return true;
 }
 
-template <int Q>
+// NT: request with the non-temporal cache policy.  Down-product plane words pass
+// through once per token tile and are better kept out of the caches; gate_up ones
+// measured faster with the default policy.
+template <int Q, bool NT>
 __device__ inline void load_planes(u32x2 (&w)[Q], const __amdgpu_buffer_rsrc_t (&rs)[Q], uint32_t word)
 {
 #pragma unroll
     for (int p = 0; p < Q; ++p)
-        w[p] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs[p], (int)(word * 4u), 0, 0));
+        w[p] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs[p], (int)(word * 4u), 0, NT ? 2 : 0));
 }
 
 // Codes of word W (32 columns) of this lane's row: d[j] byte b = transposed code of
@@ -330,7 +333,7 @@ __device__ inline void consume(uint32_t a_stage, uint32_t a_lane, uint32_t x_sta
 // TTN: token tiles per consumer (a power of two, at most 4); consumers whose token
 // half holds no row of the tile skip their products.  Rows past the tile's last
 // token repeat that token and are not written.
-template <int Q, int TTN>
+template <int Q, int TTN, int KIND>
 __device__ __attribute__((always_inline)) void tile_block(const TileParams &P, const DevBlock &blk, const Tile &T,
                                                           char *smem)
 {
@@ -425,7 +428,7 @@ __device__ __attribute__((always_inline)) void tile_block(const TileParams &P, c
         constexpr int kWaitOdd = 8 * D + Q * (D == 0 ? 0 : 1);
         constexpr int kWaitEven = 8 * D + Q;
         auto xbuf = [&](int n) -> char * { return x_dst + (n % L::kNxb) * kStageBytes; };
-        load_planes<Q>(pa, rs, step_word(0));
+        load_planes<Q, KIND == APMOE_DOWN>(pa, rs, step_word(0));
 #pragma unroll
         for (int n = 0; n < D; ++n)
             x_stage(xbuf(n), rx, X, n, nst);
@@ -433,7 +436,7 @@ __device__ __attribute__((always_inline)) void tile_block(const TileParams &P, c
         // phase 0: stage 0 = word 0 of step 0
         x_stage(xbuf(D), rx, X, D, nst);
         __builtin_amdgcn_sched_barrier(0);
-        load_planes<Q>(pb, rs, step_word(1));
+        load_planes<Q, KIND == APMOE_DOWN>(pb, rs, step_word(1));
         produce_a<Q, 0>(pa, lane_const, a_dst);
         phase_barrier<kWaitEven>();
         for (int m = 0; m < KT2 / 2; ++m) {
@@ -445,7 +448,7 @@ __device__ __attribute__((always_inline)) void tile_block(const TileParams &P, c
             // phase n+2: stage n+2 = word 0 of step 2m+1 -> A buffer 0
             x_stage(xbuf(n + 2 + D), rx, X, n + 2 + D, nst);
             __builtin_amdgcn_sched_barrier(0);  // the plane requests follow the token copies
-            load_planes<Q>(pa, rs, step_word(2 * m + 2));
+            load_planes<Q, KIND == APMOE_DOWN>(pa, rs, step_word(2 * m + 2));
             produce_a<Q, 0>(pb, lane_const, a_dst);
             phase_barrier<kWaitEven>();
             // phase n+3: stage n+3 = word 1 of step 2m+1 -> A buffer 1
@@ -455,7 +458,7 @@ __device__ __attribute__((always_inline)) void tile_block(const TileParams &P, c
             // phase n+4: stage n+4 = word 0 of step 2m+2 -> A buffer 0
             x_stage(xbuf(n + 4 + D), rx, X, n + 4 + D, nst);
             __builtin_amdgcn_sched_barrier(0);
-            load_planes<Q>(pb, rs, step_word(2 * m + 3));
+            load_planes<Q, KIND == APMOE_DOWN>(pb, rs, step_word(2 * m + 3));
             produce_a<Q, 0>(pa, lane_const, a_dst);
             phase_barrier<kWaitEven>();
         }
@@ -595,17 +598,17 @@ __device__ __attribute__((always_inline)) void tile_block(const TileParams &P, c
     }
 }
 
-template <int TTN>
+template <int TTN, int KIND>
 __device__ __attribute__((always_inline)) void dispatch_q(const TileParams &P, const DevBlock &blk, const Tile &T,
                                                           char *smem)
 {
     switch (blk.q) {
-    case 3: tile_block<3, TTN>(P, blk, T, smem); break;
-    case 4: tile_block<4, TTN>(P, blk, T, smem); break;
-    case 5: tile_block<5, TTN>(P, blk, T, smem); break;
-    case 6: tile_block<6, TTN>(P, blk, T, smem); break;
-    case 7: tile_block<7, TTN>(P, blk, T, smem); break;
-    case 8: tile_block<8, TTN>(P, blk, T, smem); break;
+    case 3: tile_block<3, TTN, KIND>(P, blk, T, smem); break;
+    case 4: tile_block<4, TTN, KIND>(P, blk, T, smem); break;
+    case 5: tile_block<5, TTN, KIND>(P, blk, T, smem); break;
+    case 6: tile_block<6, TTN, KIND>(P, blk, T, smem); break;
+    case 7: tile_block<7, TTN, KIND>(P, blk, T, smem); break;
+    case 8: tile_block<8, TTN, KIND>(P, blk, T, smem); break;
     default: break;  // unreachable: commit validates q
     }
 }
@@ -621,11 +624,11 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
     const DevBlock blk = P.table[2 * T.e + P.kind];
     const int ntt = (T.M + 31) / 32;  // token tiles of the tile (two halves of at most 4)
     if (ntt > 2)
-        dispatch_q<4>(P, blk, T, smem);
+        dispatch_q<4, KIND>(P, blk, T, smem);
     else if (ntt > 1)
-        dispatch_q<2>(P, blk, T, smem);
+        dispatch_q<2, KIND>(P, blk, T, smem);
     else
-        dispatch_q<1>(P, blk, T, smem);
+        dispatch_q<1, KIND>(P, blk, T, smem);
 }
 
 }  // namespace
