@@ -41,6 +41,16 @@ constexpr int kStepCols = 128;            // columns per wave step (2 lane halve
 constexpr int kTokTile = 32;
 constexpr int kLutBytes = 32 * 1024;                       // LUT region, every q
 constexpr int kRedBytes = (kParts - 1) * 2 * 16 * kWave * sizeof(float);  // column-part reduction
+constexpr int kXRowBytes = kStepCols * 2;                   // one token row of one step (fp16)
+constexpr uint32_t kNoWord = 0x20000000u;  // plane word offset past every plane (byte offset 2^31)
+// s_waitcnt operands (vmcnt in bits 3:0 and 15:14, expcnt 6:4 left open, lgkmcnt 11:8)
+constexpr int kWaitAll = 7 << 4;
+template <int VM>
+constexpr int wait_vm()
+{
+    static_assert(VM >= 0 && VM < 16, "vmcnt range");
+    return VM | (7 << 4);
+}
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float float16v __attribute__((ext_vector_type(16)));
@@ -103,6 +113,7 @@ struct GemmParams {
     int kind, E, N, K, topk, gather, out_f32, row_blocks;
     int act;               // gate_up with the activation fused: out = a [rows][N/2] fp16
     int max_rows;          // experts with more rows belong to the tile product
+    int tokl;              // token rows per pass (8 or 16): the LDS token buffers' size
     uint32_t in_bytes;     // bytes of `in` (buffer range of the B-operand loads)
     uint32_t plane_bytes;  // bytes of one tiled plane
 };
@@ -121,12 +132,10 @@ __device__ inline void load_planes(u32x2 (&w)[Q], const __amdgpu_buffer_rsrc_t (
         w[p] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs[p], (int)(word * 4u), 0, kLoadNT));
 }
 
-// 4 B fragments (32 fp16 columns) of this lane's token row, starting at byte `off`.
-__device__ inline void load_x_group(u32x4 (&xg)[4], __amdgpu_buffer_rsrc_t rx, uint32_t off)
+// One B fragment (8 fp16 columns of one token row) from the LDS token buffer.
+__device__ inline u32x4 lds_b128(uint32_t addr)
 {
-#pragma unroll
-    for (int f = 0; f < 4; ++f)
-        xg[f] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(off + 16u * f), 0, 0));
+    return *reinterpret_cast<const __attribute__((address_space(3))) u32x4 *>((uintptr_t)addr);
 }
 
 // 4 MFMAs over one 32-column word of each needed plane: unpack, LUT gather, multiply.
@@ -135,10 +144,14 @@ __device__ inline void load_x_group(u32x4 (&xg)[4], __amdgpu_buffer_rsrc_t rx, u
 // transposed codes of columns 8b+j (bits 0..2) and 8b+j+1 (bits 3..5) -- an index
 // into the pair table of LUT_3 (entry = two fp16, the even column's in the low half).
 // One ds_read_b32 per pair yields two A-operand elements with no repacking.
-template <int W>
-__device__ inline void group_product_pair3(const u32x2 (&w)[3], const u32x4 (&xg)[4], uint32_t lut_base,
+template <int W, int XOFF>
+__device__ inline void group_product_pair3(const u32x2 (&w)[3], const uint32_t (&xaddr)[8], uint32_t lut_base,
                                            uint32_t lane_const, float16v &acc)
 {
+    u32x4 xg[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+        xg[b] = lds_b128(xaddr[4 * W + b] + XOFF);
     uint32_t d[8];
 #pragma unroll
     for (int p = 0; p < 3; ++p) {
@@ -160,10 +173,14 @@ __device__ inline void group_product_pair3(const u32x2 (&w)[3], const u32x4 (&xg
     }
 }
 
-template <int Q, int W>
-__device__ inline void group_product(const u32x2 (&w)[Q], const u32x4 (&xg)[4], uint32_t lut_base,
+template <int Q, int W, int XOFF>
+__device__ inline void group_product(const u32x2 (&w)[Q], const uint32_t (&xaddr)[8], uint32_t lut_base,
                                      uint32_t lane_const, float16v &acc)
 {
+    u32x4 xg[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+        xg[b] = lds_b128(xaddr[4 * W + b] + XOFF);
     uint32_t d[8];
 #pragma unroll
     for (int p = 0; p < 8; ++p)
@@ -255,7 +272,7 @@ __device__ __attribute__((always_inline)) inline void stage_lut(const __amdgpu_b
     }
 }
 
-template <int Q>
+template <int Q, int TOKL>
 __device__ void gemm_block(const GemmParams &P, const DevBlock &blk, int rb, int r0, int Me, char *smem)
 {
     const int tid = threadIdx.x;
@@ -286,73 +303,109 @@ __device__ void gemm_block(const GemmParams &P, const DevBlock &blk, int rb, int
     const __amdgpu_buffer_rsrc_t rl = make_rsrc(blk.lut, (uint32_t)N << (Q + 1));
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(P.in, P.in_bytes);
 
+    // a wave whose part has no step here reads nothing: its plane requests fall past the
+    // buffer (zeros, no memory traffic), and it still takes part in the barriers
+    const uint32_t first_word = has_steps ? lane_word : kNoWord;
     u32x2 wc[Q];
-    stage_lut<Q>(rl, nA, nB, N, tid, smem, [&] {
-        if (has_steps)
-            load_planes<Q>(wc, rs, lane_word);
-    });
+    stage_lut<Q>(rl, nA, nB, N, tid, smem, [&] { load_planes<Q>(wc, rs, first_word); });
     __syncthreads();
 
-    // LDS byte address of the region (a compile-time constant for the static array)
+    // LDS byte addresses (dynamic LDS starts at address 0 of the workgroup's allocation)
     const uint32_t lds_base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char *)smem);
     const uint32_t lane_const = Q == 3  ? (uint32_t)(128 * t + 4 * i)
                                 : Q < 8 ? (uint32_t)(4 * (32 * g + i) + 2 * t)
                                         : (uint32_t)(4 * i + 2 * t);
-    float *red = reinterpret_cast<float *>(smem + kLutBytes);
+    char *xs = smem + kLutBytes;
+    const uint32_t xs_base = lds_base + kLutBytes;
+    float *red = reinterpret_cast<float *>(xs);  // used after the last token tile is read
+    constexpr int kXBuf = 2 * TOKL * kXRowBytes;  // one token buffer: 2 parts x TOKL rows
+    constexpr int kDma = TOKL / 8;                // token copies per wave and workgroup step
+    const int nws = (nsteps + 1) / 2;              // workgroup steps: part p takes step 2s + p
+    static_assert(kParts == 2, "token tiles and workgroup steps assume two column parts");
 
-    for (int tp = 0; tp < Me; tp += kTokTile) {
-        const int j = lane & 31;  // token of this lane in the B operand
-        const bool tok_ok = tp + j < Me;
-        // lanes past the last token keep a valid row index; their D columns are discarded
-        const int r = r0 + min(tp + j, Me - 1);
-        const int src = P.gather ? P.perm[r] / P.topk : r;
-        // lanes past the last token request an offset beyond the buffer: zeros, no cache traffic
-        uint32_t xoff = tok_ok ? ((uint32_t)src * (uint32_t)K + (uint32_t)(part * kStepCols + 64 * g)) * 2u  // bytes
-                               : 0x80000000u;
-        if (tp > 0 && has_steps)
-            load_planes<Q>(wc, rs, lane_word);
+    for (int tp = 0; tp < Me; tp += TOKL) {
+        const int j = lane & 31;  // token column of this lane in the B operand and in D
+        const bool tok_ok = j < TOKL && tp + j < Me;
+        // token copies: instruction u = wave + 4k fills rows 4u .. 4u+3 of a buffer; lane L
+        // writes 16-byte position L % 16 of row 4u + L / 16 (part row / TOKL, token row
+        // % TOKL) and fetches the chunk stored there, chunk = position ^ token row
+        uint32_t doff[kDma];
+#pragma unroll
+        for (int k = 0; k < kDma; ++k) {
+            const int row = 4 * (wave + 4 * k) + (lane >> 4);
+            const int pu = row / TOKL, jj = row % TOKL;
+            const int c = (lane & 15) ^ jj;
+            const int tok = tp + jj;
+            const int src = tok < Me ? (P.gather ? P.perm[r0 + tok] / P.topk : r0 + tok) : 0;
+            // rows past the expert's last token request an offset beyond the buffer
+            doff[k] = tok < Me ? ((uint32_t)src * (uint32_t)K + (uint32_t)(pu * kStepCols + 8 * c)) * 2u : 0x80000000u;
+        }
+        // token tile of workgroup step s (columns 256 s .. +255) into buffer b; the step
+        // is part of the lane offset, so the buffer's range check covers it
+        auto copy_tokens = [&](int s, int b) {
+#pragma unroll
+            for (int k = 0; k < kDma; ++k)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rx, (__attribute__((address_space(3))) void *)(xs + b * kXBuf + 1024 * (wave + 4 * k)), 16,
+                    doff[k] + (uint32_t)s * (2u * kStepCols * 2u), 0, 0, 0);
+        };
+        // B-operand addresses in buffer 0: fragment f of word W is chunk 8g + 4W + f of this
+        // lane's token row in its part; lanes of token columns >= TOKL repeat a row (their
+        // D columns are not written)
+        const int jb = j & (TOKL - 1);
+        uint32_t xaddr[8];
+#pragma unroll
+        for (int f = 0; f < 8; ++f)
+            xaddr[f] = xs_base + (uint32_t)((part * TOKL + jb) * kXRowBytes + (((8 * g + f) ^ jb) << 4));
+
+        if (tp > 0)
+            load_planes<Q>(wc, rs, first_word);
+        copy_tokens(0, 0);
+        __builtin_amdgcn_s_waitcnt(kWaitAll);
+        __syncthreads();
+
         float16v acc;
 #pragma unroll
         for (int v = 0; v < 16; ++v)
             acc[v] = 0.f;
-        // B-operand groups (4 fragments = 32 columns) are double-buffered and requested
-        // one group ahead, continuing across steps; planes are requested one step ahead.
-        u32x4 xa[4], xb[4];
-        if (has_steps)
-            load_x_group(xa, rx, xoff);
-        uint32_t word = lane_word;
-        // one step: requests for the next step go to `nxt` while `cur` is consumed
-        auto step_body = [&](const u32x2 (&cur)[Q], u32x2 (&nxt)[Q], int step) {
-            const bool more = step + kParts < nsteps;
-            // Vector-memory requests complete in issue order: the B group used later in
-            // this step goes first, so waiting for it leaves the next step's plane words
-            // in flight for a whole step.
-            load_x_group(xb, rx, xoff + 64);
+        uint32_t word = first_word;
+        // workgroup step s: request the next token tile and this wave's next plane words,
+        // multiply, then wait for the token tile only (the plane words stay in flight)
+        // and pass the barrier that frees the buffer just read
+        auto step_body = [&](const u32x2 (&cur)[Q], u32x2 (&nxt)[Q], int s, auto buf) {
+            constexpr int B = decltype(buf)::value;
+            const int step = 2 * s + part;
+            // the wait below counts on the plane requests being issued after the token
+            // copies: keep the scheduler from reordering them
+            copy_tokens(s + 1 < nws ? s + 1 : s, B ^ 1);
             __builtin_amdgcn_sched_barrier(0);
-            word += more ? kNextWords : 0u;
+            word = step + kParts < nsteps ? word + kNextWords : kNoWord;
             load_planes<Q>(nxt, rs, word);
             __builtin_amdgcn_sched_barrier(0);
-            if constexpr (Q == 3)
-                group_product_pair3<0>(cur, xa, lds_base, lane_const, acc);
-            else
-                group_product<Q, 0>(cur, xa, lds_base, lane_const, acc);
-            xoff += more ? kParts * kStepCols * 2 : 0;  // this wave's next step: kParts x 128 columns on
-            load_x_group(xa, rx, xoff);
-            if constexpr (Q == 3)
-                group_product_pair3<1>(cur, xb, lds_base, lane_const, acc);
-            else
-                group_product<Q, 1>(cur, xb, lds_base, lane_const, acc);
+            if (step < nsteps) {
+                if constexpr (Q == 3) {
+                    group_product_pair3<0, B * kXBuf>(cur, xaddr, lds_base, lane_const, acc);
+                    group_product_pair3<1, B * kXBuf>(cur, xaddr, lds_base, lane_const, acc);
+                } else {
+                    group_product<Q, 0, B * kXBuf>(cur, xaddr, lds_base, lane_const, acc);
+                    group_product<Q, 1, B * kXBuf>(cur, xaddr, lds_base, lane_const, acc);
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(wait_vm<Q>());
+            asm volatile("s_barrier" ::: "memory");
         };
-        // two steps per iteration with the plane registers in swapped roles: no copies
+        // two steps per iteration with the plane registers and token buffers in swapped roles
         u32x2 wd[Q];
-        for (int step = part; step < nsteps; step += 2 * kParts) {
-            step_body(wc, wd, step);
-            if (step + kParts >= nsteps)
+        for (int s = 0; s < nws; s += 2) {
+            step_body(wc, wd, s, std::integral_constant<int, 0>{});
+            if (s + 1 >= nws)
                 break;
-            step_body(wd, wc, step + kParts);
+            step_body(wd, wc, s + 1, std::integral_constant<int, 1>{});
         }
 
         // ---- sum the column parts (fixed order), write rows of this pass ---------
+        // every token copy has landed and every wave has passed the last barrier, so the
+        // token buffers are free for the part sums
         // part p >= 1 of row tile t writes slot (p - 1, t)
         auto slot = [&](int p, int tt, int v) { return (((p - 1) * 2 + tt) * 16 + v) * kWave + lane; };
         if (part > 0) {
@@ -412,11 +465,26 @@ __device__ void gemm_block(const GemmParams &P, const DevBlock &blk, int rb, int
     }
 }
 
+template <int TOKL>
+__device__ __attribute__((always_inline)) inline void dispatch_q(const GemmParams &P, const DevBlock &blk, int rb,
+                                                                 int r0, int Me, char *smem)
+{
+    switch (blk.q) {
+    case 3: gemm_block<3, TOKL>(P, blk, rb, r0, Me, smem); break;
+    case 4: gemm_block<4, TOKL>(P, blk, rb, r0, Me, smem); break;
+    case 5: gemm_block<5, TOKL>(P, blk, rb, r0, Me, smem); break;
+    case 6: gemm_block<6, TOKL>(P, blk, rb, r0, Me, smem); break;
+    case 7: gemm_block<7, TOKL>(P, blk, rb, r0, Me, smem); break;
+    case 8: gemm_block<8, TOKL>(P, blk, rb, r0, Me, smem); break;
+    default: break;  // unreachable: commit validates q
+    }
+}
+
 // KIND (APMOE_GATE_UP / APMOE_DOWN) only names the launch, so profiles tell them apart.
 template <int KIND>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) gemm_kernel(GemmParams P)
 {
-    __shared__ __attribute__((aligned(16))) char smem[kLutBytes + kRedBytes];
+    extern __shared__ __attribute__((aligned(16))) char smem[];
     const int e = blockIdx.x % P.E;
     const int rb = blockIdx.x / P.E;
     const int r0 = P.offsets[e];
@@ -424,15 +492,10 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
     if (Me <= 0 || Me > P.max_rows)
         return;  // expert without tokens (no weight reads), or one for the tile product
     const DevBlock blk = P.table[2 * e + P.kind];
-    switch (blk.q) {
-    case 3: gemm_block<3>(P, blk, rb, r0, Me, smem); break;
-    case 4: gemm_block<4>(P, blk, rb, r0, Me, smem); break;
-    case 5: gemm_block<5>(P, blk, rb, r0, Me, smem); break;
-    case 6: gemm_block<6>(P, blk, rb, r0, Me, smem); break;
-    case 7: gemm_block<7>(P, blk, rb, r0, Me, smem); break;
-    case 8: gemm_block<8>(P, blk, rb, r0, Me, smem); break;
-    default: break;  // unreachable: commit validates q
-    }
+    if (P.tokl == 8)
+        dispatch_q<8>(P, blk, rb, r0, Me, smem);
+    else
+        dispatch_q<16>(P, blk, rb, r0, Me, smem);
 }
 
 }  // namespace
@@ -461,10 +524,16 @@ hipError_t launch_gemm(const DevBlock *table, int kind, int E, int N, int K, int
     P.in_bytes = (uint32_t)in_bytes;
     P.plane_bytes = (uint32_t)(tiled_plane_words(N, K) * 4);
     P.max_rows = kDecodeMaxRows;
+    // A token is routed to an expert at most once, so no expert has more rows than the
+    // batch has tokens (R / topk); the token buffers hold 8 or 16 rows, and an expert
+    // with more takes further passes over its weights.
+    const int tokens = topk > 0 ? R / topk : R;
+    P.tokl = tokens <= 8 ? 8 : 16;
+    const size_t lds = kLutBytes + std::max<size_t>(kRedBytes, 2 * 2 * (size_t)P.tokl * kXRowBytes);
     if (kind == APMOE_GATE_UP)
-        hipLaunchKernelGGL(gemm_kernel<APMOE_GATE_UP>, dim3(P.row_blocks * E), dim3(kThreads), 0, s, P);
+        hipLaunchKernelGGL(gemm_kernel<APMOE_GATE_UP>, dim3(P.row_blocks * E), dim3(kThreads), lds, s, P);
     else
-        hipLaunchKernelGGL(gemm_kernel<APMOE_DOWN>, dim3(P.row_blocks * E), dim3(kThreads), 0, s, P);
+        hipLaunchKernelGGL(gemm_kernel<APMOE_DOWN>, dim3(P.row_blocks * E), dim3(kThreads), lds, s, P);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || R <= kDecodeMaxRows)
         return err;  // no expert can have more rows than the decode product takes
