@@ -310,7 +310,7 @@ __device__ void gemm_block(const GemmParams &P, const DevBlock &blk, int rb, int
     stage_lut<Q>(rl, nA, nB, N, tid, smem, [&] { load_planes<Q>(wc, rs, first_word); });
     __syncthreads();
 
-    // LDS byte addresses (dynamic LDS starts at address 0 of the workgroup's allocation)
+    // LDS byte addresses (compile-time constants for the static array)
     const uint32_t lds_base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char *)smem);
     const uint32_t lane_const = Q == 3  ? (uint32_t)(128 * t + 4 * i)
                                 : Q < 8 ? (uint32_t)(4 * (32 * g + i) + 2 * t)
@@ -481,10 +481,15 @@ __device__ __attribute__((always_inline)) inline void dispatch_q(const GemmParam
 }
 
 // KIND (APMOE_GATE_UP / APMOE_DOWN) only names the launch, so profiles tell them apart.
-template <int KIND>
+// The LDS region is a static array (its address is a compile-time constant, so LUT
+// gathers need no base add): LUT, then the token buffers, which the part sums reuse.
+template <int TOKL>
+constexpr int kLdsBytes = kLutBytes + (kRedBytes > 4 * TOKL * kXRowBytes ? kRedBytes : 4 * TOKL * kXRowBytes);
+
+template <int KIND, int TOKL>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) gemm_kernel(GemmParams P)
 {
-    extern __shared__ __attribute__((aligned(16))) char smem[];
+    __shared__ __attribute__((aligned(16))) char smem[kLdsBytes<TOKL>];
     const int e = blockIdx.x % P.E;
     const int rb = blockIdx.x / P.E;
     const int r0 = P.offsets[e];
@@ -492,10 +497,17 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
     if (Me <= 0 || Me > P.max_rows)
         return;  // expert without tokens (no weight reads), or one for the tile product
     const DevBlock blk = P.table[2 * e + P.kind];
+    dispatch_q<TOKL>(P, blk, rb, r0, Me, smem);
+}
+
+template <int KIND>
+void launch_kind(const GemmParams &P, hipStream_t s)
+{
+    const dim3 grid(P.row_blocks * P.E);
     if (P.tokl == 8)
-        dispatch_q<8>(P, blk, rb, r0, Me, smem);
+        hipLaunchKernelGGL((gemm_kernel<KIND, 8>), grid, dim3(kThreads), 0, s, P);
     else
-        dispatch_q<16>(P, blk, rb, r0, Me, smem);
+        hipLaunchKernelGGL((gemm_kernel<KIND, 16>), grid, dim3(kThreads), 0, s, P);
 }
 
 }  // namespace
@@ -525,15 +537,16 @@ hipError_t launch_gemm(const DevBlock *table, int kind, int E, int N, int K, int
     P.plane_bytes = (uint32_t)(tiled_plane_words(N, K) * 4);
     P.max_rows = kDecodeMaxRows;
     // A token is routed to an expert at most once, so no expert has more rows than the
-    // batch has tokens (R / topk); the token buffers hold 8 or 16 rows, and an expert
-    // with more takes further passes over its weights.
+    // batch has tokens (R / topk).  The token buffers hold 8 rows up to 16 tokens (40 KB
+    // of LDS: four workgroups per CU; with 16 tokens spread over the experts few have
+    // more than 8) and 16 rows above (48 KB, three workgroups); an expert with more rows
+    // than the buffers takes further passes over its weights.
     const int tokens = topk > 0 ? R / topk : R;
-    P.tokl = tokens <= 8 ? 8 : 16;
-    const size_t lds = kLutBytes + std::max<size_t>(kRedBytes, 2 * 2 * (size_t)P.tokl * kXRowBytes);
+    P.tokl = tokens <= 16 ? 8 : 16;
     if (kind == APMOE_GATE_UP)
-        hipLaunchKernelGGL(gemm_kernel<APMOE_GATE_UP>, dim3(P.row_blocks * E), dim3(kThreads), lds, s, P);
+        launch_kind<APMOE_GATE_UP>(P, s);
     else
-        hipLaunchKernelGGL(gemm_kernel<APMOE_DOWN>, dim3(P.row_blocks * E), dim3(kThreads), lds, s, P);
+        launch_kind<APMOE_DOWN>(P, s);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || R <= kDecodeMaxRows)
         return err;  // no expert can have more rows than the decode product takes
