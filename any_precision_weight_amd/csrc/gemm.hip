@@ -7,17 +7,26 @@
 //   out[r][n] = sum_c in_row(r)[c] * LUT_q[n][code_q(n, c)],  fp32 accumulation,
 //   code_q(n, c) = bits of planes 0..q-1 at column c, plane 0 most significant.
 //
-// Workgroup = 2 x kParts waves = 64 weight rows of one expert.  Wave w covers rows
-// 32*(w&1) .. +31 and every kParts-th 128-column step (w>>1 picks the column part);
+// Workgroup = 2 x KP waves = 64 weight rows of one expert.  Wave w covers rows
+// 32*(w&1) .. +31 and every KP-th 128-column step (w>>1 picks the column part);
 // the parts are summed through LDS at the end in a fixed order.  Planes are read in the tiled layout
 // (32-row x 128-column tiles of 512 bytes, one tile per wave step and plane).  For
 // each step a lane loads, for its row, two words (64 columns) of each of the q
 // needed planes (only planes p < q are touched), turns them into 8-bit codes with an 8x8 bit transpose, looks the
 // codes up in the row's LUT level q staged in LDS, and feeds the fp16 centroids as
-// the A operand of v_mfma_f32_32x32x16_f16 against up to 32 tokens (B operand).
+// the A operand of v_mfma_f32_32x32x16_f16 against the expert's tokens (B operand).
 // The reduction over columns is a sum, so the order in which columns are assigned
 // to MFMA k-slots is free as long as A and B agree.  Plane words of the next step
-// and B fragments of the next word are requested ahead of use.
+// are requested one step ahead.
+//
+// Token rows reach the B operand through LDS.  A workgroup step is one step of each
+// column part; its token tile (2 parts x TOKL token rows x 128 columns, fp16) is
+// copied global -> LDS by buffer_load ... lds one step ahead into a second buffer,
+// and the four waves share it, so each token chunk is requested once per workgroup
+// instead of once per wave with 64 scattered 16-byte pieces per request.  A step ends
+// with a wait for the token copy and a workgroup barrier.  Token row jb stores its
+// 16-byte chunk c at position c ^ jb, so 16 lanes reading one chunk of 16 rows hit
+// distinct banks.
 //
 // LDS LUT layout: the transposed code byte v has bit p = plane p's bit, i.e. v is
 // the q-bit code with its bits reversed; entry LUT_q[n][code] is stored at
@@ -34,13 +43,15 @@ namespace apmoe {
 namespace {
 
 constexpr int kWave = 64;
-constexpr int kParts = 2;                  // column parts of a workgroup (waves: 2 row tiles x kParts)
-constexpr int kThreads = 2 * kParts * 64;
+// KP: column parts of a workgroup (waves: 2 row tiles x KP), 2 or 4
+template <int KP>
+constexpr int kThreadsOf = 2 * KP * 64;
 constexpr int kRows = kGemmRowsPerBlock;  // 64
 constexpr int kStepCols = 128;            // columns per wave step (2 lane halves x 64)
 constexpr int kTokTile = 32;
 constexpr int kLutBytes = 32 * 1024;                       // LUT region, every q
-constexpr int kRedBytes = (kParts - 1) * 2 * 16 * kWave * sizeof(float);  // column-part reduction
+template <int KP>
+constexpr int kRedBytesOf = (KP - 1) * 2 * 16 * kWave * sizeof(float);  // column-part reduction
 constexpr int kXRowBytes = kStepCols * 2;                   // one token row of one step (fp16)
 constexpr uint32_t kNoWord = 0x20000000u;  // plane word offset past every plane (byte offset 2^31)
 // s_waitcnt operands (vmcnt in bits 3:0 and 15:14, expcnt 6:4 left open, lgkmcnt 11:8)
@@ -206,14 +217,14 @@ __device__ inline void group_product(const u32x2 (&w)[Q], const uint32_t (&xaddr
 // in the file header; q = 3 as the pair table).  first_loads() runs once the LUT
 // requests are out and before their data is written, so the caller's first weight
 // requests overlap the LUT's latency.
-template <int Q, typename F>
+template <int Q, int KP, typename F>
 __device__ __attribute__((always_inline)) inline void stage_lut(const __amdgpu_buffer_rsrc_t rl, int nA, int nB,
                                                                 int N, int tid, char *smem, F &&first_loads)
 {
     if constexpr (Q == 3) {
         // pair table of LUT_3: entry (row 32t+i, pair code v) at v*256 + 128t + 4i;
         // thread -> row tid % 64 and kPairsPer of the 64 pair codes
-        constexpr int kPairsPer = 64 / (kThreads / kRows);
+        constexpr int kPairsPer = 64 / (kThreadsOf<KP> / kRows);
         const int nl = tid % kRows, part = tid / kRows;
         const int n = (nl < 32 ? nA : nB) + (nl & 31);
         const u32x4 lv = n < N ? __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
@@ -232,14 +243,14 @@ __device__ __attribute__((always_inline)) inline void stage_lut(const __amdgpu_b
     } else {
         // 16-byte loads (8 entries of one row), lane -> row so that one wave touches 64 rows
         constexpr int kLutU4 = (kRows << Q) / 8;
-        constexpr int kPer = (kLutU4 + kThreads - 1) / kThreads;
+        constexpr int kPer = (kLutU4 + kThreadsOf<KP> - 1) / kThreadsOf<KP>;
         constexpr int kBatch = kPer < 4 ? kPer : 4;  // loads in flight per batch (register budget)
 #pragma unroll
         for (int j0 = 0; j0 < kPer; j0 += kBatch) {
             u32x4 lv[kBatch];
 #pragma unroll
             for (int jj = 0; jj < kBatch; ++jj) {
-                const int idx = tid + (j0 + jj) * kThreads;
+                const int idx = tid + (j0 + jj) * kThreadsOf<KP>;
                 const int nl = idx % kRows, ch = idx / kRows;
                 const int n = (nl < 32 ? nA : nB) + (nl & 31);
                 const bool ok = idx < kLutU4 && n < N;
@@ -251,7 +262,7 @@ __device__ __attribute__((always_inline)) inline void stage_lut(const __amdgpu_b
                 first_loads();
 #pragma unroll
             for (int jj = 0; jj < kBatch; ++jj) {
-                const int idx = tid + (j0 + jj) * kThreads;
+                const int idx = tid + (j0 + jj) * kThreadsOf<KP>;
                 if (idx >= kLutU4)
                     break;
                 const int nl = idx % kRows, ch = idx / kRows;
@@ -272,7 +283,7 @@ __device__ __attribute__((always_inline)) inline void stage_lut(const __amdgpu_b
     }
 }
 
-template <int Q, int TOKL>
+template <int Q, int TOKL, int KP>
 __device__ void gemm_block(const GemmParams &P, const DevBlock &blk, int rb, int r0, int Me, char *smem)
 {
     const int tid = threadIdx.x;
@@ -287,7 +298,7 @@ __device__ void gemm_block(const GemmParams &P, const DevBlock &blk, int rb, int
     const int nB = P.act ? (N >> 1) + 32 * rb : rb * kRows + 32;
     const int nt = t ? nB : nA;  // this wave's tile
     const int nsteps = K / kStepCols;  // K % 128 == 0
-    // a part past the last step (K < 128 kParts) must not touch planes or token rows at all
+    // a part past the last step (K < 128 KP) must not touch planes or token rows at all
     const bool has_steps = part < nsteps;
     // tiled planes: tile (rt, kt) = rows 32rt.., columns 128kt.., 128 words; this lane
     // reads words 2*lane, 2*lane+1 of each tile.  A row tile past the end (N % 64 in
@@ -295,7 +306,7 @@ __device__ void gemm_block(const GemmParams &P, const DevBlock &blk, int rb, int
     const int RT = (N + 31) / 32, KT = K / kStepCols;
     const int rt = nt / 32;
     const uint32_t lane_word = ((uint32_t)(rt < RT ? rt : 0) * (uint32_t)KT + (uint32_t)part) * 128u + 2u * lane;
-    constexpr uint32_t kNextWords = kParts * 128;  // this wave's next step: kParts tiles on
+    constexpr uint32_t kNextWords = KP * 128;  // this wave's next step: KP tiles on
     __amdgpu_buffer_rsrc_t rs[Q];
 #pragma unroll
     for (int p = 0; p < Q; ++p)
@@ -307,7 +318,7 @@ __device__ void gemm_block(const GemmParams &P, const DevBlock &blk, int rb, int
     // buffer (zeros, no memory traffic), and it still takes part in the barriers
     const uint32_t first_word = has_steps ? lane_word : kNoWord;
     u32x2 wc[Q];
-    stage_lut<Q>(rl, nA, nB, N, tid, smem, [&] { load_planes<Q>(wc, rs, first_word); });
+    stage_lut<Q, KP>(rl, nA, nB, N, tid, smem, [&] { load_planes<Q>(wc, rs, first_word); });
     __syncthreads();
 
     // LDS byte addresses (compile-time constants for the static array)
@@ -318,21 +329,20 @@ __device__ void gemm_block(const GemmParams &P, const DevBlock &blk, int rb, int
     char *xs = smem + kLutBytes;
     const uint32_t xs_base = lds_base + kLutBytes;
     float *red = reinterpret_cast<float *>(xs);  // used after the last token tile is read
-    constexpr int kXBuf = 2 * TOKL * kXRowBytes;  // one token buffer: 2 parts x TOKL rows
-    constexpr int kDma = TOKL / 8;                // token copies per wave and workgroup step
-    const int nws = (nsteps + 1) / 2;              // workgroup steps: part p takes step 2s + p
-    static_assert(kParts == 2, "token tiles and workgroup steps assume two column parts");
+    constexpr int kXBuf = KP * TOKL * kXRowBytes;  // one token buffer: KP parts x TOKL rows
+    constexpr int kDma = TOKL / 8;                 // token copies per wave and workgroup step
+    const int nws = (nsteps + KP - 1) / KP;         // workgroup steps: part p takes step KP s + p
 
     for (int tp = 0; tp < Me; tp += TOKL) {
         const int j = lane & 31;  // token column of this lane in the B operand and in D
         const bool tok_ok = j < TOKL && tp + j < Me;
-        // token copies: instruction u = wave + 4k fills rows 4u .. 4u+3 of a buffer; lane L
+        // token copies: instruction u = wave + 2 KP k fills rows 4u .. 4u+3 of a buffer; lane L
         // writes 16-byte position L % 16 of row 4u + L / 16 (part row / TOKL, token row
         // % TOKL) and fetches the chunk stored there, chunk = position ^ token row
         uint32_t doff[kDma];
 #pragma unroll
         for (int k = 0; k < kDma; ++k) {
-            const int row = 4 * (wave + 4 * k) + (lane >> 4);
+            const int row = 4 * (wave + 2 * KP * k) + (lane >> 4);
             const int pu = row / TOKL, jj = row % TOKL;
             const int c = (lane & 15) ^ jj;
             const int tok = tp + jj;
@@ -340,14 +350,14 @@ __device__ void gemm_block(const GemmParams &P, const DevBlock &blk, int rb, int
             // rows past the expert's last token request an offset beyond the buffer
             doff[k] = tok < Me ? ((uint32_t)src * (uint32_t)K + (uint32_t)(pu * kStepCols + 8 * c)) * 2u : 0x80000000u;
         }
-        // token tile of workgroup step s (columns 256 s .. +255) into buffer b; the step
-        // is part of the lane offset, so the buffer's range check covers it
+        // token tile of workgroup step s (columns 128 KP s .. +128 KP - 1) into buffer b;
+        // the step is part of the lane offset, so the buffer's range check covers it
         auto copy_tokens = [&](int s, int b) {
 #pragma unroll
             for (int k = 0; k < kDma; ++k)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rx, (__attribute__((address_space(3))) void *)(xs + b * kXBuf + 1024 * (wave + 4 * k)), 16,
-                    doff[k] + (uint32_t)s * (2u * kStepCols * 2u), 0, 0, 0);
+                    rx, (__attribute__((address_space(3))) void *)(xs + b * kXBuf + 1024 * (wave + 2 * KP * k)),
+                    16, doff[k] + (uint32_t)s * (uint32_t)(KP * kStepCols * 2), 0, 0, 0);
         };
         // B-operand addresses in buffer 0: fragment f of word W is chunk 8g + 4W + f of this
         // lane's token row in its part; lanes of token columns >= TOKL repeat a row (their
@@ -374,12 +384,12 @@ __device__ void gemm_block(const GemmParams &P, const DevBlock &blk, int rb, int
         // and pass the barrier that frees the buffer just read
         auto step_body = [&](const u32x2 (&cur)[Q], u32x2 (&nxt)[Q], int s, auto buf) {
             constexpr int B = decltype(buf)::value;
-            const int step = 2 * s + part;
+            const int step = KP * s + part;
             // the wait below counts on the plane requests being issued after the token
             // copies: keep the scheduler from reordering them
             copy_tokens(s + 1 < nws ? s + 1 : s, B ^ 1);
             __builtin_amdgcn_sched_barrier(0);
-            word = step + kParts < nsteps ? word + kNextWords : kNoWord;
+            word = step + KP < nsteps ? word + kNextWords : kNoWord;
             load_planes<Q>(nxt, rs, word);
             __builtin_amdgcn_sched_barrier(0);
             if (step < nsteps) {
@@ -416,7 +426,7 @@ __device__ void gemm_block(const GemmParams &P, const DevBlock &blk, int rb, int
         __syncthreads();
         if (part == 0) {
 #pragma unroll
-            for (int p = 1; p < kParts; ++p)
+            for (int p = 1; p < KP; ++p)
 #pragma unroll
                 for (int v = 0; v < 16; ++v)
                     acc[v] += red[slot(p, t, v)];
@@ -465,17 +475,17 @@ __device__ void gemm_block(const GemmParams &P, const DevBlock &blk, int rb, int
     }
 }
 
-template <int TOKL>
+template <int TOKL, int KP>
 __device__ __attribute__((always_inline)) inline void dispatch_q(const GemmParams &P, const DevBlock &blk, int rb,
                                                                  int r0, int Me, char *smem)
 {
     switch (blk.q) {
-    case 3: gemm_block<3, TOKL>(P, blk, rb, r0, Me, smem); break;
-    case 4: gemm_block<4, TOKL>(P, blk, rb, r0, Me, smem); break;
-    case 5: gemm_block<5, TOKL>(P, blk, rb, r0, Me, smem); break;
-    case 6: gemm_block<6, TOKL>(P, blk, rb, r0, Me, smem); break;
-    case 7: gemm_block<7, TOKL>(P, blk, rb, r0, Me, smem); break;
-    case 8: gemm_block<8, TOKL>(P, blk, rb, r0, Me, smem); break;
+    case 3: gemm_block<3, TOKL, KP>(P, blk, rb, r0, Me, smem); break;
+    case 4: gemm_block<4, TOKL, KP>(P, blk, rb, r0, Me, smem); break;
+    case 5: gemm_block<5, TOKL, KP>(P, blk, rb, r0, Me, smem); break;
+    case 6: gemm_block<6, TOKL, KP>(P, blk, rb, r0, Me, smem); break;
+    case 7: gemm_block<7, TOKL, KP>(P, blk, rb, r0, Me, smem); break;
+    case 8: gemm_block<8, TOKL, KP>(P, blk, rb, r0, Me, smem); break;
     default: break;  // unreachable: commit validates q
     }
 }
@@ -483,13 +493,14 @@ __device__ __attribute__((always_inline)) inline void dispatch_q(const GemmParam
 // KIND (APMOE_GATE_UP / APMOE_DOWN) only names the launch, so profiles tell them apart.
 // The LDS region is a static array (its address is a compile-time constant, so LUT
 // gathers need no base add): LUT, then the token buffers, which the part sums reuse.
-template <int TOKL>
-constexpr int kLdsBytes = kLutBytes + (kRedBytes > 4 * TOKL * kXRowBytes ? kRedBytes : 4 * TOKL * kXRowBytes);
+template <int TOKL, int KP>
+constexpr int kLdsBytes = kLutBytes + (kRedBytesOf<KP> > 2 * KP * TOKL * kXRowBytes ? kRedBytesOf<KP>
+                                                                                    : 2 * KP * TOKL * kXRowBytes);
 
-template <int KIND, int TOKL>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) gemm_kernel(GemmParams P)
+template <int KIND, int TOKL, int KP>
+__global__ void __launch_bounds__(kThreadsOf<KP>) __attribute__((amdgpu_waves_per_eu(3))) gemm_kernel(GemmParams P)
 {
-    __shared__ __attribute__((aligned(16))) char smem[kLdsBytes<TOKL>];
+    __shared__ __attribute__((aligned(16))) char smem[kLdsBytes<TOKL, KP>];
     const int e = blockIdx.x % P.E;
     const int rb = blockIdx.x / P.E;
     const int r0 = P.offsets[e];
@@ -497,17 +508,17 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
     if (Me <= 0 || Me > P.max_rows)
         return;  // expert without tokens (no weight reads), or one for the tile product
     const DevBlock blk = P.table[2 * e + P.kind];
-    dispatch_q<TOKL>(P, blk, rb, r0, Me, smem);
+    dispatch_q<TOKL, KP>(P, blk, rb, r0, Me, smem);
 }
 
-template <int KIND>
+template <int KIND, int KP>
 void launch_kind(const GemmParams &P, hipStream_t s)
 {
     const dim3 grid(P.row_blocks * P.E);
     if (P.tokl == 8)
-        hipLaunchKernelGGL((gemm_kernel<KIND, 8>), grid, dim3(kThreads), 0, s, P);
+        hipLaunchKernelGGL((gemm_kernel<KIND, 8, KP>), grid, dim3(kThreadsOf<KP>), 0, s, P);
     else
-        hipLaunchKernelGGL((gemm_kernel<KIND, 16>), grid, dim3(kThreads), 0, s, P);
+        hipLaunchKernelGGL((gemm_kernel<KIND, 16, KP>), grid, dim3(kThreadsOf<KP>), 0, s, P);
 }
 
 }  // namespace
@@ -543,10 +554,13 @@ hipError_t launch_gemm(const DevBlock *table, int kind, int E, int N, int K, int
     // than the buffers takes further passes over its weights.
     const int tokens = topk > 0 ? R / topk : R;
     P.tokl = tokens <= 16 ? 8 : 16;
+    // Few workgroups (the down product's N / 64 row blocks) leave two per CU: four
+    // column parts then give each CU four waves per SIMD instead of two.
+    const bool wide = (long)P.row_blocks * E <= 4 * 256;
     if (kind == APMOE_GATE_UP)
-        launch_kind<APMOE_GATE_UP>(P, s);
+        wide ? launch_kind<APMOE_GATE_UP, 4>(P, s) : launch_kind<APMOE_GATE_UP, 2>(P, s);
     else
-        launch_kind<APMOE_DOWN>(P, s);
+        wide ? launch_kind<APMOE_DOWN, 4>(P, s) : launch_kind<APMOE_DOWN, 2>(P, s);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || R <= kDecodeMaxRows)
         return err;  // no expert can have more rows than the decode product takes
