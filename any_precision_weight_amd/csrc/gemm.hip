@@ -49,6 +49,7 @@ constexpr int kThreadsOf = 2 * KP * 64;
 constexpr int kRows = kGemmRowsPerBlock;  // 64
 constexpr int kStepCols = 128;            // columns per wave step (2 lane halves x 64)
 constexpr int kTokTile = 32;
+constexpr int kXcds = 8;                  // accelerator complex dies; workgroup b runs on XCD b % 8
 constexpr int kLutBytes = 32 * 1024;                       // LUT region, every q
 template <int KP>
 constexpr int kRedBytesOf = (KP - 1) * 2 * 16 * kWave * sizeof(float);  // column-part reduction
@@ -501,8 +502,16 @@ template <int KIND, int TOKL, int KP>
 __global__ void __launch_bounds__(kThreadsOf<KP>) __attribute__((amdgpu_waves_per_eu(3))) gemm_kernel(GemmParams P)
 {
     __shared__ __attribute__((aligned(16))) char smem[kLdsBytes<TOKL, KP>];
-    const int e = blockIdx.x % P.E;
-    const int rb = blockIdx.x / P.E;
+    // Workgroup b runs on XCD b % 8.  XCD x takes the x-th eighth of the work items and
+    // consecutive work items cycle over the experts, so every XCD streams an equal share
+    // of every expert's rows.  (With e = b % E and E = 8, each expert would run on one
+    // XCD, and the launch would wait for the XCD with the most planes or token passes.)
+    const int per = (int)gridDim.x / kXcds;
+    const int w = (int)(blockIdx.x % kXcds) * per + (int)(blockIdx.x / kXcds);
+    if (w >= P.row_blocks * P.E)
+        return;  // grid padding to a multiple of the XCD count
+    const int e = w % P.E;
+    const int rb = w / P.E;
     const int r0 = P.offsets[e];
     const int Me = P.offsets[e + 1] - r0;
     if (Me <= 0 || Me > P.max_rows)
@@ -514,7 +523,7 @@ __global__ void __launch_bounds__(kThreadsOf<KP>) __attribute__((amdgpu_waves_pe
 template <int KIND, int KP>
 void launch_kind(const GemmParams &P, hipStream_t s)
 {
-    const dim3 grid(P.row_blocks * P.E);
+    const dim3 grid((P.row_blocks * P.E + kXcds - 1) / kXcds * kXcds);
     if (P.tokl == 8)
         hipLaunchKernelGGL((gemm_kernel<KIND, 8, KP>), grid, dim3(kThreadsOf<KP>), 0, s, P);
     else
