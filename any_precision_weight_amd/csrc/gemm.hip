@@ -520,6 +520,340 @@ __global__ void __launch_bounds__(kThreadsOf<KP>) __attribute__((amdgpu_waves_pe
     dispatch_q<TOKL, KP>(P, blk, rb, r0, Me, smem);
 }
 
+// ---------------------------------------------------------------------------
+// Mid product: experts with kDecodeMaxRows + 1 .. kMidMaxRows rows (33..64: experts
+// of a skewed decode batch, shared experts of a small batch).  Same result as the
+// decode product.  Each weight is decoded once per expert and its fp16 centroids stay
+// in registers as the A operand of two MFMAs, one per 32-token tile of the expert.
+// (Four token tiles, for experts up to 128 rows, measured slower than the tile
+// product there: with one workgroup per CU the waves are bound by LDS latency.)
+//
+// Workgroup = 8 waves = 128 weight rows (four 32-row tiles) of one expert.  Wave w
+// takes row tile w % 4 and word w / 4 of every 128-column step (lane slot 32g + i of
+// the tiled layout holds row i's columns 64g .. 64g + 63 in two words), so the two
+// waves of a row tile split its columns and are summed through LDS at the end in a
+// fixed order.  All eight waves read the same token tile, which is copied global ->
+// LDS by buffer_load ... lds one step ahead into the second of two buffers.
+//
+// LDS (112 KB, one workgroup per CU, two waves per SIMD):
+//   [0, 64 KB)    LUT level q of the 128 rows: entry (row nl, code) at
+//                 v*256 + 4*(nl % 64) + 2*(nl / 64), v = the code with its q bits
+//                 reversed (the transposed code byte); one v_perm forms an address
+//                 for every q (v < 256, lane constant < 256).  Within a 32-lane half
+//                 of a wave the 32 rows fall in 32 distinct banks.
+//   [64, 112 KB)  three token buffers of 64 rows x 128 columns fp16; token row r
+//                 stores its 16-byte chunk c at position c ^ (r % 16).
+// Step s requests the token tile of step s + 2 and the plane words of step s + 2,
+// so two steps of plane requests are in flight per wave: with one workgroup per CU
+// that many are needed to cover the memory latency.
+// ---------------------------------------------------------------------------
+constexpr int kMidWaves = 8;
+constexpr int kMidThreads = kMidWaves * kWave;
+constexpr int kMidRows = 128;                              // weight rows per workgroup
+constexpr int kMidLutBytes = 64 * 1024;
+constexpr int kMidTT = kMidMaxRows / kTokTile;             // token tiles (2)
+constexpr int kMidXBuf = kMidMaxRows * kXRowBytes;         // 16 KB token buffer
+constexpr int kMidNxb = 3;                                 // token buffers (steps in flight + 1)
+constexpr int kMidLds = kMidLutBytes + kMidNxb * kMidXBuf;  // 112 KB
+static_assert(kMidMaxRows % kTokTile == 0 && kMidTT <= 4, "whole 32-token tiles");
+
+// s_waitcnt with vmcnt up to 63 (bits 3:0 and 15:14), expcnt open, lgkmcnt 0
+template <int VM>
+constexpr int wait_vm63()
+{
+    static_assert(VM >= 0 && VM < 64, "vmcnt range");
+    return (VM & 15) | (7 << 4) | ((VM >> 4) << 14);
+}
+
+// One word of each needed plane (32 columns of the lane's row), non-temporal.
+template <int Q>
+__device__ inline void load_words(uint32_t (&w)[Q], const __amdgpu_buffer_rsrc_t (&rs)[Q], uint32_t word)
+{
+#pragma unroll
+    for (int p = 0; p < Q; ++p)
+        w[p] = __builtin_amdgcn_raw_buffer_load_b32(rs[p], (int)(word * 4u), 0, kLoadNT);
+}
+
+// One wave step: the lane's 32 weights (word `cur` of each plane) -> codes -> four
+// fp16 A fragments, each multiplied by the B fragments of TT token tiles.  With two
+// waves per SIMD the LDS latency must be hidden inside the wave: the lookups and B
+// fragments of k-group b + 2 are requested before k-group b multiplies.
+template <int Q, int TT, int XOFF>
+__device__ inline void mid_group(const uint32_t (&cur)[Q], const uint32_t (&xaddr)[4], uint32_t lut_base,
+                                 uint32_t lane_const, float16v (&acc)[TT])
+{
+    uint32_t d[8];
+#pragma unroll
+    for (int p = 0; p < 8; ++p)
+        d[p] = p < Q ? cur[p < Q ? p : 0] : 0u;
+    transpose8x8<Q == 8 || Q == 3>(d);
+    half8 a[4];
+    u32x4 xb[4][TT];
+    auto request = [&](auto bb) {
+        constexpr int b = decltype(bb)::value;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t addr = __builtin_amdgcn_perm(d[j], lane_const, 0x0C0C0000u | ((4u + b) << 8));
+            a[b][j] = *reinterpret_cast<const __attribute__((address_space(3))) _Float16 *>((uintptr_t)(lut_base + addr));
+        }
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt)
+            xb[b][tt] = lds_b128(xaddr[b] + (uint32_t)(XOFF + tt * kTokTile * kXRowBytes));
+    };
+    auto multiply = [&](auto bb) {
+        constexpr int b = decltype(bb)::value;
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt)
+            acc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[b], __builtin_bit_cast(half8, xb[b][tt]), acc[tt], 0, 0, 0);
+    };
+    request(std::integral_constant<int, 0>{});
+    request(std::integral_constant<int, 1>{});
+    __builtin_amdgcn_sched_barrier(0);
+    multiply(std::integral_constant<int, 0>{});
+    request(std::integral_constant<int, 2>{});
+    __builtin_amdgcn_sched_barrier(0);
+    multiply(std::integral_constant<int, 1>{});
+    request(std::integral_constant<int, 3>{});
+    __builtin_amdgcn_sched_barrier(0);
+    multiply(std::integral_constant<int, 2>{});
+    multiply(std::integral_constant<int, 3>{});
+}
+
+template <int Q, int TT>
+__device__ __attribute__((always_inline)) inline void mid_block(const GemmParams &P, const DevBlock &blk, int rb, int r0,
+                                                               int Me, char *smem)
+{
+    const int tid = threadIdx.x;
+    const int lane = tid % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int rt = wave & 3, W = wave >> 2;  // row tile, word of every step
+    const int i = lane & 31, g = lane >> 5, j = lane & 31;
+    const int N = P.N, K = P.K;
+    const int nsteps = K / kStepCols;
+    // first rows of the workgroup's two 64-row halves: consecutive, or with the
+    // activation fused, gate rows 64rb.. and the matching up rows F + 64rb..
+    const int rowA0 = P.act ? 64 * rb : kMidRows * rb;
+    const int rowB0 = P.act ? (N >> 1) + 64 * rb : kMidRows * rb + 64;
+    const int nt = (rt < 2 ? rowA0 : rowB0) + 32 * (rt & 1);  // this wave's row tile
+    // tiled planes: tile (rt, kt) = rows 32rt.., columns 128kt.., 128 words; this lane
+    // reads word 2*lane + W of each tile.  A row tile past the end reads tile row 0;
+    // its outputs are not written.
+    const int RT = (N + 31) / 32, rtg = nt / 32;
+    const uint32_t lane_word = (uint32_t)(rtg < RT ? rtg : 0) * (uint32_t)nsteps * 128u + 2u * lane + (uint32_t)W;
+    __amdgpu_buffer_rsrc_t rs[Q];
+#pragma unroll
+    for (int p = 0; p < Q; ++p)
+        rs[p] = make_rsrc(blk.plane[p], P.plane_bytes);
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(P.in, P.in_bytes);
+    const uint32_t lds_base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char *)smem);
+    char *xs = smem + kMidLutBytes;
+    const uint32_t xs_base = lds_base + kMidLutBytes;
+
+    // token copies: instruction u = wave + 8k fills rows 4u .. 4u+3 of a buffer; lane L
+    // writes 16-byte position L % 16 of row 4u + L / 16 and fetches the chunk stored
+    // there, chunk = position ^ (row % 16).  Rows past the expert's last token request
+    // an offset beyond the buffer (zeros, no memory traffic).
+    uint32_t doff[TT];
+#pragma unroll
+    for (int k = 0; k < TT; ++k) {
+        const int row = 4 * (wave + kMidWaves * k) + (lane >> 4);
+        const int c = (lane & 15) ^ (row & 15);
+        const int src = row < Me ? (P.gather ? P.perm[r0 + row] / P.topk : r0 + row) : 0;
+        doff[k] = row < Me ? ((uint32_t)src * (uint32_t)K + 8u * (uint32_t)c) * 2u : 0x80000000u;
+    }
+    auto copy_tokens = [&](int s, int b) {
+#pragma unroll
+        for (int k = 0; k < TT; ++k)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rx, (__attribute__((address_space(3))) void *)(xs + b * kMidXBuf + 1024 * (wave + kMidWaves * k)), 16,
+                doff[k] + (uint32_t)s * (uint32_t)(kStepCols * 2), 0, 0, 0);
+    };
+    // B fragment of k-group b in buffer 0, token tile 0: chunk 8g + 4W + b of token row j
+    uint32_t xaddr[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+        xaddr[b] = xs_base + (uint32_t)(j * kXRowBytes + (((8 * g + 4 * W + b) ^ (j & 15)) << 4));
+
+    // plane words of steps 0 and 1 and token tiles of steps 0 and 1 (clamped) first
+    uint32_t wr[kMidNxb][Q];
+    load_words<Q>(wr[0], rs, lane_word);
+    load_words<Q>(wr[1], rs, nsteps > 1 ? lane_word + 128u : kNoWord);
+    copy_tokens(0, 0);
+    copy_tokens(nsteps > 1 ? 1 : 0, 1);
+    // ---- LUT level Q of the 128 rows -> LDS (row pair (pr, pr + 64) shares a word) ----
+    {
+        const __amdgpu_buffer_rsrc_t rl = make_rsrc(blk.lut, (uint32_t)N << (Q + 1));
+        constexpr int kChunksPerRow = (1 << Q) / 8;  // 16-byte chunks of one LUT row
+        constexpr int kPairChunks = 64 * kChunksPerRow;
+        constexpr int kPer = (kPairChunks + kMidThreads - 1) / kMidThreads;
+#pragma unroll
+        for (int jj = 0; jj < kPer; ++jj) {
+            const int pc = tid + jj * kMidThreads;
+            if (pc < kPairChunks) {
+                const int pr = pc % 64, ch = pc / 64;
+                const int na = rowA0 + pr, nb = rowB0 + pr;
+                const u32x4 za = {0, 0, 0, 0};
+                const u32x4 la = na < N ? __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                                     rl, (int)((((uint32_t)na << Q) + 8u * ch) * 2u), 0, 0))
+                                        : za;
+                const u32x4 lb = nb < N ? __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                                     rl, (int)((((uint32_t)nb << Q) + 8u * ch) * 2u), 0, 0))
+                                        : za;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t lo = (la[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+                    const uint32_t hi = (lb[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+                    const uint32_t v = bitrev((uint32_t)(8 * ch + e), Q);
+                    *reinterpret_cast<uint32_t *>(smem + v * 256 + 4 * pr) = lo | (hi << 16);
+                }
+            }
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitAll);
+    __syncthreads();
+
+    const uint32_t lane_const = (uint32_t)(4 * (32 * (rt & 1) + i) + 2 * (rt >> 1));
+    float16v acc[TT];
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+            acc[tt][v] = 0.f;
+    // step s (plane set and token buffer s % 3): request the token tile and the plane
+    // words of step s + 2 (the token request first), multiply, then wait for the token
+    // tile of step s + 1 -- requested one step earlier, before the plane words of step
+    // s + 1, the token tile of step s + 2 and the plane words of step s + 2, which stay
+    // in flight -- and pass the barrier that frees buffer s % 3 for step s + 3
+    auto step_body = [&](int s, auto uu) {
+        constexpr int U = decltype(uu)::value;
+        constexpr int U2 = (U + 2) % kMidNxb;
+        const int s2 = s + U + 2;
+        copy_tokens(s2 < nsteps ? s2 : nsteps - 1, U2);
+        __builtin_amdgcn_sched_barrier(0);  // the wait below counts on this order
+        load_words<Q>(wr[U2], rs, s2 < nsteps ? lane_word + 128u * (uint32_t)s2 : kNoWord);
+        __builtin_amdgcn_sched_barrier(0);
+        mid_group<Q, TT, U * kMidXBuf>(wr[U], xaddr, lds_base, lane_const, acc);
+        __builtin_amdgcn_s_waitcnt(wait_vm63<2 * Q + TT>());
+        asm volatile("s_barrier" ::: "memory");
+    };
+    for (int s = 0; s < nsteps; s += kMidNxb) {
+        step_body(s, std::integral_constant<int, 0>{});
+        if (s + 1 >= nsteps)
+            break;
+        step_body(s, std::integral_constant<int, 1>{});
+        if (s + 2 >= nsteps)
+            break;
+        step_body(s, std::integral_constant<int, 2>{});
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitAll);  // the last (repeated) token copy has landed
+    __syncthreads();
+
+    // ---- sum the two words of each row tile (word 0 + word 1), write ---------------
+    float *red = reinterpret_cast<float *>(xs);
+    auto slot = [&](int r, int tt, int v) { return ((r * TT + tt) * 16 + v) * kWave + lane; };
+    if (W == 1) {
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                red[slot(rt, tt, v)] = acc[tt][v];
+    }
+    __syncthreads();
+    if (W == 0) {
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                acc[tt][v] += red[slot(rt, tt, v)];
+    }
+    // D layout of the 32x32 MFMA: column j = lane%32, row = 8*(v/4) + 4*(lane/32) + v%4
+    if (!P.act) {
+        if (W == 0) {
+            const int nleft = N - (nt + 4 * g);
+#pragma unroll
+            for (int tt = 0; tt < TT; ++tt) {
+                const int tok = kTokTile * tt + j;
+                if (tok < Me) {
+                    const size_t o0 = (size_t)(r0 + tok) * N + (size_t)(nt + 4 * g);
+                    float *of = reinterpret_cast<float *>(P.out) + o0;
+                    _Float16 *oh = reinterpret_cast<_Float16 *>(P.out) + o0;
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int d = 8 * (v >> 2) + (v & 3);
+                        if (d < nleft) {
+                            if (P.out_f32)
+                                of[d] = acc[tt][v];
+                            else
+                                oh[d] = (_Float16)acc[tt][v];
+                        }
+                    }
+                }
+            }
+        }
+    } else {
+        // the up waves (row tiles 2, 3) hand their fp16-rounded rows to the gate waves
+        // of the same rows (tiles 0, 1) through the LUT region, no longer read; the gate
+        // waves write a = SiLU(gate) * up for rows f = nt + 4g + 8(v/4) + v%4 < F
+        float *xch = reinterpret_cast<float *>(smem);
+        if (W == 0 && rt >= 2) {
+#pragma unroll
+            for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    xch[slot(rt - 2, tt, v)] = (float)(_Float16)acc[tt][v];
+        }
+        __syncthreads();
+        if (W == 0 && rt < 2) {
+#pragma unroll
+            for (int tt = 0; tt < TT; ++tt) {
+                const int tok = kTokTile * tt + j;
+                if (tok < Me) {
+                    _Float16 *oa = reinterpret_cast<_Float16 *>(P.out) + (size_t)(r0 + tok) * (size_t)(N >> 1) +
+                                   (size_t)(nt + 4 * g);
+#pragma unroll
+                    for (int v = 0; v < 16; ++v)
+                        oa[8 * (v >> 2) + (v & 3)] = silu_mul((_Float16)acc[tt][v], (_Float16)xch[slot(rt, tt, v)]);
+                }
+            }
+        }
+    }
+}
+
+template <int TT>
+__device__ __attribute__((always_inline)) inline void mid_dispatch_q(const GemmParams &P, const DevBlock &blk, int rb,
+                                                                     int r0, int Me, char *smem)
+{
+    switch (blk.q) {
+    case 3: mid_block<3, TT>(P, blk, rb, r0, Me, smem); break;
+    case 4: mid_block<4, TT>(P, blk, rb, r0, Me, smem); break;
+    case 5: mid_block<5, TT>(P, blk, rb, r0, Me, smem); break;
+    case 6: mid_block<6, TT>(P, blk, rb, r0, Me, smem); break;
+    case 7: mid_block<7, TT>(P, blk, rb, r0, Me, smem); break;
+    case 8: mid_block<8, TT>(P, blk, rb, r0, Me, smem); break;
+    default: break;  // unreachable: commit validates q
+    }
+}
+
+// P.row_blocks here counts 128-row blocks (with the activation fused: 64 gate rows
+// and their 64 up rows).  Experts outside 33..64 rows return at once.
+template <int KIND>
+__global__ void __launch_bounds__(kMidThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) gemm_mid_kernel(GemmParams P)
+{
+    __shared__ __attribute__((aligned(16))) char smem[kMidLds];
+    const int per = (int)gridDim.x / kXcds;
+    const int w = (int)(blockIdx.x % kXcds) * per + (int)(blockIdx.x / kXcds);
+    if (w >= P.row_blocks * P.E)
+        return;
+    const int e = w % P.E;
+    const int rb = w / P.E;
+    const int r0 = P.offsets[e];
+    const int Me = P.offsets[e + 1] - r0;
+    if (Me <= kDecodeMaxRows || Me > kMidMaxRows)
+        return;
+    const DevBlock blk = P.table[2 * e + P.kind];
+    mid_dispatch_q<kMidTT>(P, blk, rb, r0, Me, smem);
+}
+
 template <int KIND, int KP>
 void launch_kind(const GemmParams &P, hipStream_t s)
 {
@@ -573,6 +907,16 @@ hipError_t launch_gemm(const DevBlock *table, int kind, int E, int N, int K, int
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || R <= kDecodeMaxRows)
         return err;  // no expert can have more rows than the decode product takes
+    GemmParams M = P;
+    M.row_blocks = act ? (N / 2) / 64 : (N + kMidRows - 1) / kMidRows;
+    const dim3 mgrid((M.row_blocks * E + kXcds - 1) / kXcds * kXcds);
+    if (kind == APMOE_GATE_UP)
+        hipLaunchKernelGGL(gemm_mid_kernel<APMOE_GATE_UP>, mgrid, dim3(kMidThreads), 0, s, M);
+    else
+        hipLaunchKernelGGL(gemm_mid_kernel<APMOE_DOWN>, mgrid, dim3(kMidThreads), 0, s, M);
+    err = hipGetLastError();
+    if (err != hipSuccess || R <= kMidMaxRows)
+        return err;
     return launch_gemm_tile(table, kind, E, N, K, in, in_bytes, gather, perm, offsets, topk, out, out_f32, act, R, s);
 }
 

@@ -636,9 +636,9 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
 int tile_grid(int N, int E, int R)
 {
     const int NT = (N + kBN - 1) / kBN;
-    // sum over experts with more than kDecodeMaxRows rows of ceil(M_e / 256) is at
-    // most R / 256 + (number of such experts)
-    const int big = min(E, R / (kDecodeMaxRows + 1));
+    // sum over experts with more than kMidMaxRows rows of ceil(M_e / 256) is at most
+    // R / 256 + (number of such experts)
+    const int big = min(E, R / (kMidMaxRows + 1));
     const long long tiles = (long long)NT * (R / kBM + big);
     return (int)((tiles + kXcds - 1) / kXcds * kXcds);
 }
@@ -662,7 +662,7 @@ hipError_t launch_gemm_tile(const DevBlock *table, int kind, int E, int N, int K
     P.out_f32 = out_f32;
     P.act = act;
     P.NT = (N + kBN - 1) / kBN;  // with the activation fused: F / 64 tiles of 64 gate + 64 up rows
-    P.min_rows = kDecodeMaxRows;
+    P.min_rows = kMidMaxRows;
     P.in_bytes = (uint32_t)in_bytes;
     P.plane_bytes = (uint32_t)(tiled_plane_words(N, K) * 4);
     const int grid = tile_grid(N, E, R);

@@ -22,9 +22,11 @@ struct DevBlock {
 
 // Rows of the weight matrix handled by one workgroup of the decode product.
 constexpr int kGemmRowsPerBlock = 64;
-// Experts with at most this many rows use the decode product (one pass of 32 token
-// columns); larger ones use the MFMA tile product.
+// Experts with at most kDecodeMaxRows rows use the decode product (one pass of 32
+// token columns); up to kMidMaxRows the mid product (each weight decoded once, two
+// 32-token tiles); larger ones the MFMA tile product.
 constexpr int kDecodeMaxRows = 32;
+constexpr int kMidMaxRows = 64;
 
 // Expert activation of one (gate, up) pair of fp16 values: SiLU(g) * u with
 // SiLU(z) = z / (1 + e^-z), fp32 math (the hardware reciprocal, 1 ulp, instead of a

@@ -328,9 +328,10 @@ def test_gemm_non_gather_rows():
     tbl.close()
 
 
-# Experts above 32 rows take the MFMA tile product (128 weight rows x 256 rows per
+# Experts above 64 rows take the MFMA tile product (128 weight rows x 256 rows per
 # tile): several token tiles per expert with ragged tails, a weight-row tail, and
-# more than one group of 8 weight-row tiles.
+# more than one group of 8 weight-row tiles.  The smaller counts in these cases take
+# the decode and mid products in the same call.
 TILE_CASES = [
     (200, 384, [300, 0, 257, 33, 600, 64]),
     (112, 128, [40, 300, 0, 33, 1, 90]),  # K = 128: one step; N % 128 = 112
@@ -376,6 +377,64 @@ def test_gemm_tile_random_lut(out_dtype):
 def test_gemm_tile_non_gather_rows():
     N, K, counts = 136, 256, [70, 300, 0, 33, 1, 260]
     tbl, keep, P, L, offsets, perm, T = _gemm_setup(GEMM_QS, counts, N, K, True, 46)
+    R = int(offsets[-1])
+    a = RNG.integers(-2, 3, (R, K)).astype(np.float16)
+    got = _gemm_run(tbl, a, offsets, perm, R, N, apw.F16, gather=False)
+    for e, q in enumerate(GEMM_QS):
+        codes = oracle.unpack_codes(P[e], q).astype(np.int64)
+        ref = a[offsets[e]:offsets[e + 1]].astype(np.int64) @ codes.T
+        assert np.array_equal(got[offsets[e]:offsets[e + 1]].astype(np.float64), ref.astype(np.float16).astype(np.float64))
+    tbl.close()
+
+
+# Experts with 33..64 rows take the mid product (128 weight rows per workgroup, each
+# weight decoded once for two 32-token tiles): the boundaries 32 / 33 and 64 / 65
+# between the three products, weight-row tails (N % 128 of 72, 8 and 40), K = 128
+# (one step) and odd numbers of steps; the larger counts take the tile product in
+# the same call.
+MID_CASES = [
+    (200, 384, [33, 64, 65, 128, 129, 32]),
+    (136, 128, [128, 33, 0, 100, 1, 65]),
+    (40, 640, [64, 127, 33, 96, 50, 128]),
+    (256, 1152, [90, 33, 128, 0, 64, 70]),
+]
+
+
+@pytest.mark.parametrize("case", MID_CASES)
+def test_gemm_mid_identity_lut_exact(case):
+    N, K, counts = case
+    tbl, keep, P, L, offsets, perm, T = _gemm_setup(GEMM_QS, counts, N, K, True, 47)
+    x = RNG.integers(-2, 3, (T, K)).astype(np.float16)
+    got = _gemm_run(tbl, x, offsets, perm, T, N, apw.F32)
+    for e, q in enumerate(GEMM_QS):
+        rows = perm[offsets[e]:offsets[e + 1]]
+        codes = oracle.unpack_codes(P[e], q).astype(np.int64)
+        ref = x[rows].astype(np.int64) @ codes.T
+        assert np.array_equal(got[offsets[e]:offsets[e + 1]], ref.astype(np.float32)), (e, q, counts[e])
+    tbl.close()
+
+
+@pytest.mark.parametrize("out_dtype", [apw.F16, apw.F32])
+def test_gemm_mid_random_lut(out_dtype):
+    N, K, counts = 200, 640, [33, 64, 65, 128, 100, 40]
+    tbl, keep, P, L, offsets, perm, T = _gemm_setup(GEMM_QS, counts, N, K, False, 48)
+    x = synth.gen_aux_fp16(48, 0, T * K).reshape(T, K)
+    got = _gemm_run(tbl, x, offsets, perm, T, N, out_dtype).astype(np.float64)
+    for e, q in enumerate(GEMM_QS):
+        rows = perm[offsets[e]:offsets[e + 1]]
+        xin = x[rows].astype(np.float64)
+        ref = oracle.block_gemm(P[e], L[e], q, xin)
+        S = oracle.block_gemm(P[e], np.abs(L[e]), q, np.abs(xin))
+        acc = K * 2.0 ** -24 * S
+        tol = acc + (0.5 * ulp16(np.abs(ref) + acc) if out_dtype == apw.F16 else 0.0)
+        d = np.abs(got[offsets[e]:offsets[e + 1]] - ref)
+        assert np.all(d <= tol), (e, q, float((d - tol).max()))
+    tbl.close()
+
+
+def test_gemm_mid_non_gather_rows():
+    N, K, counts = 136, 256, [70, 128, 0, 33, 1, 64]
+    tbl, keep, P, L, offsets, perm, T = _gemm_setup(GEMM_QS, counts, N, K, True, 49)
     R = int(offsets[-1])
     a = RNG.integers(-2, 3, (R, K)).astype(np.float16)
     got = _gemm_run(tbl, a, offsets, perm, R, N, apw.F16, gather=False)
@@ -473,11 +532,12 @@ def test_layer_shared_experts(T, renorm):
 
 
 @pytest.mark.parametrize("q", [3, 4, 5, 6, 7, 8])
-@pytest.mark.parametrize("T", [8, 150])
+@pytest.mark.parametrize("T", [8, 100, 600])
 def test_gemm_act_matches_two_steps(T, q):
-    """The activation fused into the gate_up epilogue (decode product at T = 8, tile
-    product for experts above 32 rows at T = 150) gives exactly the bits of gate_up to
-    fp16 h followed by the activation launch."""
+    """The activation fused into the gate_up epilogue (decode product at T = 8, mid
+    product for experts of 33..64 rows at T = 100, tile product above 64 rows at
+    T = 600) gives exactly the bits of gate_up to fp16 h followed by the activation
+    launch."""
     cfg = synth.CONFIGS[0]
     L = Layer(cfg, T=T, qmap=np.full((cfg.weight_experts, 2), q, np.int32))
     o = L.run()
