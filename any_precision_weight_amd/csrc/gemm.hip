@@ -124,7 +124,8 @@ struct GemmParams {
     void *out;
     int kind, E, N, K, topk, gather, out_f32, row_blocks;
     int act;               // gate_up with the activation fused: out = a [rows][N/2] fp16
-    int max_rows;          // experts with more rows belong to the tile product
+    int max_rows;          // decode product: experts with more rows belong to the mid / tile products
+    int min_rows;          // mid product: experts with at most this many rows belong to the decode product
     int tokl;              // token rows per pass (8 or 16): the LDS token buffers' size
     uint32_t in_bytes;     // bytes of `in` (buffer range of the B-operand loads)
     uint32_t plane_bytes;  // bytes of one tiled plane
@@ -835,7 +836,8 @@ __device__ __attribute__((always_inline)) inline void mid_dispatch_q(const GemmP
 }
 
 // P.row_blocks here counts 128-row blocks (with the activation fused: 64 gate rows
-// and their 64 up rows).  Experts outside 33..64 rows return at once.
+// and their 64 up rows).  Experts outside P.min_rows + 1 .. kMidMaxRows rows return
+// at once.
 template <int KIND>
 __global__ void __launch_bounds__(kMidThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) gemm_mid_kernel(GemmParams P)
 {
@@ -848,7 +850,7 @@ __global__ void __launch_bounds__(kMidThreads) __attribute__((amdgpu_waves_per_e
     const int rb = w / P.E;
     const int r0 = P.offsets[e];
     const int Me = P.offsets[e + 1] - r0;
-    if (Me <= kDecodeMaxRows || Me > kMidMaxRows)
+    if (Me <= P.min_rows || Me > kMidMaxRows)
         return;
     const DevBlock blk = P.table[2 * e + P.kind];
     mid_dispatch_q<kMidTT>(P, blk, rb, r0, Me, smem);
@@ -889,14 +891,20 @@ hipError_t launch_gemm(const DevBlock *table, int kind, int E, int N, int K, int
     P.row_blocks = act ? (N / 2) / 32 : (N + kRows - 1) / kRows;
     P.in_bytes = (uint32_t)in_bytes;
     P.plane_bytes = (uint32_t)(tiled_plane_words(N, K) * 4);
-    P.max_rows = kDecodeMaxRows;
     // A token is routed to an expert at most once, so no expert has more rows than the
-    // batch has tokens (R / topk).  The token buffers hold 8 rows up to 16 tokens (40 KB
-    // of LDS: four workgroups per CU; with 16 tokens spread over the experts few have
-    // more than 8) and 16 rows above (48 KB, three workgroups); an expert with more rows
-    // than the buffers takes further passes over its weights.
+    // batch has tokens (R / topk; a shared expert has exactly that many).  The token
+    // buffers hold 8 rows up to 16 tokens (40 KB of LDS: four workgroups per CU; with 16
+    // tokens spread over the experts few have more than 8) and 16 rows above (48 KB,
+    // three workgroups); an expert with more rows than the buffers takes further passes
+    // over its weights.  The decode product takes experts with up to kDecodeMaxRows
+    // rows, the mid product those up to kMidMaxRows, the tile product the rest; the
+    // launches that no expert can need (by the token count) are skipped.  (Giving the
+    // mid product the experts of 17..32 rows, one pass instead of two, measured slower
+    // on a skewed 256-token batch.)
     const int tokens = topk > 0 ? R / topk : R;
     P.tokl = tokens <= 16 ? 8 : 16;
+    P.max_rows = kDecodeMaxRows;
+    P.min_rows = 0;
     // Few workgroups (the down product's N / 64 row blocks) leave two per CU: four
     // column parts then give each CU four waves per SIMD instead of two.
     const bool wide = (long)P.row_blocks * E <= 4 * 256;
@@ -905,9 +913,10 @@ hipError_t launch_gemm(const DevBlock *table, int kind, int E, int N, int K, int
     else
         wide ? launch_kind<APMOE_DOWN, 4>(P, s) : launch_kind<APMOE_DOWN, 2>(P, s);
     hipError_t err = hipGetLastError();
-    if (err != hipSuccess || R <= kDecodeMaxRows)
+    if (err != hipSuccess || tokens <= P.max_rows)
         return err;  // no expert can have more rows than the decode product takes
     GemmParams M = P;
+    M.min_rows = P.max_rows;
     M.row_blocks = act ? (N / 2) / 64 : (N + kMidRows - 1) / kMidRows;
     const dim3 mgrid((M.row_blocks * E + kXcds - 1) / kXcds * kXcds);
     if (kind == APMOE_GATE_UP)
@@ -915,7 +924,7 @@ hipError_t launch_gemm(const DevBlock *table, int kind, int E, int N, int K, int
     else
         hipLaunchKernelGGL(gemm_mid_kernel<APMOE_DOWN>, mgrid, dim3(kMidThreads), 0, s, M);
     err = hipGetLastError();
-    if (err != hipSuccess || R <= kMidMaxRows)
+    if (err != hipSuccess || tokens <= kMidMaxRows)
         return err;
     return launch_gemm_tile(table, kind, E, N, K, in, in_bytes, gather, perm, offsets, topk, out, out_f32, act, R, s);
 }

@@ -22,9 +22,9 @@ struct DevBlock {
 
 // Rows of the weight matrix handled by one workgroup of the decode product.
 constexpr int kGemmRowsPerBlock = 64;
-// Experts with at most kDecodeMaxRows rows use the decode product (one pass of 32
-// token columns); up to kMidMaxRows the mid product (each weight decoded once, two
-// 32-token tiles); larger ones the MFMA tile product.
+// Experts with at most kDecodeMaxRows rows use the decode product (one or two passes
+// of its token buffers); up to kMidMaxRows the mid product (each weight decoded once
+// for two 32-token tiles); larger ones the MFMA tile product.
 constexpr int kDecodeMaxRows = 32;
 constexpr int kMidMaxRows = 64;
 

@@ -295,6 +295,23 @@ def test_gemm_identity_lut_exact(NK):
     tbl.close()
 
 
+@pytest.mark.parametrize("counts", [[9, 1, 0, 3, 2, 1], [0, 1, 20, 3, 5, 3], [0, 0, 32, 0, 0, 0]])
+def test_gemm_decode_multipass_exact(counts):
+    """The decode product's token buffers hold 8 rows (batches up to 16 tokens) or 16
+    rows: an expert with more rows takes a second pass over its weights (9 rows of 16
+    tokens; 20 and 32 rows of 32 tokens)."""
+    N, K = 136, 384
+    tbl, keep, P, L, offsets, perm, T = _gemm_setup(GEMM_QS, counts, N, K, True, 50)
+    x = RNG.integers(-2, 3, (T, K)).astype(np.float16)
+    got = _gemm_run(tbl, x, offsets, perm, T, N, apw.F32)
+    for e, q in enumerate(GEMM_QS):
+        rows = perm[offsets[e]:offsets[e + 1]]
+        codes = oracle.unpack_codes(P[e], q).astype(np.int64)
+        ref = x[rows].astype(np.int64) @ codes.T
+        assert np.array_equal(got[offsets[e]:offsets[e + 1]], ref.astype(np.float32)), (e, q, counts[e])
+    tbl.close()
+
+
 @pytest.mark.parametrize("out_dtype", [apw.F16, apw.F32])
 def test_gemm_random_lut(out_dtype):
     N, K = 136, 384
@@ -390,13 +407,13 @@ def test_gemm_tile_non_gather_rows():
 # Experts with 33..64 rows take the mid product (128 weight rows per workgroup, each
 # weight decoded once for two 32-token tiles): the boundaries 32 / 33 and 64 / 65
 # between the three products, weight-row tails (N % 128 of 72, 8 and 40), K = 128
-# (one step) and odd numbers of steps; the larger counts take the tile product in
-# the same call.
+# (one step) and odd numbers of steps; the other counts take the decode product (one
+# or two passes) and the tile product in the same call.
 MID_CASES = [
-    (200, 384, [33, 64, 65, 128, 129, 32]),
+    (200, 384, [33, 64, 65, 16, 17, 32]),
     (136, 128, [128, 33, 0, 100, 1, 65]),
-    (40, 640, [64, 127, 33, 96, 50, 128]),
-    (256, 1152, [90, 33, 128, 0, 64, 70]),
+    (40, 640, [64, 127, 17, 96, 50, 16]),
+    (256, 1152, [90, 33, 128, 0, 64, 20]),
 ]
 
 
