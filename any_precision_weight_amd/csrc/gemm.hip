@@ -534,28 +534,35 @@ __global__ void __launch_bounds__(kThreadsOf<KP>) __attribute__((amdgpu_waves_pe
 // the tiled layout holds row i's columns 64g .. 64g + 63 in two words), so the two
 // waves of a row tile split its columns and are summed through LDS at the end in a
 // fixed order.  All eight waves read the same token tile, which is copied global ->
-// LDS by buffer_load ... lds one step ahead into the second of two buffers.
+// LDS by buffer_load ... lds.
 //
-// LDS (112 KB, one workgroup per CU, two waves per SIMD):
-//   [0, 64 KB)    LUT level q of the 128 rows: entry (row nl, code) at
+// LDS (112 KB: one workgroup per CU, two waves per SIMD; or, for launches with many
+// row blocks, 80 KB for the blocks at q <= 7 -- two workgroups per CU -- and a second
+// launch for those at q = 8):
+//   [0, L)        LUT level q of the 128 rows (L = 64 KB, or 32 KB for q <= 7 only): entry (row nl, code) at
 //                 v*256 + 4*(nl % 64) + 2*(nl / 64), v = the code with its q bits
 //                 reversed (the transposed code byte); one v_perm forms an address
 //                 for every q (v < 256, lane constant < 256).  Within a 32-lane half
 //                 of a wave the 32 rows fall in 32 distinct banks.
-//   [64, 112 KB)  three token buffers of 64 rows x 128 columns fp16; token row r
+//   [L, L + 48 KB) three token buffers of 64 rows x 128 columns fp16; token row r
 //                 stores its 16-byte chunk c at position c ^ (r % 16).
 // Step s requests the token tile of step s + 2 and the plane words of step s + 2,
-// so two steps of plane requests are in flight per wave: with one workgroup per CU
-// that many are needed to cover the memory latency.
+// so two steps of plane requests are in flight per wave.
 // ---------------------------------------------------------------------------
 constexpr int kMidWaves = 8;
 constexpr int kMidThreads = kMidWaves * kWave;
 constexpr int kMidRows = 128;                              // weight rows per workgroup
-constexpr int kMidLutBytes = 64 * 1024;
+// Launch modes: kMidAll takes every q with a 64 KB LUT region (112 KB of LDS: one
+// workgroup per CU); kMidLow takes q <= 7 with a 32 KB region (80 KB: two per CU) and
+// kMidQ8 the blocks at q = 8 (112 KB), as two launches.
+constexpr int kMidAll = 0, kMidLow = 1, kMidQ8 = 2;
+template <int MODE>
+constexpr int kMidLutBytes = MODE == kMidLow ? 32 * 1024 : 64 * 1024;
 constexpr int kMidTT = kMidMaxRows / kTokTile;             // token tiles (2)
 constexpr int kMidXBuf = kMidMaxRows * kXRowBytes;         // 16 KB token buffer
 constexpr int kMidNxb = 3;                                 // token buffers (steps in flight + 1)
-constexpr int kMidLds = kMidLutBytes + kMidNxb * kMidXBuf;  // 112 KB
+template <int MODE>
+constexpr int kMidLds = kMidLutBytes<MODE> + kMidNxb * kMidXBuf;
 static_assert(kMidMaxRows % kTokTile == 0 && kMidTT <= 4, "whole 32-token tiles");
 
 // s_waitcnt with vmcnt up to 63 (bits 3:0 and 15:14), expcnt open, lgkmcnt 0
@@ -620,7 +627,7 @@ __device__ inline void mid_group(const uint32_t (&cur)[Q], const uint32_t (&xadd
     multiply(std::integral_constant<int, 3>{});
 }
 
-template <int Q, int TT>
+template <int Q, int TT, int MODE>
 __device__ __attribute__((always_inline)) inline void mid_block(const GemmParams &P, const DevBlock &blk, int rb, int r0,
                                                                int Me, char *smem)
 {
@@ -647,8 +654,8 @@ __device__ __attribute__((always_inline)) inline void mid_block(const GemmParams
         rs[p] = make_rsrc(blk.plane[p], P.plane_bytes);
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(P.in, P.in_bytes);
     const uint32_t lds_base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char *)smem);
-    char *xs = smem + kMidLutBytes;
-    const uint32_t xs_base = lds_base + kMidLutBytes;
+    char *xs = smem + kMidLutBytes<MODE>;
+    const uint32_t xs_base = lds_base + kMidLutBytes<MODE>;
 
     // token copies: instruction u = wave + 8k fills rows 4u .. 4u+3 of a buffer; lane L
     // writes 16-byte position L % 16 of row 4u + L / 16 and fetches the chunk stored
@@ -820,28 +827,37 @@ __device__ __attribute__((always_inline)) inline void mid_block(const GemmParams
     }
 }
 
-template <int TT>
+template <int MODE, int TT>
 __device__ __attribute__((always_inline)) inline void mid_dispatch_q(const GemmParams &P, const DevBlock &blk, int rb,
                                                                      int r0, int Me, char *smem)
 {
-    switch (blk.q) {
-    case 3: mid_block<3, TT>(P, blk, rb, r0, Me, smem); break;
-    case 4: mid_block<4, TT>(P, blk, rb, r0, Me, smem); break;
-    case 5: mid_block<5, TT>(P, blk, rb, r0, Me, smem); break;
-    case 6: mid_block<6, TT>(P, blk, rb, r0, Me, smem); break;
-    case 7: mid_block<7, TT>(P, blk, rb, r0, Me, smem); break;
-    case 8: mid_block<8, TT>(P, blk, rb, r0, Me, smem); break;
-    default: break;  // unreachable: commit validates q
+    if constexpr (MODE == kMidQ8) {
+        if (blk.q == 8)
+            mid_block<8, TT, MODE>(P, blk, rb, r0, Me, smem);
+    } else {
+        switch (blk.q) {
+        case 3: mid_block<3, TT, MODE>(P, blk, rb, r0, Me, smem); break;
+        case 4: mid_block<4, TT, MODE>(P, blk, rb, r0, Me, smem); break;
+        case 5: mid_block<5, TT, MODE>(P, blk, rb, r0, Me, smem); break;
+        case 6: mid_block<6, TT, MODE>(P, blk, rb, r0, Me, smem); break;
+        case 7: mid_block<7, TT, MODE>(P, blk, rb, r0, Me, smem); break;
+        case 8:
+            if constexpr (MODE == kMidAll)
+                mid_block<8, TT, MODE>(P, blk, rb, r0, Me, smem);
+            break;  // kMidLow: the q = 8 launch
+        default: break;  // unreachable: commit validates q
+        }
     }
 }
 
 // P.row_blocks here counts 128-row blocks (with the activation fused: 64 gate rows
-// and their 64 up rows).  Experts outside P.min_rows + 1 .. kMidMaxRows rows return
-// at once.
-template <int KIND>
-__global__ void __launch_bounds__(kMidThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) gemm_mid_kernel(GemmParams P)
+// and their 64 up rows).  Experts outside P.min_rows + 1 .. kMidMaxRows rows, and
+// blocks of the other launch's bitwidths, return at once.
+template <int KIND, int MODE>
+__global__ void __launch_bounds__(kMidThreads)
+__attribute__((amdgpu_waves_per_eu(MODE == kMidLow ? 4 : 2, MODE == kMidLow ? 4 : 2))) gemm_mid_kernel(GemmParams P)
 {
-    __shared__ __attribute__((aligned(16))) char smem[kMidLds];
+    __shared__ __attribute__((aligned(16))) char smem[kMidLds<MODE>];
     const int per = (int)gridDim.x / kXcds;
     const int w = (int)(blockIdx.x % kXcds) * per + (int)(blockIdx.x / kXcds);
     if (w >= P.row_blocks * P.E)
@@ -853,7 +869,7 @@ __global__ void __launch_bounds__(kMidThreads) __attribute__((amdgpu_waves_per_e
     if (Me <= P.min_rows || Me > kMidMaxRows)
         return;
     const DevBlock blk = P.table[2 * e + P.kind];
-    mid_dispatch_q<kMidTT>(P, blk, rb, r0, Me, smem);
+    mid_dispatch_q<MODE, kMidTT>(P, blk, rb, r0, Me, smem);
 }
 
 template <int KIND, int KP>
@@ -872,7 +888,6 @@ hipError_t launch_gemm(const DevBlock *table, int kind, int E, int N, int K, int
                        size_t in_bytes, int gather, const int32_t *perm, const int32_t *offsets, int topk, int R,
                        void *out, int out_f32, int act, hipStream_t s)
 {
-    (void)max_q;
     GemmParams P;
     P.table = table;
     P.in = in;
@@ -919,11 +934,29 @@ hipError_t launch_gemm(const DevBlock *table, int kind, int E, int N, int K, int
     M.min_rows = P.max_rows;
     M.row_blocks = act ? (N / 2) / 64 : (N + kMidRows - 1) / kMidRows;
     const dim3 mgrid((M.row_blocks * E + kXcds - 1) / kXcds * kXcds);
-    if (kind == APMOE_GATE_UP)
-        hipLaunchKernelGGL(gemm_mid_kernel<APMOE_GATE_UP>, mgrid, dim3(kMidThreads), 0, s, M);
-    else
-        hipLaunchKernelGGL(gemm_mid_kernel<APMOE_DOWN>, mgrid, dim3(kMidThreads), 0, s, M);
-    err = hipGetLastError();
+    // Two workgroups per CU pay where an expert alone has many row blocks (the 8x22B
+    // gate_up: 256); with few (its down: 48) they measured slower than one.  The q = 8
+    // launch runs only if the committed map of the layer has such a block.
+    if (M.row_blocks >= 128) {
+        if (kind == APMOE_GATE_UP)
+            hipLaunchKernelGGL((gemm_mid_kernel<APMOE_GATE_UP, kMidLow>), mgrid, dim3(kMidThreads), 0, s, M);
+        else
+            hipLaunchKernelGGL((gemm_mid_kernel<APMOE_DOWN, kMidLow>), mgrid, dim3(kMidThreads), 0, s, M);
+        err = hipGetLastError();
+        if (err == hipSuccess && max_q == 8) {
+            if (kind == APMOE_GATE_UP)
+                hipLaunchKernelGGL((gemm_mid_kernel<APMOE_GATE_UP, kMidQ8>), mgrid, dim3(kMidThreads), 0, s, M);
+            else
+                hipLaunchKernelGGL((gemm_mid_kernel<APMOE_DOWN, kMidQ8>), mgrid, dim3(kMidThreads), 0, s, M);
+            err = hipGetLastError();
+        }
+    } else {
+        if (kind == APMOE_GATE_UP)
+            hipLaunchKernelGGL((gemm_mid_kernel<APMOE_GATE_UP, kMidAll>), mgrid, dim3(kMidThreads), 0, s, M);
+        else
+            hipLaunchKernelGGL((gemm_mid_kernel<APMOE_DOWN, kMidAll>), mgrid, dim3(kMidThreads), 0, s, M);
+        err = hipGetLastError();
+    }
     if (err != hipSuccess || tokens <= kMidMaxRows)
         return err;
     return launch_gemm_tile(table, kind, E, N, K, in, in_bytes, gather, perm, offsets, topk, out, out_f32, act, R, s);

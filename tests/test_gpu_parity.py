@@ -408,11 +408,12 @@ def test_gemm_tile_non_gather_rows():
 # weight decoded once for two 32-token tiles): the boundaries 32 / 33 and 64 / 65
 # between the three products, weight-row tails (N % 128 of 72, 8 and 40), K = 128
 # (one step) and odd numbers of steps; the other counts take the decode product (one
-# or two passes) and the tile product in the same call.
+# or two passes) and the tile product in the same call.  Blocks at q = 8 (the last
+# expert) take a launch of their own (64 KB LUT region).
 MID_CASES = [
-    (200, 384, [33, 64, 65, 16, 17, 32]),
+    (200, 384, [32, 64, 65, 16, 17, 33]),
     (136, 128, [128, 33, 0, 100, 1, 65]),
-    (40, 640, [64, 127, 17, 96, 50, 16]),
+    (40, 640, [64, 127, 17, 96, 16, 50]),
     (256, 1152, [90, 33, 128, 0, 64, 20]),
 ]
 
@@ -421,6 +422,22 @@ MID_CASES = [
 def test_gemm_mid_identity_lut_exact(case):
     N, K, counts = case
     tbl, keep, P, L, offsets, perm, T = _gemm_setup(GEMM_QS, counts, N, K, True, 47)
+    x = RNG.integers(-2, 3, (T, K)).astype(np.float16)
+    got = _gemm_run(tbl, x, offsets, perm, T, N, apw.F32)
+    for e, q in enumerate(GEMM_QS):
+        rows = perm[offsets[e]:offsets[e + 1]]
+        codes = oracle.unpack_codes(P[e], q).astype(np.int64)
+        ref = x[rows].astype(np.int64) @ codes.T
+        assert np.array_equal(got[offsets[e]:offsets[e + 1]], ref.astype(np.float32)), (e, q, counts[e])
+    tbl.close()
+
+
+def test_gemm_mid_wide_launch_exact():
+    """A launch with at least 128 row blocks of 128 rows runs the mid product as two
+    launches: blocks at q <= 7 with two workgroups per CU, then the blocks at q = 8
+    (here the expert with 50 rows)."""
+    N, K, counts = 16384, 256, [33, 64, 40, 0, 5, 50]
+    tbl, keep, P, L, offsets, perm, T = _gemm_setup(GEMM_QS, counts, N, K, True, 51)
     x = RNG.integers(-2, 3, (T, K)).astype(np.float16)
     got = _gemm_run(tbl, x, offsets, perm, T, N, apw.F32)
     for e, q in enumerate(GEMM_QS):
