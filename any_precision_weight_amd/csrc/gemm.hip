@@ -50,6 +50,7 @@ constexpr int kRows = kGemmRowsPerBlock;  // 64
 constexpr int kStepCols = 128;            // columns per wave step (2 lane halves x 64)
 constexpr int kTokTile = 32;
 constexpr int kXcds = 8;                  // accelerator complex dies; workgroup b runs on XCD b % 8
+constexpr int kLptExperts = 16;           // launches with at most this many experts run heaviest first
 constexpr int kLutBytes = 32 * 1024;                       // LUT region, every q
 template <int KP>
 constexpr int kRedBytesOf = (KP - 1) * 2 * 16 * kWave * sizeof(float);  // column-part reduction
@@ -503,16 +504,50 @@ template <int KIND, int TOKL, int KP>
 __global__ void __launch_bounds__(kThreadsOf<KP>) __attribute__((amdgpu_waves_per_eu(3))) gemm_kernel(GemmParams P)
 {
     __shared__ __attribute__((aligned(16))) char smem[kLdsBytes<TOKL, KP>];
-    // Workgroup b runs on XCD b % 8.  XCD x takes the x-th eighth of the work items and
-    // consecutive work items cycle over the experts, so every XCD streams an equal share
-    // of every expert's rows.  (With e = b % E and E = 8, each expert would run on one
-    // XCD, and the launch would wait for the XCD with the most planes or token passes.)
-    const int per = (int)gridDim.x / kXcds;
-    const int w = (int)(blockIdx.x % kXcds) * per + (int)(blockIdx.x / kXcds);
-    if (w >= P.row_blocks * P.E)
-        return;  // grid padding to a multiple of the XCD count
-    const int e = w % P.E;
-    const int rb = w / P.E;
+    // Workgroup b runs on XCD b % 8, and XCD x takes the x-th eighth of every expert's
+    // row blocks, so every XCD streams an equal share of every expert.  (With e = b % E
+    // and E = 8, each expert would run on one XCD, and the launch would wait for the
+    // XCD with the most planes or token passes.)
+    int e, rb;
+    if (P.E <= kLptExperts) {
+        // XCD x runs its row blocks expert by expert, heaviest first (bitwidth q, then
+        // lower index; experts this launch does not serve last), so the last workgroups
+        // of the launch are the shortest.  Every thread computes the same order from
+        // wave-uniform loads.
+        const int r8 = (P.row_blocks + kXcds - 1) / kXcds;
+        const int l = (int)(blockIdx.x / kXcds);
+        const int j = l / r8;
+        rb = (int)(blockIdx.x % kXcds) * r8 + l % r8;
+        if (j >= P.E || rb >= P.row_blocks)
+            return;  // grid padding
+        int key[kLptExperts];
+#pragma unroll
+        for (int u = 0; u < kLptExperts; ++u) {
+            key[u] = 0;
+            if (u < P.E) {
+                const int mu = P.offsets[u + 1] - P.offsets[u];
+                key[u] = mu > 0 && mu <= P.max_rows ? P.table[2 * u + P.kind].q : 0;
+            }
+        }
+        e = 0;
+#pragma unroll
+        for (int u = 0; u < kLptExperts; ++u) {
+            int rank = 0;
+#pragma unroll
+            for (int v = 0; v < kLptExperts; ++v)
+                rank += v < P.E && (key[v] > key[u] || (key[v] == key[u] && v < u));
+            if (u < P.E && rank == j)
+                e = u;
+        }
+    } else {
+        // consecutive work items cycle over the experts
+        const int per = (int)gridDim.x / kXcds;
+        const int w = (int)(blockIdx.x % kXcds) * per + (int)(blockIdx.x / kXcds);
+        if (w >= P.row_blocks * P.E)
+            return;  // grid padding to a multiple of the XCD count
+        e = w % P.E;
+        rb = w / P.E;
+    }
     const int r0 = P.offsets[e];
     const int Me = P.offsets[e + 1] - r0;
     if (Me <= 0 || Me > P.max_rows)
@@ -875,7 +910,8 @@ __attribute__((amdgpu_waves_per_eu(MODE == kMidLow ? 4 : 2, MODE == kMidLow ? 4 
 template <int KIND, int KP>
 void launch_kind(const GemmParams &P, hipStream_t s)
 {
-    const dim3 grid((P.row_blocks * P.E + kXcds - 1) / kXcds * kXcds);
+    const dim3 grid(P.E <= kLptExperts ? kXcds * P.E * ((P.row_blocks + kXcds - 1) / kXcds)
+                                       : (P.row_blocks * P.E + kXcds - 1) / kXcds * kXcds);
     if (P.tokl == 8)
         hipLaunchKernelGGL((gemm_kernel<KIND, 8, KP>), grid, dim3(kThreadsOf<KP>), 0, s, P);
     else
