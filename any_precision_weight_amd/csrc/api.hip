@@ -732,8 +732,18 @@ static apmoe_status gemm_common(apmoe_ctx *ctx, const apmoe_table *tbl, int32_t 
         return fail(APMOE_INVALID_ARG, "operands above 2 GiB per buffer are not supported (in %zu B, plane %zu B)",
                     in_bytes, plane_bytes);
     const DevBlock *slice = tbl->d_table + tbl->index(layer, 0, 0);
-    hipError_t e = apmoe::launch_gemm(slice, kind, tbl->E, N, K, max_q, in, in_bytes, gather, perm, offsets, topk,
-                                      T * topk, out, out_dtype == APMOE_F32, act,
+    // experts by committed q, highest first (stable): the order the decode product starts them in
+    uint8_t order[APMOE_MAX_EXPERTS];
+    int n = 0;
+    for (int q = APMOE_MAX_BITS; q >= 0; --q)
+        for (int e = 0; e < tbl->E; ++e)
+            if (tbl->cq[tbl->index(layer, e, kind)] == q)
+                order[n++] = (uint8_t)e;
+    if (n != tbl->E)  // unreachable: commit keeps every q in 3..8
+        for (n = 0; n < tbl->E; ++n)
+            order[n] = (uint8_t)n;
+    hipError_t e = apmoe::launch_gemm(slice, kind, tbl->E, N, K, max_q, order, in, in_bytes, gather, perm, offsets,
+                                      topk, T * topk, out, out_dtype == APMOE_F32, act,
                                       reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? ok() : hip_fail(e, "gemm launch");
 }

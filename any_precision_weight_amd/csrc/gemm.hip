@@ -50,7 +50,7 @@ constexpr int kRows = kGemmRowsPerBlock;  // 64
 constexpr int kStepCols = 128;            // columns per wave step (2 lane halves x 64)
 constexpr int kTokTile = 32;
 constexpr int kXcds = 8;                  // accelerator complex dies; workgroup b runs on XCD b % 8
-constexpr int kLptExperts = 16;           // launches with at most this many experts run heaviest first
+constexpr int kLptExperts = 16;           // launches with at most this many experts rank them on the device
 constexpr int kLutBytes = 32 * 1024;                       // LUT region, every q
 template <int KP>
 constexpr int kRedBytesOf = (KP - 1) * 2 * 16 * kWave * sizeof(float);  // column-part reduction
@@ -130,6 +130,7 @@ struct GemmParams {
     int tokl;              // token rows per pass (8 or 16): the LDS token buffers' size
     uint32_t in_bytes;     // bytes of `in` (buffer range of the B-operand loads)
     uint32_t plane_bytes;  // bytes of one tiled plane
+    uint8_t order[APMOE_MAX_EXPERTS];  // experts by committed q, highest first (launches with E > 16)
 };
 
 // Plane bases are wave-uniform (scalar registers); the per-lane part is a 32-bit
@@ -508,25 +509,27 @@ __global__ void __launch_bounds__(kThreadsOf<KP>) __attribute__((amdgpu_waves_pe
     // row blocks, so every XCD streams an equal share of every expert.  (With e = b % E
     // and E = 8, each expert would run on one XCD, and the launch would wait for the
     // XCD with the most planes or token passes.)
-    int e, rb;
+    // XCD x runs its row blocks expert by expert, longest workgroups first, so the last
+    // workgroups of the launch (a partial round) are the shortest.
+    const int r8 = (P.row_blocks + kXcds - 1) / kXcds;
+    const int l = (int)(blockIdx.x / kXcds);
+    const int j = l / r8;  // rank of the expert
+    const int rb = (int)(blockIdx.x % kXcds) * r8 + l % r8;
+    if (j >= P.E || rb >= P.row_blocks)
+        return;  // grid padding
+    int e;
     if (P.E <= kLptExperts) {
-        // XCD x runs its row blocks expert by expert, heaviest first (bitwidth q, then
-        // lower index; experts this launch does not serve last), so the last workgroups
-        // of the launch are the shortest.  Every thread computes the same order from
-        // wave-uniform loads.
-        const int r8 = (P.row_blocks + kXcds - 1) / kXcds;
-        const int l = (int)(blockIdx.x / kXcds);
-        const int j = l / r8;
-        rb = (int)(blockIdx.x % kXcds) * r8 + l % r8;
-        if (j >= P.E || rb >= P.row_blocks)
-            return;  // grid padding
+        // rank by the estimated workgroup length, passes over the weights x (2q + 7) (a
+        // fit of the measured time per q), then lower index; experts this launch does
+        // not serve last.  Every thread computes the same ranks from wave-uniform loads.
         int key[kLptExperts];
 #pragma unroll
         for (int u = 0; u < kLptExperts; ++u) {
             key[u] = 0;
             if (u < P.E) {
                 const int mu = P.offsets[u + 1] - P.offsets[u];
-                key[u] = mu > 0 && mu <= P.max_rows ? P.table[2 * u + P.kind].q : 0;
+                if (mu > 0 && mu <= P.max_rows)
+                    key[u] = (mu + TOKL - 1) / TOKL * (2 * P.table[2 * u + P.kind].q + 7);
             }
         }
         e = 0;
@@ -540,13 +543,7 @@ __global__ void __launch_bounds__(kThreadsOf<KP>) __attribute__((amdgpu_waves_pe
                 e = u;
         }
     } else {
-        // consecutive work items cycle over the experts
-        const int per = (int)gridDim.x / kXcds;
-        const int w = (int)(blockIdx.x % kXcds) * per + (int)(blockIdx.x / kXcds);
-        if (w >= P.row_blocks * P.E)
-            return;  // grid padding to a multiple of the XCD count
-        e = w % P.E;
-        rb = w / P.E;
+        e = P.order[j];  // by committed q (the host's view of the table)
     }
     const int r0 = P.offsets[e];
     const int Me = P.offsets[e + 1] - r0;
@@ -910,8 +907,7 @@ __attribute__((amdgpu_waves_per_eu(MODE == kMidLow ? 4 : 2, MODE == kMidLow ? 4 
 template <int KIND, int KP>
 void launch_kind(const GemmParams &P, hipStream_t s)
 {
-    const dim3 grid(P.E <= kLptExperts ? kXcds * P.E * ((P.row_blocks + kXcds - 1) / kXcds)
-                                       : (P.row_blocks * P.E + kXcds - 1) / kXcds * kXcds);
+    const dim3 grid(kXcds * P.E * ((P.row_blocks + kXcds - 1) / kXcds));
     if (P.tokl == 8)
         hipLaunchKernelGGL((gemm_kernel<KIND, 8, KP>), grid, dim3(kThreadsOf<KP>), 0, s, P);
     else
@@ -920,9 +916,9 @@ void launch_kind(const GemmParams &P, hipStream_t s)
 
 }  // namespace
 
-hipError_t launch_gemm(const DevBlock *table, int kind, int E, int N, int K, int max_q, const uint16_t *in,
-                       size_t in_bytes, int gather, const int32_t *perm, const int32_t *offsets, int topk, int R,
-                       void *out, int out_f32, int act, hipStream_t s)
+hipError_t launch_gemm(const DevBlock *table, int kind, int E, int N, int K, int max_q, const uint8_t *order,
+                       const uint16_t *in, size_t in_bytes, int gather, const int32_t *perm, const int32_t *offsets,
+                       int topk, int R, void *out, int out_f32, int act, hipStream_t s)
 {
     GemmParams P;
     P.table = table;
@@ -942,6 +938,8 @@ hipError_t launch_gemm(const DevBlock *table, int kind, int E, int N, int K, int
     P.row_blocks = act ? (N / 2) / 32 : (N + kRows - 1) / kRows;
     P.in_bytes = (uint32_t)in_bytes;
     P.plane_bytes = (uint32_t)(tiled_plane_words(N, K) * 4);
+    for (int u = 0; u < E; ++u)
+        P.order[u] = order[u];
     // A token is routed to an expert at most once, so no expert has more rows than the
     // batch has tokens (R / topk; a shared expert has exactly that many).  The token
     // buffers hold 8 rows up to 16 tokens (40 KB of LDS: four workgroups per CU; with 16
