@@ -521,27 +521,22 @@ __global__ void __launch_bounds__(kThreadsOf<KP>) __attribute__((amdgpu_waves_pe
     if (P.E <= kLptExperts) {
         // rank by the estimated workgroup length, passes over the weights x (2q + 7) (a
         // fit of the measured time per q), then lower index; experts this launch does
-        // not serve last.  Every thread computes the same ranks from wave-uniform loads.
-        int key[kLptExperts];
-#pragma unroll
-        for (int u = 0; u < kLptExperts; ++u) {
-            key[u] = 0;
-            if (u < P.E) {
-                const int mu = P.offsets[u + 1] - P.offsets[u];
-                if (mu > 0 && mu <= P.max_rows)
-                    key[u] = (mu + TOKL - 1) / TOKL * (2 * P.table[2 * u + P.kind].q + 7);
-            }
+        // not serve last.  Lane u holds expert u's key; every wave computes the ranks.
+        const int lane = (int)(threadIdx.x % kWave);
+        int key = 0;
+        if (lane < P.E) {
+            const int mu = P.offsets[lane + 1] - P.offsets[lane];
+            if (mu > 0 && mu <= P.max_rows)
+                key = (mu + TOKL - 1) / TOKL * (2 * P.table[2 * lane + P.kind].q + 7);
         }
-        e = 0;
+        int rank = 0;
 #pragma unroll
-        for (int u = 0; u < kLptExperts; ++u) {
-            int rank = 0;
-#pragma unroll
-            for (int v = 0; v < kLptExperts; ++v)
-                rank += v < P.E && (key[v] > key[u] || (key[v] == key[u] && v < u));
-            if (u < P.E && rank == j)
-                e = u;
+        for (int v = 0; v < kLptExperts; ++v) {
+            const int kv = __builtin_amdgcn_readlane(key, v);
+            rank += v < P.E && (kv > key || (kv == key && v < lane));
         }
+        const uint64_t hit = __ballot(lane < P.E && rank == j);  // exactly one lane: ranks are distinct
+        e = __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(hit));
     } else {
         e = P.order[j];  // by committed q (the host's view of the table)
     }
