@@ -34,9 +34,10 @@
 //   [128, 160 KB) two 16 KB A stages: fragment (producer p, k-group b) of lane L at
 //                 ((4p + b) * 64 + L) * 16.
 //
-// Tile order: tiles of one expert are grouped as (8 weight-row tiles) x (all token
-// tiles), consecutive tiles run on the same XCD (workgroup b runs on XCD b % 8), so
-// a group's weight and token tiles are shared through that XCD's L2.
+// Tile order: weight-row groups of 8 tiles, each with the token tiles of every served
+// expert; consecutive tiles run on the same XCD (workgroup b runs on XCD b % 8), so a
+// group's weight and token tiles are shared through that XCD's L2, and every XCD
+// runs tiles of every expert.
 #include "internal.h"
 
 namespace apmoe {
@@ -134,15 +135,20 @@ struct Tile {
 };
 
 // Workgroup -> tile.  Every thread computes the same answer; E <= 256 < blockDim.
+// Tile order: weight-row group k (kGroupN weight tiles; the last group the NT % 8
+// left), then token tile u over all served experts (expert by expert), then the gs
+// weight tiles of the group.  XCD x takes the x-th eighth of that order, so every XCD
+// runs tiles of every expert (tile cost depends on the expert's q), and consecutive
+// tiles on an XCD share a group's weight tiles and a token tile through its L2.
 __device__ __attribute__((always_inline)) bool resolve_tile(const TileParams &P, int *scan, Tile &T)
 {
     const int tid = threadIdx.x;
-    int tiles = 0;
+    int mt_e = 0;
     if (tid < P.E) {
         const int me = P.offsets[tid + 1] - P.offsets[tid];
-        tiles = me > P.min_rows ? (me + kBM - 1) / kBM * P.NT : 0;
+        mt_e = me > P.min_rows ? (me + kBM - 1) / kBM : 0;
     }
-    scan[tid] = tiles;
+    scan[tid] = mt_e;
     __syncthreads();
     for (int d = 1; d < kThreads; d <<= 1) {  // inclusive scan (Hillis-Steele)
         const int v = tid >= d ? scan[tid - d] : 0;
@@ -150,42 +156,35 @@ __device__ __attribute__((always_inline)) bool resolve_tile(const TileParams &P,
         scan[tid] += v;
         __syncthreads();
     }
-    const int total = scan[kThreads - 1];
+    const int MT = scan[kThreads - 1];  // token tiles of all served experts
+    const int total = MT * P.NT;
     const int per_xcd = (total + kXcds - 1) / kXcds;
     const int b = blockIdx.x;
     const int local = b / kXcds;
     const int l = (b % kXcds) * per_xcd + local;
     if (local >= per_xcd || l >= total)
         return false;
-    // expert: the first e with scan[e] > l
+    const int k = l / (kGroupN * MT);
+    const int gs = min(kGroupN, P.NT - kGroupN * k);
+    const int rem = l - k * kGroupN * MT;
+    const int u = rem / gs;
+    const int nt = k * kGroupN + rem % gs;
+    // expert: the first e with scan[e] > u
     int e = 0;
     {
         int lo = 0, hi = P.E - 1;
         while (lo < hi) {
             const int mid = (lo + hi) >> 1;
-            if (scan[mid] > l)
+            if (scan[mid] > u)
                 hi = mid;
             else
                 lo = mid + 1;
         }
         e = lo;
     }
-    const int t = l - (e > 0 ? scan[e - 1] : 0);
+    const int mt = u - (e > 0 ? scan[e - 1] : 0);
     const int r0 = P.offsets[e];
     const int me = P.offsets[e + 1] - r0;
-    const int mt_n = (me + kBM - 1) / kBM;
-    const int full_groups = P.NT / kGroupN;
-    int mt, nt;
-    if (t < full_groups * kGroupN * mt_n) {
-        const int ng = t / (kGroupN * mt_n), w = t % (kGroupN * mt_n);
-        mt = w / kGroupN;
-        nt = ng * kGroupN + w % kGroupN;
-    } else {
-        const int gs = P.NT - full_groups * kGroupN;
-        const int w = t - full_groups * kGroupN * mt_n;
-        mt = w / gs;
-        nt = full_groups * kGroupN + w % gs;
-    }
     // identical in every lane: keep the tile in scalar registers
     T.e = __builtin_amdgcn_readfirstlane(e);
     T.r0 = __builtin_amdgcn_readfirstlane(r0);
