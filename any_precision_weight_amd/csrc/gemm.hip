@@ -501,34 +501,29 @@ template <int TOKL, int KP>
 constexpr int kLdsBytes = kLutBytes + (kRedBytesOf<KP> > 2 * KP * TOKL * kXRowBytes ? kRedBytesOf<KP>
                                                                                     : 2 * KP * TOKL * kXRowBytes);
 
-template <int KIND, int TOKL, int KP>
-__global__ void __launch_bounds__(kThreadsOf<KP>) __attribute__((amdgpu_waves_per_eu(3))) gemm_kernel(GemmParams P)
+// Workgroup -> (expert e, row block rb).  Workgroup b runs on XCD b % 8, and XCD x
+// takes the x-th eighth of every expert's row blocks, so every XCD streams an equal
+// share of every expert.  (With e = b % E and E = 8, each expert would run on one
+// XCD, and the launch would wait for the XCD with the most planes or token passes.)
+// XCD x runs its row blocks expert by expert, longest workgroups first, so the last
+// workgroups of the launch (a partial round) are the shortest.  With at most 16
+// experts the ranks come from key_of(u), the estimated workgroup length of expert u
+// (0 when this launch does not serve it), then the lower index: lane u holds expert
+// u's key and every wave computes the ranks.  Above 16 experts the host's order of
+// the committed q map is used.  Returns false for grid padding.
+template <typename KeyOf>
+__device__ __attribute__((always_inline)) inline bool work_item(const GemmParams &P, const KeyOf &key_of, int &e,
+                                                                int &rb)
 {
-    __shared__ __attribute__((aligned(16))) char smem[kLdsBytes<TOKL, KP>];
-    // Workgroup b runs on XCD b % 8, and XCD x takes the x-th eighth of every expert's
-    // row blocks, so every XCD streams an equal share of every expert.  (With e = b % E
-    // and E = 8, each expert would run on one XCD, and the launch would wait for the
-    // XCD with the most planes or token passes.)
-    // XCD x runs its row blocks expert by expert, longest workgroups first, so the last
-    // workgroups of the launch (a partial round) are the shortest.
     const int r8 = (P.row_blocks + kXcds - 1) / kXcds;
     const int l = (int)(blockIdx.x / kXcds);
     const int j = l / r8;  // rank of the expert
-    const int rb = (int)(blockIdx.x % kXcds) * r8 + l % r8;
+    rb = (int)(blockIdx.x % kXcds) * r8 + l % r8;
     if (j >= P.E || rb >= P.row_blocks)
-        return;  // grid padding
-    int e;
+        return false;
     if (P.E <= kLptExperts) {
-        // rank by the estimated workgroup length, passes over the weights x (2q + 7) (a
-        // fit of the measured time per q), then lower index; experts this launch does
-        // not serve last.  Lane u holds expert u's key; every wave computes the ranks.
         const int lane = (int)(threadIdx.x % kWave);
-        int key = 0;
-        if (lane < P.E) {
-            const int mu = P.offsets[lane + 1] - P.offsets[lane];
-            if (mu > 0 && mu <= P.max_rows)
-                key = (mu + TOKL - 1) / TOKL * (2 * P.table[2 * lane + P.kind].q + 7);
-        }
+        const int key = lane < P.E ? key_of(lane) : 0;
         int rank = 0;
 #pragma unroll
         for (int v = 0; v < kLptExperts; ++v) {
@@ -538,8 +533,23 @@ __global__ void __launch_bounds__(kThreadsOf<KP>) __attribute__((amdgpu_waves_pe
         const uint64_t hit = __ballot(lane < P.E && rank == j);  // exactly one lane: ranks are distinct
         e = __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(hit));
     } else {
-        e = P.order[j];  // by committed q (the host's view of the table)
+        e = P.order[j];
     }
+    return true;
+}
+
+template <int KIND, int TOKL, int KP>
+__global__ void __launch_bounds__(kThreadsOf<KP>) __attribute__((amdgpu_waves_per_eu(3))) gemm_kernel(GemmParams P)
+{
+    __shared__ __attribute__((aligned(16))) char smem[kLdsBytes<TOKL, KP>];
+    int e, rb;
+    const auto key_of = [&](int u) {
+        // passes over the weights x (2q + 7), a fit of the measured time per q
+        const int mu = P.offsets[u + 1] - P.offsets[u];
+        return mu > 0 && mu <= P.max_rows ? (mu + TOKL - 1) / TOKL * (2 * P.table[2 * u + P.kind].q + 7) : 0;
+    };
+    if (!work_item(P, key_of, e, rb))
+        return;  // grid padding
     const int r0 = P.offsets[e];
     const int Me = P.offsets[e + 1] - r0;
     if (Me <= 0 || Me > P.max_rows)
@@ -885,12 +895,15 @@ __global__ void __launch_bounds__(kMidThreads)
 __attribute__((amdgpu_waves_per_eu(MODE == kMidLow ? 4 : 2, MODE == kMidLow ? 4 : 2))) gemm_mid_kernel(GemmParams P)
 {
     __shared__ __attribute__((aligned(16))) char smem[kMidLds<MODE>];
-    const int per = (int)gridDim.x / kXcds;
-    const int w = (int)(blockIdx.x % kXcds) * per + (int)(blockIdx.x / kXcds);
-    if (w >= P.row_blocks * P.E)
-        return;
-    const int e = w % P.E;
-    const int rb = w / P.E;
+    int e, rb;
+    const auto key_of = [&](int u) {
+        const int mu = P.offsets[u + 1] - P.offsets[u];
+        const int q = P.table[2 * u + P.kind].q;
+        const bool mine = MODE == kMidAll || (MODE == kMidQ8) == (q == 8);
+        return mu > P.min_rows && mu <= kMidMaxRows && mine ? 2 * q + 7 : 0;
+    };
+    if (!work_item(P, key_of, e, rb))
+        return;  // grid padding
     const int r0 = P.offsets[e];
     const int Me = P.offsets[e + 1] - r0;
     if (Me <= P.min_rows || Me > kMidMaxRows)
@@ -962,7 +975,7 @@ hipError_t launch_gemm(const DevBlock *table, int kind, int E, int N, int K, int
     GemmParams M = P;
     M.min_rows = P.max_rows;
     M.row_blocks = act ? (N / 2) / 64 : (N + kMidRows - 1) / kMidRows;
-    const dim3 mgrid((M.row_blocks * E + kXcds - 1) / kXcds * kXcds);
+    const dim3 mgrid(kXcds * E * ((M.row_blocks + kXcds - 1) / kXcds));
     // Two workgroups per CU pay where an expert alone has many row blocks (the 8x22B
     // gate_up: 256); with few (its down: 48) they measured slower than one.  The q = 8
     // launch runs only if the committed map of the layer has such a block.
