@@ -280,7 +280,9 @@ apmoe_status apmoe_route_stats(apmoe_ctx *ctx, const float *topk_w, const int32_
                                void *stream);
 
 /*
- * Any-precision product of every expert of one (layer, kind) in one launch.
+ * Any-precision product of every expert of one (layer, kind) in one call: up to
+ * three kernel launches on `stream`, by the experts' row counts (up to 32 rows, 33..64,
+ * more), each skipped when the batch has too few tokens for any expert to need it.
  * For expert e, rows r in [offsets[e], offsets[e+1]) of the output:
  *   out[r][n] = sum_c in_row(r)[c] * LUT_q[n][code_q(n, c)],   fp32 accumulation,
  * with q, planes and LUT of block (layer, e, kind) read from the committed
