@@ -312,6 +312,25 @@ def test_gemm_decode_multipass_exact(counts):
     tbl.close()
 
 
+def test_gemm_many_experts_exact():
+    """Above 16 experts the decode and mid products start the experts in the host's
+    order of the committed q map (a scheduling hint): 40 experts, q cycling 3..8,
+    rows 0..70 (decode, mid and tile products in one call), identity LUTs, exact."""
+    E = 40
+    qs = [3 + (e * 5) % 6 for e in range(E)]
+    counts = [(e * 37) % 71 for e in range(E)]
+    N, K = 136, 256
+    tbl, keep, P, L, offsets, perm, T = _gemm_setup(qs, counts, N, K, True, 52)
+    x = RNG.integers(-2, 3, (T, K)).astype(np.float16)
+    got = _gemm_run(tbl, x, offsets, perm, T, N, apw.F32)
+    for e, q in enumerate(qs):
+        rows = perm[offsets[e]:offsets[e + 1]]
+        codes = oracle.unpack_codes(P[e], q).astype(np.int64)
+        ref = x[rows].astype(np.int64) @ codes.T
+        assert np.array_equal(got[offsets[e]:offsets[e + 1]], ref.astype(np.float32)), (e, q, counts[e])
+    tbl.close()
+
+
 @pytest.mark.parametrize("out_dtype", [apw.F16, apw.F32])
 def test_gemm_random_lut(out_dtype):
     N, K = 136, 384
