@@ -732,7 +732,8 @@ static apmoe_status gemm_common(apmoe_ctx *ctx, const apmoe_table *tbl, int32_t 
         return fail(APMOE_INVALID_ARG, "operands above 2 GiB per buffer are not supported (in %zu B, plane %zu B)",
                     in_bytes, plane_bytes);
     const DevBlock *slice = tbl->d_table + tbl->index(layer, 0, 0);
-    // experts by committed q, highest first (stable): the order the decode product starts them in
+    // experts by committed q, highest first (stable): the order in which the decode and mid
+    // products start them when the layer has more than 16 experts (a scheduling hint)
     uint8_t order[APMOE_MAX_EXPERTS];
     int n = 0;
     for (int q = APMOE_MAX_BITS; q >= 0; --q)

@@ -57,7 +57,7 @@ hipError_t launch_route_stats(const float *w, const int32_t *perm, const int32_t
 // act = 1 (gate_up only, F = N/2 a multiple of 64): the epilogue applies silu_mul to
 // the fp16-rounded gate row f and up row F + f and writes fp16 a[R][F] to out.
 // order: the E experts by committed q, highest first, lower index on ties (a
-// scheduling hint: the decode product of a launch with more than 16 experts starts
+// scheduling hint: the decode and mid products of a launch with more than 16 experts start
 // the experts in this order; any permutation gives the same result).
 hipError_t launch_gemm(const DevBlock *table, int kind, int E, int N, int K, int max_q, const uint8_t *order,
                        const uint16_t *in, size_t in_bytes, int gather, const int32_t *perm, const int32_t *offsets,
