@@ -51,6 +51,7 @@ struct apmoe_ctx {
     int device;
     int cus;
     char arch[64];
+    apmoe::SideStream side;  // runs a short tile launch beside the decode and mid launches
 };
 
 struct apmoe_table {
@@ -197,12 +198,37 @@ apmoe_status apmoe_create(apmoe_ctx **out, int device)
     c->device = device;
     c->cus = prop.multiProcessorCount;
     snprintf(c->arch, sizeof(c->arch), "%s", prop.gcnArchName);
+    // side stream (default priority) and its events, created on `device`
+    int cur = -1;
+    e = hipGetDevice(&cur);
+    if (e == hipSuccess && cur != device)
+        e = hipSetDevice(device);
+    if (e == hipSuccess)
+        e = hipStreamCreateWithFlags(&c->side.stream, hipStreamNonBlocking);
+    if (e == hipSuccess)
+        e = hipEventCreateWithFlags(&c->side.fork, hipEventDisableTiming);
+    if (e == hipSuccess)
+        e = hipEventCreateWithFlags(&c->side.join, hipEventDisableTiming);
+    if (cur >= 0 && cur != device)
+        hipSetDevice(cur);
+    if (e != hipSuccess) {
+        apmoe_destroy(c);
+        return hip_fail(e, "side stream of the context");
+    }
     *out = c;
     return ok();
 }
 
 apmoe_status apmoe_destroy(apmoe_ctx *ctx)
 {
+    if (ctx) {
+        if (ctx->side.stream)
+            hipStreamDestroy(ctx->side.stream);
+        if (ctx->side.fork)
+            hipEventDestroy(ctx->side.fork);
+        if (ctx->side.join)
+            hipEventDestroy(ctx->side.join);
+    }
     delete ctx;
     return ok();
 }
@@ -745,7 +771,7 @@ static apmoe_status gemm_common(apmoe_ctx *ctx, const apmoe_table *tbl, int32_t 
             order[n] = (uint8_t)n;
     hipError_t e = apmoe::launch_gemm(slice, kind, tbl->E, N, K, max_q, order, in, in_bytes, gather, perm, offsets,
                                       topk, T * topk, out, out_dtype == APMOE_F32, act,
-                                      reinterpret_cast<hipStream_t>(stream));
+                                      reinterpret_cast<hipStream_t>(stream), ctx->cus, ctx->side);
     return e == hipSuccess ? ok() : hip_fail(e, "gemm launch");
 }
 

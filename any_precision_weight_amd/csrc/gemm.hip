@@ -924,9 +924,12 @@ void launch_kind(const GemmParams &P, hipStream_t s)
 
 }  // namespace
 
+static hipError_t launch_mid(const GemmParams &P, int max_q, int act, int N, int E, hipStream_t s);
+
 hipError_t launch_gemm(const DevBlock *table, int kind, int E, int N, int K, int max_q, const uint8_t *order,
                        const uint16_t *in, size_t in_bytes, int gather, const int32_t *perm, const int32_t *offsets,
-                       int topk, int R, void *out, int out_f32, int act, hipStream_t s)
+                       int topk, int R, void *out, int out_f32, int act, hipStream_t s, int cus,
+                       const SideStream &side)
 {
     GemmParams P;
     P.table = table;
@@ -962,6 +965,26 @@ hipError_t launch_gemm(const DevBlock *table, int kind, int E, int N, int K, int
     P.tokl = tokens <= 16 ? 8 : 16;
     P.max_rows = kDecodeMaxRows;
     P.min_rows = 0;
+    // A tile launch of at most two tiles per CU (by its bound) cannot fill the GPU for
+    // long, and each of its tiles is long: it runs on the context's side stream beside
+    // the decode and mid launches (they serve other experts and write other rows),
+    // forked from the caller's stream before them and joined back after, so the call
+    // stays ordered on the caller's stream.
+    const bool tile = tokens > kMidMaxRows;
+    const bool beside = tile && cus > 0 && tile_grid(N, E, R) <= 2 * cus;
+    hipError_t err = hipSuccess;
+    if (beside) {
+        err = hipEventRecord(side.fork, s);
+        if (err == hipSuccess)
+            err = hipStreamWaitEvent(side.stream, side.fork, 0);
+        if (err == hipSuccess)
+            err = launch_gemm_tile(table, kind, E, N, K, in, in_bytes, gather, perm, offsets, topk, out, out_f32, act, R,
+                                   side.stream);
+        if (err == hipSuccess)
+            err = hipEventRecord(side.join, side.stream);
+        if (err != hipSuccess)
+            return err;
+    }
     // Few workgroups (the down product's N / 64 row blocks) leave two per CU: four
     // column parts then give each CU four waves per SIMD instead of two.
     const bool wide = (long)P.row_blocks * E <= 4 * 256;
@@ -969,9 +992,21 @@ hipError_t launch_gemm(const DevBlock *table, int kind, int E, int N, int K, int
         wide ? launch_kind<APMOE_GATE_UP, 4>(P, s) : launch_kind<APMOE_GATE_UP, 2>(P, s);
     else
         wide ? launch_kind<APMOE_DOWN, 4>(P, s) : launch_kind<APMOE_DOWN, 2>(P, s);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess || tokens <= P.max_rows)
-        return err;  // no expert can have more rows than the decode product takes
+    err = hipGetLastError();
+    if (err == hipSuccess && tokens > P.max_rows)
+        err = launch_mid(P, max_q, act, N, E, s);
+    if (err != hipSuccess || !tile)
+        return err;
+    if (beside)
+        return hipStreamWaitEvent(s, side.join, 0);
+    return launch_gemm_tile(table, kind, E, N, K, in, in_bytes, gather, perm, offsets, topk, out, out_f32, act, R, s);
+}
+
+// The mid product's launch(es) for the experts with kDecodeMaxRows + 1 .. kMidMaxRows rows.
+static hipError_t launch_mid(const GemmParams &P, int max_q, int act, int N, int E, hipStream_t s)
+{
+    hipError_t err = hipSuccess;
+    const int kind = P.kind;
     GemmParams M = P;
     M.min_rows = P.max_rows;
     M.row_blocks = act ? (N / 2) / 64 : (N + kMidRows - 1) / kMidRows;
@@ -999,9 +1034,7 @@ hipError_t launch_gemm(const DevBlock *table, int kind, int E, int N, int K, int
             hipLaunchKernelGGL((gemm_mid_kernel<APMOE_DOWN, kMidAll>), mgrid, dim3(kMidThreads), 0, s, M);
         err = hipGetLastError();
     }
-    if (err != hipSuccess || tokens <= kMidMaxRows)
-        return err;
-    return launch_gemm_tile(table, kind, E, N, K, in, in_bytes, gather, perm, offsets, topk, out, out_f32, act, R, s);
+    return err;
 }
 
 }  // namespace apmoe

@@ -56,12 +56,23 @@ hipError_t launch_route_stats(const float *w, const int32_t *perm, const int32_t
 // product by their row count (read on the device).
 // act = 1 (gate_up only, F = N/2 a multiple of 64): the epilogue applies silu_mul to
 // the fp16-rounded gate row f and up row F + f and writes fp16 a[R][F] to out.
+// A stream of the context beside the caller's, and the events that fork work onto it
+// from the caller's stream and join it back.
+struct SideStream {
+    hipStream_t stream = nullptr;
+    hipEvent_t fork = nullptr;
+    hipEvent_t join = nullptr;
+};
+
+int tile_grid(int N, int E, int R);
+
 // order: the E experts by committed q, highest first, lower index on ties (a
 // scheduling hint: the decode and mid products of a launch with more than 16 experts start
 // the experts in this order; any permutation gives the same result).
 hipError_t launch_gemm(const DevBlock *table, int kind, int E, int N, int K, int max_q, const uint8_t *order,
                        const uint16_t *in, size_t in_bytes, int gather, const int32_t *perm, const int32_t *offsets,
-                       int topk, int R, void *out, int out_f32, int act, hipStream_t s);
+                       int topk, int R, void *out, int out_f32, int act, hipStream_t s, int cus,
+                       const SideStream &side);
 hipError_t launch_gemm_tile(const DevBlock *table, int kind, int E, int N, int K, const uint16_t *in, size_t in_bytes,
                             int gather, const int32_t *perm, const int32_t *offsets, int topk, void *out, int out_f32,
                             int act, int R, hipStream_t s);
