@@ -113,7 +113,9 @@ const char *apmoe_last_error(void);
 int32_t apmoe_version(void);
 
 /* Bind a context to HIP device `device`.  Fails with APMOE_UNSUPPORTED on a
- * device that is not gfx950. */
+ * device that is not gfx950.  The context owns one stream of its own (default
+ * priority) and two events, destroyed by apmoe_destroy; APMOE_HIP_ERROR if they
+ * cannot be created. */
 apmoe_status apmoe_create(apmoe_ctx **out, int device);
 apmoe_status apmoe_destroy(apmoe_ctx *ctx);
 
@@ -281,8 +283,11 @@ apmoe_status apmoe_route_stats(apmoe_ctx *ctx, const float *topk_w, const int32_
 
 /*
  * Any-precision product of every expert of one (layer, kind) in one call: up to
- * three kernel launches on `stream`, by the experts' row counts (up to 32 rows, 33..64,
- * more), each skipped when the batch has too few tokens for any expert to need it.
+ * three kernel launches, by the experts' row counts (up to 32 rows, 33..64, more),
+ * each skipped when the batch has too few tokens for any expert to need it.  A short
+ * launch for the largest experts (at most two tiles per CU) runs on the context's own
+ * stream, forked from `stream` and joined back into it within the call: work
+ * enqueued on `stream` after the call sees the whole product.
  * For expert e, rows r in [offsets[e], offsets[e+1]) of the output:
  *   out[r][n] = sum_c in_row(r)[c] * LUT_q[n][code_q(n, c)],   fp32 accumulation,
  * with q, planes and LUT of block (layer, e, kind) read from the committed
