@@ -65,7 +65,6 @@ def _declare(L):
     L.apo_block_bytes.argtypes = [I64, I64, I32]
     L.apo_route.argtypes = [P, P, P, I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, P, P]
     L.apo_block_gemm.argtypes = [P, P, I32, I64, I64, P, I64, P]
-    L.apo_dequant_block.argtypes = [P, P, I32, I64, I64, P]
     L.apo_act.argtypes = [P, I64, I64, P]
     L.apo_combine.argtypes = [P, P, P, I32, I32, I64, P]
     L.apo_moe_forward.restype = I32
@@ -193,16 +192,6 @@ def block_gemm(planes, lut_q, q: int, inp: np.ndarray) -> np.ndarray:
     assert inp.shape[1] == K
     out = np.empty((M, N), np.float64)
     lib().apo_block_gemm(_p(planes), _p(lut_q), q, N, K, _p(inp), M, _p(out))
-    return out
-
-
-def dequant_block(planes, lut_q, q: int) -> np.ndarray:
-    planes = _c(planes, np.uint32)
-    lut_q = _c(lut_q, np.float16).view(np.uint16)
-    _, N, W = planes.shape
-    K = W * 32
-    out = np.empty((N, K), np.float64)
-    lib().apo_dequant_block(_p(planes), _p(lut_q), q, N, K, _p(out))
     return out
 
 

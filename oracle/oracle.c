@@ -29,7 +29,9 @@
  * pack/unpack round trip, identity LUT == exact integer matmul, constant LUT closed
  * form, brute force on tiny shapes (independent Python), E=1/k=1/q=8 == dense FFN,
  * LUT ordering invariants, permutation invariants, fp16 conversion against numpy,
- * Eq. 3 byte count.
+ * Eq. 3 byte count, activation against scipy's logistic function, combine on a
+ * hand-worked dyadic example, as a gather at top-1, and equal to the layer's own
+ * accumulation.  Every exported function is pinned.
  */
 #include <math.h>
 #include <stdint.h>
@@ -297,14 +299,6 @@ void apo_block_gemm(const uint32_t *planes, const uint16_t *lut_q, int q, int64_
         }
         free(row);
     }
-}
-
-/* Dequantised block W [N][K] in fp64 (tests on small shapes). */
-void apo_dequant_block(const uint32_t *planes, const uint16_t *lut_q, int q, int64_t N, int64_t K, double *W)
-{
-#pragma omp parallel for schedule(static)
-    for (int64_t n = 0; n < N; ++n)
-        dequant_row(planes, lut_q, q, N, K, n, W + n * K);
 }
 
 /* a[m][f] = SiLU(h[m][f]) * h[m][F + f], SiLU(z) = z / (1 + e^{-z}). */

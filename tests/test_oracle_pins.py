@@ -185,6 +185,57 @@ def test_one_hot_activation_reads_one_centroid():
             assert np.array_equal(got, ref)
 
 
+# ---------------------------------------------------------------- act, combine --
+
+def test_act_matches_scipy_logistic():
+    """Expert activation (Section 3.3): a = SiLU(gate) * up with SiLU(z) = z * sigmoid(z),
+    gate = columns [0, F) and up = columns [F, 2F) of h.  Checked against scipy's
+    logistic function on random values (a swapped gate/up or a dropped factor fails),
+    plus the exact zeros of a zero gate or a zero up."""
+    from scipy.special import expit
+    F = 7
+    h = RNG.normal(0, 3, size=(5, 2 * F))
+    h[0, :F] = 0.0
+    h[1, F:] = 0.0
+    a = oracle.act(h)
+    g, u = h[:, :F], h[:, F:]
+    assert np.allclose(a, g * expit(g) * u, rtol=1e-14, atol=0)
+    assert np.all(a[0] == 0.0) and np.all(a[1] == 0.0)
+
+
+def test_combine_hand_example():
+    """Output accumulation (Section 3.3): out[t] = sum_j w[t][j] * y[inv_perm[t*k + j]].
+    Two tokens, top-2, dyadic weights and values, so every sum is exact; the expected
+    rows are worked out by hand."""
+    y = np.array([[1.0, -2.0, 4.0],
+                  [8.0, 0.5, -1.0],
+                  [-3.0, 6.0, 2.0],
+                  [0.25, 1.0, -8.0]])
+    w = np.array([[0.75, 0.25], [0.5, 0.5]])
+    inv_perm = np.array([2, 0, 3, 1], np.int32)  # token 0 -> rows 2, 0; token 1 -> rows 3, 1
+    out = oracle.combine(y, w, inv_perm, 2)
+    # token 0: 0.75 * [-3, 6, 2] + 0.25 * [1, -2, 4]
+    # token 1: 0.5 * [0.25, 1, -8] + 0.5 * [8, 0.5, -1]
+    assert np.array_equal(out, np.array([[-2.0, 4.0, 2.5], [4.125, 0.75, -4.5]]))
+
+
+def test_combine_single_choice_is_a_gather():
+    """With top-1 and routing weight 1 the accumulation is the row gather y[inv_perm[t]]."""
+    y = RNG.normal(0, 1, size=(6, 5))
+    inv_perm = np.array([4, 0, 5, 1, 3, 2], np.int32)
+    out = oracle.combine(y, np.ones((6, 1)), inv_perm, 1)
+    assert np.array_equal(out, y[inv_perm])
+
+
+def test_combine_equals_layer_accumulation():
+    """The combine of the tiny layer's own y, weights and inv_perm gives the layer
+    output bit for bit (the same slot order); the layer is pinned by brute force."""
+    cfg, x, wr, pg, pd, lg, ld, q = _tiny_layer()
+    r = oracle.moe_forward(x, wr, None, cfg.topk, pg, lg, q[:, 0], pd, ld, q[:, 1], intermediates=True)
+    out = oracle.combine(r["y"], r["w64"], r["inv_perm"], cfg.topk)
+    assert np.array_equal(out, r["out"])
+
+
 # ---------------------------------------------------------------- route -------
 
 def _route_case(T, H, E, seed, bias=True):
