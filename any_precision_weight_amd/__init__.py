@@ -15,6 +15,8 @@ import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libapmoe.so")
+# the same library built with every counted vector-memory wait drained to zero
+SAFE_LIB_PATH = os.path.join(_HERE, "libapmoe_safe.so")
 
 OK, INVALID_ARG, UNSUPPORTED, NOT_RESIDENT, HIP_ERROR, OUT_OF_MEMORY = range(6)
 GATE_UP, DOWN = 0, 1
@@ -25,7 +27,7 @@ EXPORTED = [
     "apmoe_status_string", "apmoe_last_error", "apmoe_version", "apmoe_create", "apmoe_destroy",
     "apmoe_block_bytes", "apmoe_table_create", "apmoe_table_destroy", "apmoe_table_set_block",
     "apmoe_table_set_bits", "apmoe_table_set_plane", "apmoe_table_validate", "apmoe_table_committed_bits",
-    "apmoe_table_commit", "apmoe_lut_build", "apmoe_tiled_plane_words", "apmoe_tile_planes", "apmoe_pack_planes", "apmoe_route", "apmoe_route_stats", "apmoe_gemm",
+    "apmoe_table_commit", "apmoe_lut_build", "apmoe_tiled_plane_words", "apmoe_tile_planes", "apmoe_pack_planes", "apmoe_route", "apmoe_route_workspace", "apmoe_route_stats", "apmoe_gemm",
     "apmoe_gemm_act", "apmoe_act",
     "apmoe_combine", "apmoe_moe_workspace", "apmoe_moe_forward", "apmoe_page_out", "apmoe_page_in",
 ]
@@ -56,15 +58,27 @@ def _status_text(s: int) -> str:
         return "?"
 
 
+_loaded: dict[str, ctypes.CDLL] = {}
+
+
+def load_library(path: str) -> ctypes.CDLL:
+    """Load a libapmoe build (once per path; raises if it has not been built).
+    Contexts and tables remember the library that made them, so two builds can be
+    used side by side in one process."""
+    if path not in _loaded:
+        if not os.path.exists(path):
+            raise ImportError(f"{path} is missing: build it with `python -m any_precision_weight_amd.build`")
+        L = ctypes.CDLL(path)
+        _declare(L)
+        _loaded[path] = L
+    return _loaded[path]
+
+
 def lib() -> ctypes.CDLL:
-    """Load libapmoe.so (raises if it has not been built)."""
+    """The default build, libapmoe.so."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise ImportError(f"{LIB_PATH} is missing: build it with `python -m any_precision_weight_amd.build`")
-        L = ctypes.CDLL(LIB_PATH)
-        _declare(L)
-        _lib = L
+        _lib = load_library(LIB_PATH)
     return _lib
 
 
@@ -91,6 +105,7 @@ def _declare(L):
         "apmoe_tile_planes": (S, [P, P, I32, I32, P, P]),
         "apmoe_pack_planes": (S, [P, P, I32, I32, P, P]),
         "apmoe_route": (S, [P, P, P, P, I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, P]),
+        "apmoe_route_workspace": (S, [P, I32, I32, I32, I32, ctypes.POINTER(SZ)]),
         "apmoe_route_stats": (S, [P, P, P, P, I32, I32, I32, P, P, P, P]),
         "apmoe_gemm": (S, [P, P, I32, I32, P, I32, P, P, I32, I32, P, I32, P]),
         "apmoe_gemm_act": (S, [P, P, I32, P, I32, P, P, I32, I32, P, P]),
@@ -107,9 +122,9 @@ def _declare(L):
         f.argtypes = args
 
 
-def _check(status: int, fn: str) -> None:
+def _check(status: int, fn: str, L: ctypes.CDLL | None = None) -> None:
     if status != OK:
-        raise ApmoeError(status, fn, lib().apmoe_last_error().decode())
+        raise ApmoeError(status, fn, (L or lib()).apmoe_last_error().decode())
 
 
 def ptr(t) -> int | None:
@@ -140,15 +155,16 @@ def block_bytes(n: int, k: int, b: int) -> int:
 class Context:
     """apmoe_create / apmoe_destroy."""
 
-    def __init__(self, device: int = 0):
+    def __init__(self, device: int = 0, library: ctypes.CDLL | None = None):
+        self.L = lib() if library is None else library
         h = ctypes.c_void_p()
-        _check(lib().apmoe_create(ctypes.byref(h), device), "apmoe_create")
+        _check(self.L.apmoe_create(ctypes.byref(h), device), "apmoe_create", self.L)
         self.handle = h.value
         self.device = device
 
     def close(self):
         if self.handle:
-            lib().apmoe_destroy(self.handle)
+            self.L.apmoe_destroy(self.handle)
             self.handle = None
 
     def __del__(self):  # pragma: no cover
@@ -161,9 +177,10 @@ class Context:
 class Table:
     """apmoe_table_* : staging, validation and stream-ordered commit."""
 
-    def __init__(self, n_layers: int, n_experts: int):
+    def __init__(self, n_layers: int, n_experts: int, library: ctypes.CDLL | None = None):
+        self.L = lib() if library is None else library
         h = ctypes.c_void_p()
-        _check(lib().apmoe_table_create(n_layers, n_experts, ctypes.byref(h)), "apmoe_table_create")
+        _check(self.L.apmoe_table_create(n_layers, n_experts, ctypes.byref(h)), "apmoe_table_create", self.L)
         self.handle = h.value
         self.n_layers, self.n_experts = n_layers, n_experts
 
@@ -183,32 +200,32 @@ class Table:
         desc.resident_mask = mask if resident_mask is None else resident_mask
         for b in range(MAX_BITS + 1):
             desc.lut[b] = ptr(luts.get(b)) if b in luts else None
-        _check(lib().apmoe_table_set_block(self.handle, layer, expert, kind, ctypes.byref(desc)),
-               "apmoe_table_set_block")
+        _check(self.L.apmoe_table_set_block(self.handle, layer, expert, kind, ctypes.byref(desc)),
+               "apmoe_table_set_block", self.L)
 
     def set_bits(self, layer: int, expert: int, kind: int, q: int) -> None:
-        _check(lib().apmoe_table_set_bits(self.handle, layer, expert, kind, q), "apmoe_table_set_bits")
+        _check(self.L.apmoe_table_set_bits(self.handle, layer, expert, kind, q), "apmoe_table_set_bits", self.L)
 
     def set_plane(self, layer: int, expert: int, kind: int, p: int, plane, resident: bool) -> None:
-        _check(lib().apmoe_table_set_plane(self.handle, layer, expert, kind, p, ptr(plane), int(resident)),
-               "apmoe_table_set_plane")
+        _check(self.L.apmoe_table_set_plane(self.handle, layer, expert, kind, p, ptr(plane), int(resident)),
+               "apmoe_table_set_plane", self.L)
 
     def validate(self) -> int:
         """Status apmoe_table_commit would return (no exception)."""
-        return int(lib().apmoe_table_validate(self.handle))
+        return int(self.L.apmoe_table_validate(self.handle))
 
     def committed_bits(self, layer: int, expert: int, kind: int) -> int:
         q = ctypes.c_int32()
-        _check(lib().apmoe_table_committed_bits(self.handle, layer, expert, kind, ctypes.byref(q)),
-               "apmoe_table_committed_bits")
+        _check(self.L.apmoe_table_committed_bits(self.handle, layer, expert, kind, ctypes.byref(q)),
+               "apmoe_table_committed_bits", self.L)
         return q.value
 
     def commit(self, ctx: Context, stream=None) -> None:
-        _check(lib().apmoe_table_commit(ctx.handle, self.handle, stream_handle(stream)), "apmoe_table_commit")
+        _check(self.L.apmoe_table_commit(ctx.handle, self.handle, stream_handle(stream)), "apmoe_table_commit", self.L)
 
     def close(self):
         if self.handle:
-            lib().apmoe_table_destroy(self.handle)
+            self.L.apmoe_table_destroy(self.handle)
             self.handle = None
 
     def __del__(self):  # pragma: no cover
@@ -220,8 +237,8 @@ class Table:
 
 def lut_build(ctx: Context, parent, n: int, levels: dict, stream=None) -> None:
     arr = (ctypes.c_void_p * (MAX_BITS + 1))(*[ptr(levels.get(b)) for b in range(MAX_BITS + 1)])
-    _check(lib().apmoe_lut_build(ctx.handle, ptr(parent), n, ctypes.cast(arr, ctypes.c_void_p),
-                                 stream_handle(stream)), "apmoe_lut_build")
+    _check(ctx.L.apmoe_lut_build(ctx.handle, ptr(parent), n, ctypes.cast(arr, ctypes.c_void_p),
+                                 stream_handle(stream)), "apmoe_lut_build", ctx.L)
 
 
 def tiled_plane_words(n: int, k: int) -> int:
@@ -229,13 +246,13 @@ def tiled_plane_words(n: int, k: int) -> int:
 
 
 def tile_planes(ctx: Context, canonical, n: int, k: int, tiled, stream=None) -> None:
-    _check(lib().apmoe_tile_planes(ctx.handle, ptr(canonical), n, k, ptr(tiled), stream_handle(stream)),
-           "apmoe_tile_planes")
+    _check(ctx.L.apmoe_tile_planes(ctx.handle, ptr(canonical), n, k, ptr(tiled), stream_handle(stream)),
+           "apmoe_tile_planes", ctx.L)
 
 
 def pack_planes(ctx: Context, codes, n: int, k: int, planes, stream=None) -> None:
-    _check(lib().apmoe_pack_planes(ctx.handle, ptr(codes), n, k, ptr(planes), stream_handle(stream)),
-           "apmoe_pack_planes")
+    _check(ctx.L.apmoe_pack_planes(ctx.handle, ptr(codes), n, k, ptr(planes), stream_handle(stream)),
+           "apmoe_pack_planes", ctx.L)
 
 
 def route(ctx: Context, x, w_router, bias, T: int, H: int, E: int, topk: int, renormalize: bool, topk_ids,
@@ -243,54 +260,62 @@ def route(ctx: Context, x, w_router, bias, T: int, H: int, E: int, topk: int, re
     """Top-k routing over E routed experts; with n_shared > 0 each token's row of
     topk_ids / topk_w (stride topk + n_shared) ends with the shared experts
     E .. E + n_shared - 1 at weight 1, and counts / offsets cover E + n_shared experts."""
-    _check(lib().apmoe_route(ctx.handle, ptr(x), ptr(w_router), ptr(bias), T, H, E, topk, n_shared, int(renormalize),
+    _check(ctx.L.apmoe_route(ctx.handle, ptr(x), ptr(w_router), ptr(bias), T, H, E, topk, n_shared, int(renormalize),
                              ptr(topk_ids), ptr(topk_w), ptr(counts), ptr(offsets), ptr(perm), ptr(inv_perm),
-                             stream_handle(stream)), "apmoe_route")
+                             stream_handle(stream)), "apmoe_route", ctx.L)
+
+
+def route_workspace(ctx: Context, T: int, E: int, topk: int, n_shared: int = 0) -> int:
+    n = ctypes.c_size_t()
+    _check(ctx.L.apmoe_route_workspace(ctx.handle, T, E, topk, n_shared, ctypes.byref(n)), "apmoe_route_workspace",
+           ctx.L)
+    return n.value
 
 
 def route_stats(ctx: Context, topk_w, perm, offsets, T: int, topk: int, E: int, mass, total, selections,
                 stream=None) -> None:
     """Add one routed batch to the routing-statistics accumulators (Eq. 1):
     mass[E] fp64, total[1] fp64, selections[E] int64, all device memory."""
-    _check(lib().apmoe_route_stats(ctx.handle, ptr(topk_w), ptr(perm), ptr(offsets), T, topk, E, ptr(mass),
-                                   ptr(total), ptr(selections), stream_handle(stream)), "apmoe_route_stats")
+    _check(ctx.L.apmoe_route_stats(ctx.handle, ptr(topk_w), ptr(perm), ptr(offsets), T, topk, E, ptr(mass),
+                                   ptr(total), ptr(selections), stream_handle(stream)), "apmoe_route_stats", ctx.L)
 
 
 def gemm(ctx: Context, table: Table, layer: int, kind: int, inp, gather: bool, perm, offsets, T: int, topk: int,
          out, out_dtype: int, stream=None) -> None:
-    _check(lib().apmoe_gemm(ctx.handle, table.handle, layer, kind, ptr(inp), int(gather), ptr(perm), ptr(offsets),
-                            T, topk, ptr(out), out_dtype, stream_handle(stream)), "apmoe_gemm")
+    _check(ctx.L.apmoe_gemm(ctx.handle, table.handle, layer, kind, ptr(inp), int(gather), ptr(perm), ptr(offsets),
+                            T, topk, ptr(out), out_dtype, stream_handle(stream)), "apmoe_gemm", ctx.L)
 
 
 def gemm_act(ctx: Context, table: Table, layer: int, x, gather: bool, perm, offsets, T: int, topk: int, a,
              stream=None) -> None:
     """gate_up product with SiLU(gate) * up in its epilogue: fp16 a [T*topk][F]."""
-    _check(lib().apmoe_gemm_act(ctx.handle, table.handle, layer, ptr(x), int(gather), ptr(perm), ptr(offsets), T,
-                                topk, ptr(a), stream_handle(stream)), "apmoe_gemm_act")
+    _check(ctx.L.apmoe_gemm_act(ctx.handle, table.handle, layer, ptr(x), int(gather), ptr(perm), ptr(offsets), T,
+                                topk, ptr(a), stream_handle(stream)), "apmoe_gemm_act", ctx.L)
 
 
 def act(ctx: Context, h, R: int, F: int, a, stream=None) -> None:
-    _check(lib().apmoe_act(ctx.handle, ptr(h), R, F, ptr(a), stream_handle(stream)), "apmoe_act")
+    _check(ctx.L.apmoe_act(ctx.handle, ptr(h), R, F, ptr(a), stream_handle(stream)), "apmoe_act", ctx.L)
 
 
 def combine(ctx: Context, y, y_dtype: int, topk_w, inv_perm, T: int, topk: int, H: int, out, stream=None) -> None:
-    _check(lib().apmoe_combine(ctx.handle, ptr(y), y_dtype, ptr(topk_w), ptr(inv_perm), T, topk, H, ptr(out),
-                               stream_handle(stream)), "apmoe_combine")
+    _check(ctx.L.apmoe_combine(ctx.handle, ptr(y), y_dtype, ptr(topk_w), ptr(inv_perm), T, topk, H, ptr(out),
+                               stream_handle(stream)), "apmoe_combine", ctx.L)
 
 
 def moe_workspace(table: Table, layer: int, T: int, topk: int, n_shared: int = 0) -> int:
     n = ctypes.c_size_t()
-    _check(lib().apmoe_moe_workspace(table.handle, layer, T, topk, n_shared, ctypes.byref(n)), "apmoe_moe_workspace")
+    _check(table.L.apmoe_moe_workspace(table.handle, layer, T, topk, n_shared, ctypes.byref(n)), "apmoe_moe_workspace",
+           table.L)
     return n.value
 
 
 def moe_forward(ctx: Context, table: Table, layer: int, x, w_router, bias, T: int, topk: int, renormalize: bool,
                 ws, ws_bytes: int, out, stream=None, n_shared: int = 0) -> None:
     """Whole layer; the table's last n_shared experts of the layer are shared ones."""
-    _check(lib().apmoe_moe_forward(ctx.handle, table.handle, layer, ptr(x), ptr(w_router), ptr(bias), T, topk,
+    _check(ctx.L.apmoe_moe_forward(ctx.handle, table.handle, layer, ptr(x), ptr(w_router), ptr(bias), T, topk,
                                    n_shared,
                                    int(renormalize), ptr(ws), ws_bytes, ptr(out), stream_handle(stream)),
-           "apmoe_moe_forward")
+           "apmoe_moe_forward", ctx.L)
 
 
 # --------------------------------------------------------------------------- page movement
@@ -315,9 +340,9 @@ def page_out(ctx: Context, table: Table, layer: int, expert: int, kind: int, q_n
     """Lower (layer, expert, kind) to q_new and copy planes q_new.. to host_planes[p]
     (8-entry list; pinned tensors).  done_event (torch.cuda.Event) completes once the
     device planes may be freed."""
-    _check(lib().apmoe_page_out(ctx.handle, table.handle, layer, expert, kind, q_new, _plane_array(host_planes),
+    _check(ctx.L.apmoe_page_out(ctx.handle, table.handle, layer, expert, kind, q_new, _plane_array(host_planes),
                                 stream_handle(stream), stream_handle(copy_stream),
-                                _event_handle(done_event, copy_stream)), "apmoe_page_out")
+                                _event_handle(done_event, copy_stream)), "apmoe_page_out", ctx.L)
 
 
 def page_in(ctx: Context, table: Table, layer: int, expert: int, kind: int, q_new: int, host_planes, dev_planes,
@@ -325,6 +350,6 @@ def page_in(ctx: Context, table: Table, layer: int, expert: int, kind: int, q_ne
     """Copy host_planes[p] to dev_planes[p] for the planes above the current bitwidth,
     then raise (layer, expert, kind) to q_new with a commit on `stream` that waits for
     the copies."""
-    _check(lib().apmoe_page_in(ctx.handle, table.handle, layer, expert, kind, q_new, _plane_array(host_planes),
+    _check(ctx.L.apmoe_page_in(ctx.handle, table.handle, layer, expert, kind, q_new, _plane_array(host_planes),
                                _plane_array(dev_planes), stream_handle(stream), stream_handle(copy_stream),
-                               _event_handle(copied_event, copy_stream)), "apmoe_page_in")
+                               _event_handle(copied_event, copy_stream)), "apmoe_page_in", ctx.L)

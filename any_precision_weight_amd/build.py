@@ -1,4 +1,7 @@
-"""Build libapmoe.so (HIP, gfx950) in-tree with hipcc.
+"""Build libapmoe.so (HIP, gfx950) in-tree with hipcc, and libapmoe_safe.so: the
+same sources with APMOE_SAFE_WAITS defined, where every counted wait for vector
+memory requests drains all of them (slower, never early).  The tests run both and
+require identical output bits.
 
 Usage: python -m any_precision_weight_amd.build
 """
@@ -14,6 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libapmoe.so")
+SAFE_LIB = os.path.join(PKG, "libapmoe_safe.so")
 SOURCES = ["api.hip", "route.hip", "gemm.hip", "gemm_tile.hip", "elementwise.hip"]
 ARCH = "gfx950"
 
@@ -26,27 +30,41 @@ FLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(job) -> str:
+    src, variant = job
+    out_dir = os.path.join(BUILD, variant)
+    obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
+    extra = ["-DAPMOE_SAFE_WAITS"] if variant == "safe" else []
+    cmd = [HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
+        raise RuntimeError(f"hipcc failed for {src} ({variant}):\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib):
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False, safe: bool = True) -> str:
+    variants = ["main", "safe"] if safe else ["main"]
+    for v in variants:
+        os.makedirs(os.path.join(BUILD, v), exist_ok=True)
+    jobs = [(src, v) for v in variants for src in SOURCES]
+    workers = min(len(jobs), int(os.environ.get("MAX_JOBS", "8")))
+    with cf.ThreadPoolExecutor(max_workers=workers) as ex:
+        objs = list(ex.map(_compile, jobs))
+    n = len(SOURCES)
+    _link(objs[:n], LIB)
+    if safe:
+        _link(objs[n:], SAFE_LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", SAFE_LIB if safe else "(no safe-wait build)")
     return LIB
 
 

@@ -54,6 +54,7 @@ struct apmoe_ctx {
     apmoe::SideStream side;  // runs a short tile launch beside the decode and mid launches
 };
 
+
 struct apmoe_table {
     int L, E;
     std::vector<apmoe_block_desc> staged;
@@ -546,6 +547,23 @@ apmoe_status apmoe_route(apmoe_ctx *ctx, const uint16_t *x, const uint16_t *w_ro
     return ok();
 }
 
+apmoe_status apmoe_route_workspace(apmoe_ctx *ctx, int32_t T, int32_t E, int32_t topk, int32_t n_shared,
+                                   size_t *bytes)
+{
+    apmoe_status s = check_ctx(ctx);
+    if (s != APMOE_OK)
+        return s;
+    if (!bytes)
+        return fail(APMOE_INVALID_ARG, "bytes is NULL");
+    if (T < 0 || E < 1 || E > APMOE_MAX_EXPERTS || topk < 1 || topk > E || topk > APMOE_MAX_TOPK || n_shared < 0 ||
+        n_shared > APMOE_MAX_SHARED || E + n_shared > APMOE_MAX_EXPERTS)
+        return fail(APMOE_INVALID_ARG, "T=%d E=%d topk=%d n_shared=%d", T, E, topk, n_shared);
+    // the selection runs in one workgroup per token and the grouping sort in the LDS
+    // of one workgroup: the route writes only its outputs
+    *bytes = 0;
+    return ok();
+}
+
 // ---- page movement ----------------------------------------------------------------
 
 static apmoe_status page_common(apmoe_ctx *ctx, apmoe_table *t, int32_t layer, int32_t expert, int32_t kind,
@@ -719,6 +737,26 @@ static apmoe_status layer_shape(const apmoe_table *t, int layer, int kind, int *
     return ok();
 }
 
+// Size limits of one product call (every buffer a kernel addresses through a 32-bit
+// buffer offset stays below 2 GiB); checked before anything is enqueued.
+static apmoe_status gemm_limits(const apmoe_table *tbl, int layer, int kind, int T, int topk, int gather, int act,
+                                int *N, int *K, int *max_q, size_t *in_bytes)
+{
+    apmoe_status s = layer_shape(tbl, layer, kind, N, K, max_q);
+    if (s != APMOE_OK)
+        return s;
+    if (act && (*N % 128 != 0))
+        return fail(APMOE_INVALID_ARG, "gate_up has %d rows: the fused activation needs F = N/2 a multiple of 64", *N);
+    const size_t in_rows = gather ? (size_t)T : (size_t)T * topk;
+    *in_bytes = in_rows * (size_t)*K * 2;
+    const size_t plane_bytes = apmoe::tiled_plane_words(*N, *K) * 4;
+    if (*in_bytes >= ((size_t)1 << 31) || plane_bytes >= ((size_t)1 << 31) ||
+        ((size_t)*N << (*max_q + 1)) >= ((size_t)1 << 31))
+        return fail(APMOE_INVALID_ARG, "operands above 2 GiB per buffer are not supported (in %zu B, plane %zu B)",
+                    *in_bytes, plane_bytes);
+    return ok();
+}
+
 static apmoe_status gemm_common(apmoe_ctx *ctx, const apmoe_table *tbl, int32_t layer, int32_t kind,
                                 const uint16_t *in, int32_t gather, const int32_t *perm, const int32_t *offsets,
                                 int32_t T, int32_t topk, void *out, int32_t out_dtype, int act, void *stream)
@@ -746,17 +784,10 @@ static apmoe_status gemm_common(apmoe_ctx *ctx, const apmoe_table *tbl, int32_t 
     if (!aligned16(in) || !aligned16(out))
         return fail(APMOE_INVALID_ARG, "in / out not 16-byte aligned");
     int N, K, max_q;
-    s = layer_shape(tbl, layer, kind, &N, &K, &max_q);
+    size_t in_bytes;
+    s = gemm_limits(tbl, layer, kind, T, topk, gather, act, &N, &K, &max_q, &in_bytes);
     if (s != APMOE_OK)
         return s;
-    if (act && (N % 128 != 0))
-        return fail(APMOE_INVALID_ARG, "gate_up has %d rows: the fused activation needs F = N/2 a multiple of 64", N);
-    const size_t in_rows = gather ? (size_t)T : (size_t)T * topk;
-    const size_t in_bytes = in_rows * (size_t)K * 2;
-    const size_t plane_bytes = apmoe::tiled_plane_words(N, K) * 4;
-    if (in_bytes >= ((size_t)1 << 31) || plane_bytes >= ((size_t)1 << 31) || ((size_t)N << (max_q + 1)) >= ((size_t)1 << 31))
-        return fail(APMOE_INVALID_ARG, "operands above 2 GiB per buffer are not supported (in %zu B, plane %zu B)",
-                    in_bytes, plane_bytes);
     const DevBlock *slice = tbl->d_table + tbl->index(layer, 0, 0);
     // experts by committed q, highest first (stable): the order in which the decode and mid
     // products start them when the layer has more than 16 experts (a scheduling hint)
@@ -900,11 +931,33 @@ apmoe_status apmoe_moe_forward(apmoe_ctx *ctx, const apmoe_table *tbl, int32_t l
     if (n_shared < 0 || n_shared >= tbl->E)
         return fail(APMOE_INVALID_ARG, "n_shared=%d with %d experts in the table", n_shared, tbl->E);
     const int kt = topk + n_shared;  // assignments per token
+    // every limit of the four steps is checked before the first launch, so a refused
+    // call enqueues nothing
+    if (T < 0 || topk < 1 || topk > tbl->E - n_shared || topk > APMOE_MAX_TOPK || H % 8 != 0)
+        return fail(APMOE_INVALID_ARG, "T=%d topk=%d H=%d", T, topk, H);
+    if ((int64_t)T * kt > (int64_t)1 << 30)
+        return fail(APMOE_INVALID_ARG, "T*topk too large");
     const WsLayout L = ws_layout(T, kt, tbl->E, H, F);
     if (!ws || ws_bytes < L.total || ((uintptr_t)ws & 255u))
         return fail(APMOE_INVALID_ARG, "workspace NULL, unaligned or smaller than %zu bytes", L.total);
     if (T > 0 && (!out || !aligned16(out)))
         return fail(APMOE_INVALID_ARG, "out NULL or misaligned");
+    if (T > 0 && (!x || !w_router || !aligned16(x) || !aligned16(w_router)))
+        return fail(APMOE_INVALID_ARG, "x / w_router NULL or not 16-byte aligned");
+    if (T > 0) {
+        if (!tbl->committed_once || !tbl->d_table)
+            return fail(APMOE_NOT_RESIDENT, "table was never committed");
+        if (tbl->device != ctx->device)
+            return fail(APMOE_INVALID_ARG, "table lives on device %d, ctx on %d", tbl->device, ctx->device);
+        int n_, k_, q_;
+        size_t b_;
+        s = gemm_limits(tbl, layer, APMOE_GATE_UP, T, kt, 1, 1, &n_, &k_, &q_, &b_);
+        if (s != APMOE_OK)
+            return s;
+        s = gemm_limits(tbl, layer, APMOE_DOWN, T, kt, 0, 0, &n_, &k_, &q_, &b_);
+        if (s != APMOE_OK)
+            return s;
+    }
     char *w = reinterpret_cast<char *>(ws);
     int32_t *ids = reinterpret_cast<int32_t *>(w + L.ids);
     float *tw = reinterpret_cast<float *>(w + L.w);

@@ -1,0 +1,103 @@
+// device.h -- device helpers shared by the expert-product kernels (not installed):
+// buffer resources, the bit transpose that turns plane words into codes, LDS
+// access, and the s_waitcnt immediates of the counted waits.
+#pragma once
+
+#include "internal.h"
+
+namespace apmoe {
+
+constexpr int kWave = 64;
+constexpr int kXcds = 8;  // accelerator complex dies; workgroup b runs on XCD b % 8
+
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float float16v __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource (base, byte range) in scalar registers: loads take a 32-bit lane
+// offset and return zeros past the range.  Word 3 is the gfx9-family raw-buffer
+// configuration.
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// The low q bits of c in reverse order.
+__device__ inline uint32_t bitrev(uint32_t c, int q) { return __builtin_bitreverse32(c) >> (32 - q); }
+
+// Exchange the bits of b under m with the bits of a under m << s.  BFI: two
+// bit-field inserts from the original pair (four instructions); otherwise the xor
+// form (five), which the compiler folds further when some words are known zero.
+template <bool BFI>
+__device__ inline void swap_bits(uint32_t &a, uint32_t &b, int s, uint32_t m)
+{
+    if constexpr (BFI) {
+        const uint32_t nb = (m & (a >> s)) | (~m & b);
+        const uint32_t na = ((m << s) & (b << s)) | (~(m << s) & a);
+        a = na;
+        b = nb;
+    } else {
+        const uint32_t t = ((a >> s) ^ b) & m;
+        b ^= t;
+        a ^= t << s;
+    }
+}
+
+// In-place transpose of 4 independent 8x8 bit blocks (the delta-swap method of
+// Hacker's Delight, section 7-3): on input d[p] byte b bit j is plane p, column
+// 8b+j; on output d[j] byte b bit p holds the same bit.
+template <bool BFI>
+__device__ inline void transpose8x8(uint32_t (&d)[8])
+{
+    swap_bits<BFI>(d[0], d[4], 4, 0x0F0F0F0Fu);
+    swap_bits<BFI>(d[1], d[5], 4, 0x0F0F0F0Fu);
+    swap_bits<BFI>(d[2], d[6], 4, 0x0F0F0F0Fu);
+    swap_bits<BFI>(d[3], d[7], 4, 0x0F0F0F0Fu);
+    swap_bits<BFI>(d[0], d[2], 2, 0x33333333u);
+    swap_bits<BFI>(d[1], d[3], 2, 0x33333333u);
+    swap_bits<BFI>(d[4], d[6], 2, 0x33333333u);
+    swap_bits<BFI>(d[5], d[7], 2, 0x33333333u);
+    swap_bits<BFI>(d[0], d[1], 1, 0x55555555u);
+    swap_bits<BFI>(d[2], d[3], 1, 0x55555555u);
+    swap_bits<BFI>(d[4], d[5], 1, 0x55555555u);
+    swap_bits<BFI>(d[6], d[7], 1, 0x55555555u);
+}
+
+// LDS byte address of a pointer into a __shared__ array.
+__device__ inline uint32_t lds_addr(const void *p)
+{
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)p;
+}
+
+__device__ inline u32x4 lds_b128(uint32_t addr)
+{
+    return *reinterpret_cast<const __attribute__((address_space(3))) u32x4 *>((uintptr_t)addr);
+}
+
+__device__ inline void lds_store_b128(uint32_t addr, u32x4 v)
+{
+    *reinterpret_cast<__attribute__((address_space(3))) u32x4 *>((uintptr_t)addr) = v;
+}
+
+// s_waitcnt immediates: vmcnt in bits 3:0 and 15:14, expcnt (6:4) left open,
+// lgkmcnt (11:8) zero.  The pipelines wait for exactly the vector-memory requests
+// that must have landed and leave later ones in flight.  A build with
+// APMOE_SAFE_WAITS defined counts every such wait down to zero instead: it drains
+// every outstanding request (slower, never early), and must give identical bits.
+#ifdef APMOE_SAFE_WAITS
+constexpr bool kSafeWaits = true;
+#else
+constexpr bool kSafeWaits = false;
+#endif
+constexpr int kWaitAll = 7 << 4;
+template <int VM>
+constexpr int wait_vm()
+{
+    static_assert(VM >= 0 && VM < 64, "vmcnt range");
+    constexpr int v = kSafeWaits ? 0 : VM;
+    return (v & 15) | (7 << 4) | ((v >> 4) << 14);
+}
+
+}  // namespace apmoe

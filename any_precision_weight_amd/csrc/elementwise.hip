@@ -1,6 +1,7 @@
 // elementwise.hip -- expert activation, output accumulation and the format tools
 // (PagedWeight, Section 3.3: "expert activation ... output accumulation"; Section 3
 // / Figure 3 caption: per-bitwidth centroid LUTs over overlaid bit-planes).
+#include "fp16_rne.h"
 #include "internal.h"
 
 namespace apmoe {
@@ -68,54 +69,6 @@ __global__ void __launch_bounds__(256) combine_kernel(const void *__restrict__ y
     *reinterpret_cast<uint4 *>(out + t * H + n) = __builtin_bit_cast(uint4, o);
 }
 
-// fp64 -> fp16 bits, round to nearest, ties to even, from the IEEE 754 encodings.
-__device__ inline uint16_t d2h_rne(double d)
-{
-    const uint64_t u = __builtin_bit_cast(uint64_t, d);
-    const uint16_t sign = (uint16_t)((u >> 48) & 0x8000u);
-    const int exp = (int)((u >> 52) & 0x7FF);
-    uint64_t mant = u & ((1ull << 52) - 1);
-    if (exp == 0x7FF)
-        return sign | (mant ? 0x7E00 : 0x7C00);
-    if (exp == 0 && mant == 0)
-        return sign;
-    // value = 1.mant * 2^(exp-1023) for normal doubles (doubles here are never subnormal)
-    const int e = exp - 1023;
-    const uint64_t sig = mant | (1ull << 52);  // 53-bit significand
-    int shift;
-    uint32_t hexp;
-    if (e >= -14) {
-        if (e > 15)
-            return sign | 0x7C00;
-        shift = 52 - 10;  // keep 11 bits
-        hexp = (uint32_t)(e + 15);
-    } else {
-        // subnormal half: quantum 2^-24, value / 2^-24 = sig * 2^(e - 52 + 24)
-        shift = 52 - 10 + (-14 - e);
-        hexp = 0;
-        if (shift > 63)
-            return sign;
-    }
-    uint64_t q = sig >> shift;
-    const uint64_t rem = sig & ((1ull << shift) - 1);
-    const uint64_t halfway = 1ull << (shift - 1);
-    if (rem > halfway || (rem == halfway && (q & 1)))
-        ++q;
-    uint32_t bits;
-    if (hexp == 0) {
-        bits = (uint32_t)q;  // q == 1024 carries into the smallest normal
-    } else {
-        if (q == 2048) {  // carry out of the significand
-            q = 1024;
-            ++hexp;
-            if (hexp >= 31)
-                return sign | 0x7C00;
-        }
-        bits = (hexp << 10) | (uint32_t)(q - 1024);
-    }
-    return sign | (uint16_t)bits;
-}
-
 struct LevelPtrs {
     uint16_t *lv[APMOE_MAX_BITS + 1];
 };
@@ -144,7 +97,7 @@ __global__ void __launch_bounds__(256) lut_build_kernel(const uint16_t *__restri
         for (int c = 0; c < (1 << b); ++c) {
             const double m = ((double)__builtin_bit_cast(_Float16, cur[2 * c]) +
                               (double)__builtin_bit_cast(_Float16, cur[2 * c + 1])) * 0.5;
-            cur[c] = d2h_rne(m);
+            cur[c] = apmoe_d2h_rne(m);
         }
         if (L.lv[b]) {
             uint16_t *dst = L.lv[b] + (size_t)row * (1u << b);

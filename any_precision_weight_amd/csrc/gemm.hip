@@ -37,85 +37,23 @@
 // halves of 32 lanes (lanes 0-31, 32-63), and within a half the 32 rows i fall in
 // 32 distinct banks.  For q = 8 one copy at v*128 + 4*i + 2*t keeps the region at
 // 32 KB (two instructions per address).
-#include "internal.h"
+#include "device.h"
 
 namespace apmoe {
 namespace {
 
-constexpr int kWave = 64;
 // KP: column parts of a workgroup (waves: 2 row tiles x KP), 2 or 4
 template <int KP>
 constexpr int kThreadsOf = 2 * KP * 64;
 constexpr int kRows = kGemmRowsPerBlock;  // 64
 constexpr int kStepCols = 128;            // columns per wave step (2 lane halves x 64)
 constexpr int kTokTile = 32;
-constexpr int kXcds = 8;                  // accelerator complex dies; workgroup b runs on XCD b % 8
 constexpr int kLptExperts = 16;           // launches with at most this many experts rank them on the device
 constexpr int kLutBytes = 32 * 1024;                       // LUT region, every q
 template <int KP>
 constexpr int kRedBytesOf = (KP - 1) * 2 * 16 * kWave * sizeof(float);  // column-part reduction
 constexpr int kXRowBytes = kStepCols * 2;                   // one token row of one step (fp16)
 constexpr uint32_t kNoWord = 0x20000000u;  // plane word offset past every plane (byte offset 2^31)
-// s_waitcnt operands (vmcnt in bits 3:0 and 15:14, expcnt 6:4 left open, lgkmcnt 11:8)
-constexpr int kWaitAll = 7 << 4;
-template <int VM>
-constexpr int wait_vm()
-{
-    static_assert(VM >= 0 && VM < 16, "vmcnt range");
-    return VM | (7 << 4);
-}
-
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef float float16v __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-// Buffer resource (base, byte range) in scalar registers: loads take a 32-bit lane
-// offset and return zeros past the range.  Word 3 is the gfx9-family raw-buffer
-// configuration.
-__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-__device__ inline uint32_t bitrev(uint32_t c, int q) { return __builtin_bitreverse32(c) >> (32 - q); }
-
-// In-place transpose of 4 independent 8x8 bit blocks: on input d[p] byte b bit j is
-// plane p, column 8b+j; on output d[j] byte b bit p holds the same bit.
-// Exchange the bits of b under m with the bits of a under m << s.  BFI: two
-// bit-field inserts from the original pair (four instructions); otherwise the xor
-// form (five), which the compiler folds further when some words are known zero.
-template <bool BFI>
-__device__ inline void swap_bits(uint32_t &a, uint32_t &b, int s, uint32_t m)
-{
-    if constexpr (BFI) {
-        const uint32_t nb = (m & (a >> s)) | (~m & b);
-        const uint32_t na = ((m << s) & (b << s)) | (~(m << s) & a);
-        a = na;
-        b = nb;
-    } else {
-        const uint32_t t = ((a >> s) ^ b) & m;
-        b ^= t;
-        a ^= t << s;
-    }
-}
-
-template <bool BFI>
-__device__ inline void transpose8x8(uint32_t (&d)[8])
-{
-    swap_bits<BFI>(d[0], d[4], 4, 0x0F0F0F0Fu);
-    swap_bits<BFI>(d[1], d[5], 4, 0x0F0F0F0Fu);
-    swap_bits<BFI>(d[2], d[6], 4, 0x0F0F0F0Fu);
-    swap_bits<BFI>(d[3], d[7], 4, 0x0F0F0F0Fu);
-    swap_bits<BFI>(d[0], d[2], 2, 0x33333333u);
-    swap_bits<BFI>(d[1], d[3], 2, 0x33333333u);
-    swap_bits<BFI>(d[4], d[6], 2, 0x33333333u);
-    swap_bits<BFI>(d[5], d[7], 2, 0x33333333u);
-    swap_bits<BFI>(d[0], d[1], 1, 0x55555555u);
-    swap_bits<BFI>(d[2], d[3], 1, 0x55555555u);
-    swap_bits<BFI>(d[4], d[5], 1, 0x55555555u);
-    swap_bits<BFI>(d[6], d[7], 1, 0x55555555u);
-}
 
 struct GemmParams {
     const DevBlock *table;  // layer slice; entry 2*e + kind
@@ -145,12 +83,6 @@ __device__ inline void load_planes(u32x2 (&w)[Q], const __amdgpu_buffer_rsrc_t (
 #pragma unroll
     for (int p = 0; p < Q; ++p)
         w[p] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs[p], (int)(word * 4u), 0, kLoadNT));
-}
-
-// One B fragment (8 fp16 columns of one token row) from the LDS token buffer.
-__device__ inline u32x4 lds_b128(uint32_t addr)
-{
-    return *reinterpret_cast<const __attribute__((address_space(3))) u32x4 *>((uintptr_t)addr);
 }
 
 // 4 MFMAs over one 32-column word of each needed plane: unpack, LUT gather, multiply.
@@ -602,14 +534,6 @@ template <int MODE>
 constexpr int kMidLds = kMidLutBytes<MODE> + kMidNxb * kMidXBuf;
 static_assert(kMidMaxRows % kTokTile == 0 && kMidTT <= 4, "whole 32-token tiles");
 
-// s_waitcnt with vmcnt up to 63 (bits 3:0 and 15:14), expcnt open, lgkmcnt 0
-template <int VM>
-constexpr int wait_vm63()
-{
-    static_assert(VM >= 0 && VM < 64, "vmcnt range");
-    return (VM & 15) | (7 << 4) | ((VM >> 4) << 14);
-}
-
 // One word of each needed plane (32 columns of the lane's row), non-temporal.
 template <int Q>
 __device__ inline void load_words(uint32_t (&w)[Q], const __amdgpu_buffer_rsrc_t (&rs)[Q], uint32_t word)
@@ -778,7 +702,7 @@ __device__ __attribute__((always_inline)) inline void mid_block(const GemmParams
         load_words<Q>(wr[U2], rs, s2 < nsteps ? lane_word + 128u * (uint32_t)s2 : kNoWord);
         __builtin_amdgcn_sched_barrier(0);
         mid_group<Q, TT, U * kMidXBuf>(wr[U], xaddr, lds_base, lane_const, acc);
-        __builtin_amdgcn_s_waitcnt(wait_vm63<2 * Q + TT>());
+        __builtin_amdgcn_s_waitcnt(wait_vm<2 * Q + TT>());
         asm volatile("s_barrier" ::: "memory");
     };
     for (int s = 0; s < nsteps; s += kMidNxb) {
@@ -1017,14 +941,16 @@ static hipError_t launch_mid(const GemmParams &P, int max_q, int act, int N, int
     const dim3 mgrid(kXcds * E * ((M.row_blocks + kXcds - 1) / kXcds));
     // Two workgroups per CU pay where an expert alone has many row blocks (the 8x22B
     // gate_up: 256); with few (its down: 48) they measured slower than one.  The q = 8
-    // launch runs only if the committed map of the layer has such a block.
+    // launch always follows: q is read from the device table when the kernels run, and
+    // its workgroups exit at once when no expert of 33..64 rows is at q = 8.
+    (void)max_q;
     if (M.row_blocks >= 128) {
         if (kind == APMOE_GATE_UP)
             hipLaunchKernelGGL((gemm_mid_kernel<APMOE_GATE_UP, kMidLow>), mgrid, dim3(kMidThreads), 0, s, M);
         else
             hipLaunchKernelGGL((gemm_mid_kernel<APMOE_DOWN, kMidLow>), mgrid, dim3(kMidThreads), 0, s, M);
         err = hipGetLastError();
-        if (err == hipSuccess && max_q == 8) {
+        if (err == hipSuccess) {
             if (kind == APMOE_GATE_UP)
                 hipLaunchKernelGGL((gemm_mid_kernel<APMOE_GATE_UP, kMidQ8>), mgrid, dim3(kMidThreads), 0, s, M);
             else

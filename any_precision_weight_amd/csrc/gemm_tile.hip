@@ -38,12 +38,11 @@
 // expert; consecutive tiles run on the same XCD (workgroup b runs on XCD b % 8), so a
 // group's weight and token tiles are shared through that XCD's L2, and every XCD
 // runs tiles of every expert.
-#include "internal.h"
+#include "device.h"
 
 namespace apmoe {
 namespace {
 
-constexpr int kWave = 64;
 constexpr int kThreads = 512;  // 4 consumer + 4 producer waves
 constexpr int kBN = 128;  // weight rows per tile
 constexpr int kBM = kTileTokens;  // token rows per tile (256)
@@ -67,56 +66,6 @@ struct Layout {
     static_assert(kA + 2 * kAStageBytes <= kLdsBytes, "LDS budget");
 };
 constexpr int kGroupN = 8;  // weight-row tiles per group
-constexpr int kXcds = 8;
-
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef float float16v __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-__device__ inline uint32_t bitrev(uint32_t c, int q) { return __builtin_bitreverse32(c) >> (32 - q); }
-
-// Exchange the bits of b under m with the bits of a under m << s.  BFI: two
-// bit-field inserts from the original pair (four instructions); otherwise the xor
-// form (five), which the compiler folds further when some words are known zero.
-template <bool BFI>
-__device__ inline void swap_bits(uint32_t &a, uint32_t &b, int s, uint32_t m)
-{
-    if constexpr (BFI) {
-        const uint32_t nb = (m & (a >> s)) | (~m & b);
-        const uint32_t na = ((m << s) & (b << s)) | (~(m << s) & a);
-        a = na;
-        b = nb;
-    } else {
-        const uint32_t t = ((a >> s) ^ b) & m;
-        b ^= t;
-        a ^= t << s;
-    }
-}
-
-// 4 independent 8x8 bit transposes: in, d[p] byte b bit j = plane p, column 8b+j;
-// out, d[j] byte b bit p = the same bit.
-template <bool BFI>
-__device__ inline void transpose8x8(uint32_t (&d)[8])
-{
-    swap_bits<BFI>(d[0], d[4], 4, 0x0F0F0F0Fu);
-    swap_bits<BFI>(d[1], d[5], 4, 0x0F0F0F0Fu);
-    swap_bits<BFI>(d[2], d[6], 4, 0x0F0F0F0Fu);
-    swap_bits<BFI>(d[3], d[7], 4, 0x0F0F0F0Fu);
-    swap_bits<BFI>(d[0], d[2], 2, 0x33333333u);
-    swap_bits<BFI>(d[1], d[3], 2, 0x33333333u);
-    swap_bits<BFI>(d[4], d[6], 2, 0x33333333u);
-    swap_bits<BFI>(d[5], d[7], 2, 0x33333333u);
-    swap_bits<BFI>(d[0], d[1], 1, 0x55555555u);
-    swap_bits<BFI>(d[2], d[3], 1, 0x55555555u);
-    swap_bits<BFI>(d[4], d[5], 1, 0x55555555u);
-    swap_bits<BFI>(d[6], d[7], 1, 0x55555555u);
-}
 
 struct TileParams {
     const DevBlock *table;  // layer slice; entry 2*e + kind
@@ -216,16 +165,6 @@ __device__ inline void word_codes(const u32x2 (&w)[Q], uint32_t (&d)[8])
     transpose8x8<Q == 8 || Q == 3>(d);  // the form with fewer instructions after folding (counted per q)
 }
 
-__device__ inline u32x4 lds_b128(uint32_t addr)
-{
-    return *(const __attribute__((address_space(3))) u32x4 *)(uintptr_t)addr;
-}
-
-__device__ inline void lds_store_b128(uint32_t addr, u32x4 v)
-{
-    *(__attribute__((address_space(3))) u32x4 *)(uintptr_t)addr = v;
-}
-
 // Token stages are copied global -> LDS by the buffer unit (buffer_load ... lds):
 // one instruction writes 64 x 16 bytes at consecutive LDS addresses, so producer p,
 // instruction u fills rows 64p + 8u .. +7 of a stage, lane L the 16-byte slot L % 8
@@ -233,8 +172,6 @@ __device__ inline void lds_store_b128(uint32_t addr, u32x4 v)
 struct XStage {
     uint32_t off[8];  // byte offset of the lane's chunk (token row + column) for instruction u
 };
-
-__device__ inline uint32_t lds_addr(const void *p) { return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)p; }
 
 // Token stage n (word n % 2 of step n / 2, clamped to the last stage) into the LDS
 // buffer at `dst` (this producer's quarter).
@@ -256,22 +193,23 @@ __device__ inline void x_stage(char *dst, __amdgpu_buffer_rsrc_t rx, const XStag
 template <int VM>
 __device__ inline void phase_barrier()
 {
-    static_assert(VM >= 0 && VM < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | (0 << 8) | ((VM >> 4) << 14));
+    __builtin_amdgcn_s_waitcnt(wait_vm<VM>());
     asm volatile("s_barrier" ::: "memory");
 }
 
-// One LUT entry of the lane's row: code byte b of dj (transposed code) -> fp16.
-__device__ inline _Float16 lookup1(uint32_t dj, int b, uint32_t lane_const)
+// One LUT entry of the lane's row: code byte b of dj (transposed code) -> fp16.  The
+// LUT region starts at LDS address lut_base (a compile-time constant: the static
+// array's address, folded into the instruction's offset).
+__device__ inline _Float16 lookup1(uint32_t dj, int b, uint32_t lane_const, uint32_t lut_base)
 {
     const uint32_t addr = __builtin_amdgcn_perm(dj, lane_const, 0x0C0C0000u | ((4u + b) << 8));
-    return *(const __attribute__((address_space(3))) _Float16 *)(uintptr_t)addr;
+    return *(const __attribute__((address_space(3))) _Float16 *)(uintptr_t)(lut_base + addr);
 }
 
 // Producer side of one stage: the lane's 32 weights of word W of `wc` -> four fp16 A
 // fragments in the A buffer.
 template <int Q, int W>
-__device__ inline void produce_a(const u32x2 (&wc)[Q], uint32_t lane_const, uint32_t a_dst)
+__device__ inline void produce_a(const u32x2 (&wc)[Q], uint32_t lane_const, uint32_t lut_base, uint32_t a_dst)
 {
     uint32_t d[8];
     word_codes<Q, W>(wc, d);
@@ -280,7 +218,7 @@ __device__ inline void produce_a(const u32x2 (&wc)[Q], uint32_t lane_const, uint
     for (int b = 0; b < 4; ++b)
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-            a[b][j] = lookup1(d[j], b, lane_const);
+            a[b][j] = lookup1(d[j], b, lane_const, lut_base);
     __builtin_amdgcn_sched_barrier(0);  // every lookup is requested before the first is used
 #pragma unroll
     for (int b = 0; b < 4; ++b)
@@ -377,7 +315,7 @@ __device__ __attribute__((always_inline)) void tile_block(const TileParams &P, c
                     const uint32_t a = (la[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
                     const uint32_t b = (lb[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
                     const uint32_t v = bitrev((uint32_t)(8 * ch + e), Q);
-                    *(__attribute__((address_space(3))) uint32_t *)(uintptr_t)(v * 256u + 4u * pr) = a | (b << 16);
+                    *(__attribute__((address_space(3))) uint32_t *)(uintptr_t)(base + v * 256u + 4u * pr) = a | (b << 16);
                 }
             }
         }
@@ -436,29 +374,29 @@ __device__ __attribute__((always_inline)) void tile_block(const TileParams &P, c
         x_stage(xbuf(D), rx, X, D, nst);
         __builtin_amdgcn_sched_barrier(0);
         load_planes<Q, KIND == APMOE_DOWN>(pb, rs, step_word(1));
-        produce_a<Q, 0>(pa, lane_const, a_dst);
+        produce_a<Q, 0>(pa, lane_const, base, a_dst);
         phase_barrier<kWaitEven>();
         for (int m = 0; m < KT2 / 2; ++m) {
             const int n = 4 * m;
             // phase n+1: stage n+1 = word 1 of step 2m -> A buffer 1
             x_stage(xbuf(n + 1 + D), rx, X, n + 1 + D, nst);
-            produce_a<Q, 1>(pa, lane_const, a_dst + kAStageBytes);
+            produce_a<Q, 1>(pa, lane_const, base, a_dst + kAStageBytes);
             phase_barrier<kWaitOdd>();
             // phase n+2: stage n+2 = word 0 of step 2m+1 -> A buffer 0
             x_stage(xbuf(n + 2 + D), rx, X, n + 2 + D, nst);
             __builtin_amdgcn_sched_barrier(0);  // the plane requests follow the token copies
             load_planes<Q, KIND == APMOE_DOWN>(pa, rs, step_word(2 * m + 2));
-            produce_a<Q, 0>(pb, lane_const, a_dst);
+            produce_a<Q, 0>(pb, lane_const, base, a_dst);
             phase_barrier<kWaitEven>();
             // phase n+3: stage n+3 = word 1 of step 2m+1 -> A buffer 1
             x_stage(xbuf(n + 3 + D), rx, X, n + 3 + D, nst);
-            produce_a<Q, 1>(pb, lane_const, a_dst + kAStageBytes);
+            produce_a<Q, 1>(pb, lane_const, base, a_dst + kAStageBytes);
             phase_barrier<kWaitOdd>();
             // phase n+4: stage n+4 = word 0 of step 2m+2 -> A buffer 0
             x_stage(xbuf(n + 4 + D), rx, X, n + 4 + D, nst);
             __builtin_amdgcn_sched_barrier(0);
             load_planes<Q, KIND == APMOE_DOWN>(pb, rs, step_word(2 * m + 3));
-            produce_a<Q, 0>(pa, lane_const, a_dst);
+            produce_a<Q, 0>(pa, lane_const, base, a_dst);
             phase_barrier<kWaitEven>();
         }
         if (P.act)
@@ -535,7 +473,6 @@ __device__ __attribute__((always_inline)) void tile_block(const TileParams &P, c
                     for (int h = 0; h < 2; ++h) {
 #pragma unroll
                         for (int a4 = 0; a4 < 4; ++a4) {
-                            typedef _Float16 half4 __attribute__((ext_vector_type(4)));
                             half4 hv;
 #pragma unroll
                             for (int b = 0; b < 4; ++b)
@@ -578,7 +515,6 @@ __device__ __attribute__((always_inline)) void tile_block(const TileParams &P, c
                     } else {
                         _Float16 *o = reinterpret_cast<_Float16 *>(P.out) + orow + n;
                         if ((N & 3) == 0 && n + 3 < N) {
-                            typedef _Float16 half4 __attribute__((ext_vector_type(4)));
                             half4 hv;
 #pragma unroll
                             for (int b = 0; b < 4; ++b)

@@ -24,7 +24,7 @@ class ResidentWeights:
         self.ctx = ctx
         self.L, self.E = n_layers, n_experts
         self.device = device
-        self.table = Table(n_layers, n_experts)
+        self.table = Table(n_layers, n_experts, library=ctx.L)
         self.planes: dict[tuple[int, int, int], torch.Tensor] = {}
         self.luts: dict[tuple[int, int, int], dict[int, torch.Tensor]] = {}
         self.shape: dict[tuple[int, int, int], tuple[int, int]] = {}
@@ -68,6 +68,18 @@ class ResidentWeights:
 
     def commit(self, stream=None) -> None:
         self.table.commit(self.ctx, stream)
+
+    def mirror_table(self, ctx: Context, stream=None) -> Table:
+        """A table of ctx's library build over the same device planes and LUTs, with
+        this table's committed bitwidths, committed on `stream`.  The caller closes it
+        before these weights."""
+        t = Table(self.L, self.E, library=ctx.L)
+        for (layer, expert, kind), pt in self.planes.items():
+            N, K = self.shape[(layer, expert, kind)]
+            q = self.table.committed_bits(layer, expert, kind)
+            t.set_block(layer, expert, kind, N, K, q, [pt[p] for p in range(8)], self.luts[(layer, expert, kind)])
+        t.commit(ctx, stream)
+        return t
 
     def plane_bytes(self, layer: int, expert: int, kind: int, q: int) -> int:
         N, K = self.shape[(layer, expert, kind)]

@@ -171,10 +171,16 @@ apmoe_status apmoe_table_commit(apmoe_ctx *ctx, apmoe_table *tbl, void *stream);
  * Format tools
  * ------------------------------------------------------------------------ */
 
-/* Child LUT levels from the parent level 8 (fp16 [n][256], device):
+/* Child LUT levels from the parent level 8 (fp16 [n][256], device).  The paper's
+ * Figure 3 caption gives every quantised tensor a LUT of bitwidth-specific
+ * centroids over the shared bit-planes, a b-bit weight reading the top b planes;
+ * it gives no rule that relates the levels.  The reading taken here: the b-bit code
+ * c covers the (b+1)-bit codes 2c and 2c+1, and its centroid is their mean --
  * level b = fp16 round-to-nearest-even of the mean of entries 2c and 2c+1 of
  * level b+1.  levels is a host array of 9 device pointers; levels[b] (fp16
- * [n][2^b]) is written for each b in 3..7 that is non-NULL. */
+ * [n][2^b]) is written for each b in 3..7 that is non-NULL (ownership: caller).
+ * Errors: INVALID_ARG for NULL or misaligned pointers or n < 0; nothing is
+ * enqueued then. */
 apmoe_status apmoe_lut_build(apmoe_ctx *ctx, const uint16_t *parent, int32_t n, uint16_t *const *levels,
                              void *stream);
 
@@ -260,6 +266,13 @@ apmoe_status apmoe_route(apmoe_ctx *ctx, const uint16_t *x, const uint16_t *w_ro
                          int32_t *topk_ids, float *topk_w, int32_t *counts, int32_t *offsets, int32_t *perm,
                          int32_t *inv_perm, void *stream);
 
+/* Device workspace of apmoe_route for these arguments: always 0 bytes.  The
+ * per-token selection runs in one workgroup per token and the expert-grouping sort
+ * in the LDS of one workgroup, so the route writes only its outputs.  INVALID_ARG
+ * for arguments apmoe_route would refuse. */
+apmoe_status apmoe_route_workspace(apmoe_ctx *ctx, int32_t T, int32_t E, int32_t topk, int32_t n_shared,
+                                   size_t *bytes);
+
 /*
  * Online routing statistics (Section 2.1, Eq. 1: the routing mass of expert e is
  * the sum of the routing weights of its selections over the sum of all routing
@@ -282,7 +295,11 @@ apmoe_status apmoe_route_stats(apmoe_ctx *ctx, const float *topk_w, const int32_
                                void *stream);
 
 /*
- * Any-precision product of every expert of one (layer, kind) in one call: up to
+ * Any-precision expert product (Section 3.3 "Fused Mixed-Precision MoE Kernel": the
+ * kernel reads the weight pages -- bit-planes and LUT -- directly and follows the
+ * bitwidth the planner committed for each gate_up and down module; Figure 3
+ * caption: a b-bit weight is the centroid its top-b-plane code selects in the
+ * b-bit LUT).  Every expert of one (layer, kind) in one call: up to
  * three kernel launches, by the experts' row counts (up to 32 rows, 33..64, more),
  * each skipped when the batch has too few tokens for any expert to need it.  A short
  * launch for the largest experts (at most two tiles per CU) runs on the context's own
@@ -297,14 +314,22 @@ apmoe_status apmoe_route_stats(apmoe_ctx *ctx, const float *topk_w, const int32_
  *   out : [T*topk][N] of out_dtype (APMOE_F16 rounds to nearest even).
  * N and K are the block shape; every expert of (layer, kind) must be committed
  * with the same shape.  offsets is device memory written by apmoe_route; no
- * host synchronisation happens.
+ * host synchronisation happens.  Errors (nothing enqueued): INVALID_ARG for NULL
+ * or misaligned pointers, a bad layer or kind, topk outside 1..16, or a buffer of
+ * 2 GiB or more; UNSUPPORTED for another out_dtype; NOT_RESIDENT if the table was
+ * never committed or a block of (layer, kind) has no committed entry.
  */
 apmoe_status apmoe_gemm(apmoe_ctx *ctx, const apmoe_table *tbl, int32_t layer, int32_t kind, const uint16_t *in,
                         int32_t gather, const int32_t *perm, const int32_t *offsets, int32_t T, int32_t topk,
                         void *out, int32_t out_dtype, void *stream);
 
-/* Expert activation: a[r][f] = SiLU(h[r][f]) * h[r][F + f] in fp32, stored fp16.
- * h fp16 [R][2F], a fp16 [R][F], F % 8 == 0. */
+/* Expert activation (Section 3.3: the fused kernel covers "expert activation"
+ * between the two projections; the pages do not name the function -- the reading
+ * taken is the SwiGLU of Mixtral-class experts):
+ *   a[r][f] = SiLU(h[r][f]) * h[r][F + f],  SiLU(z) = z / (1 + e^-z),
+ * in fp32, stored fp16 (round to nearest even).  h fp16 [R][2F] (gate columns
+ * [0, F), up columns [F, 2F)), a fp16 [R][F], both device, caller-owned;
+ * F % 8 == 0.  INVALID_ARG for NULL or misaligned pointers or a bad F. */
 apmoe_status apmoe_act(apmoe_ctx *ctx, const uint16_t *h, int32_t R, int32_t F, uint16_t *a, void *stream);
 
 /*
@@ -322,8 +347,15 @@ apmoe_status apmoe_gemm_act(apmoe_ctx *ctx, const apmoe_table *tbl, int32_t laye
                             int32_t gather, const int32_t *perm, const int32_t *offsets, int32_t T, int32_t topk,
                             uint16_t *a, void *stream);
 
-/* Output accumulation: out[t][n] = sum_{j < topk} topk_w[t][j] * y[inv_perm[t*topk + j]][n],
- * fp32, summed in j order, stored fp16.  y is [T*topk][H] of y_dtype; H % 8 == 0. */
+/* Output accumulation (Section 3.3: the fused kernel ends with the "output
+ * accumulation" of the selected experts' outputs, weighted by the routing weights
+ * of Section 2.1):
+ *   out[t][n] = sum_{j < topk} topk_w[t][j] * y[inv_perm[t*topk + j]][n],
+ * fp32, summed in j order (a gather: no atomics, the same bits on every run), stored
+ * fp16.  y is [T*topk][H] of y_dtype (expert-grouped rows, as the products write
+ * them), topk_w [T][topk] fp32, inv_perm [T*topk], out fp16 [T][H]; all device,
+ * caller-owned; H % 8 == 0.  INVALID_ARG for NULL or misaligned pointers or bad
+ * sizes, UNSUPPORTED for another y_dtype. */
 apmoe_status apmoe_combine(apmoe_ctx *ctx, const void *y, int32_t y_dtype, const float *topk_w,
                            const int32_t *inv_perm, int32_t T, int32_t topk, int32_t H, uint16_t *out, void *stream);
 
@@ -332,13 +364,16 @@ apmoe_status apmoe_moe_workspace(const apmoe_table *tbl, int32_t layer, int32_t 
                                  size_t *bytes);
 
 /*
- * Whole layer in four steps: route, gate_up with the activation fused
- * (apmoe_gemm_act, fp16 a), down (fp32 y), combine.
+ * Whole layer (Section 3.3 "Fused Mixed-Precision MoE Kernel": routing, expert
+ * activation, down projection and output accumulation, each gate_up / down module
+ * at its committed bitwidth) in four steps: route, gate_up with the activation
+ * fused (apmoe_gemm_act, fp16 a), down (fp32 y), combine.
  * The table's experts of the layer are the routed ones (w_router rows) followed by
  * n_shared shared experts.
  * ws is caller-owned device memory of at least apmoe_moe_workspace bytes, 256-byte
  * aligned; it holds ids, weights, counts, offsets, perm, inv_perm, a and y.
- * out fp16 [T][H].
+ * out fp16 [T][H].  Every argument and size limit of the four steps is checked
+ * before the first launch: a refused call enqueues nothing.
  */
 apmoe_status apmoe_moe_forward(apmoe_ctx *ctx, const apmoe_table *tbl, int32_t layer, const uint16_t *x,
                                const uint16_t *w_router, const float *bias, int32_t T, int32_t topk,

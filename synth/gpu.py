@@ -17,8 +17,10 @@ _lib = None
 
 def build() -> str:
     tmp = _LIB + ".tmp"
+    # the fp64 -> fp16 rounding is the library's own header (one definition)
+    inc = os.path.join(os.path.dirname(_HERE), "any_precision_weight_amd", "csrc")
     cmd = ["/opt/rocm/bin/hipcc", "--offload-arch=gfx950", "-O3", "-fPIC", "-shared",
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", _SRC, "-o", tmp]
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-I", inc, _SRC, "-o", tmp]
     subprocess.run(cmd, check=True, capture_output=True)
     os.replace(tmp, _LIB)
     return _LIB

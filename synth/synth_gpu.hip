@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fp16_rne.h"
+
 namespace {
 
 constexpr uint64_t kGolden = 0x9E3779B97F4A7C15ull;
@@ -33,47 +35,6 @@ __device__ inline double normal(uint64_t key, uint64_t idx)
     return (double)(acc - 393210) * (1.0 / 65536.0);
 }
 
-// fp64 -> fp16 bits, round to nearest even (IEEE 754 encodings)
-__device__ inline uint16_t to_half(double d)
-{
-    const uint64_t u = __builtin_bit_cast(uint64_t, d);
-    const uint16_t sign = (uint16_t)((u >> 48) & 0x8000u);
-    const int ex = (int)((u >> 52) & 0x7FF);
-    const uint64_t mant = u & ((1ull << 52) - 1);
-    if (ex == 0x7FF)
-        return sign | (mant ? 0x7E00 : 0x7C00);
-    if (ex == 0)
-        return sign;  // zero or fp64 subnormal: far below fp16's range
-    const int e = ex - 1023;
-    const uint64_t sig = mant | (1ull << 52);
-    int shift;
-    uint32_t hexp;
-    if (e >= -14) {
-        if (e > 15)
-            return sign | 0x7C00;
-        shift = 42;
-        hexp = (uint32_t)(e + 15);
-    } else {
-        shift = 28 - e;
-        hexp = 0;
-        if (shift > 63)
-            return sign;
-    }
-    uint64_t q = sig >> shift;
-    const uint64_t rem = sig & ((1ull << shift) - 1);
-    const uint64_t halfway = 1ull << (shift - 1);
-    if (rem > halfway || (rem == halfway && (q & 1)))
-        ++q;
-    if (hexp == 0)
-        return sign | (uint16_t)q;
-    if (q == 2048) {
-        q = 1024;
-        if (++hexp >= 31)
-            return sign | 0x7C00;
-    }
-    return sign | (uint16_t)((hexp << 10) | (uint32_t)(q - 1024));
-}
-
 __global__ void planes_kernel(uint64_t key, uint64_t nwords, uint32_t *__restrict__ out)
 {
     const uint64_t j = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -89,7 +50,7 @@ __global__ void fp16_normal_kernel(uint64_t key, uint64_t n, double std, uint16_
 {
     const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n)
-        out[i] = to_half(normal(key, i) * std);
+        out[i] = apmoe_d2h_rne(normal(key, i) * std);
 }
 
 // order-preserving key of a non-NaN fp16 bit pattern (+0 after canonicalisation)
@@ -105,7 +66,7 @@ __global__ void __launch_bounds__(256) parent_lut_kernel(uint64_t key, int rows,
     const int t = threadIdx.x;
     if (row >= rows)
         return;
-    uint16_t h = to_half(normal(key, (uint64_t)row * 256 + t) * std);
+    uint16_t h = apmoe_d2h_rne(normal(key, (uint64_t)row * 256 + t) * std);
     if (h == 0x8000)
         h = 0;
     v[t] = h;

@@ -9,8 +9,14 @@
   routed + 4 shared top-4, 128 routed + 1 shared top-8; hidden and FFN sizes chosen),
   decode and prefill.
 
-Bars: routing bit-exact for all tokens; sampled outputs within max-abs 1e-2 and
-relative L2 2e-3 of the oracle.
+Bars: routing bit-exact for all tokens; the outputs of the evaluated tokens within
+max-abs 1e-2 and relative L2 2e-3 of the oracle.  The evaluated tokens are chosen
+from the routing so that every expert's first and last row is among them, and for
+experts on the tile product (more than 64 rows) the first and last row of every
+256-row token tile, so every product and every partial tile is compared at full
+size; 32 seeded random tokens are added.  At the prefill size one complete tile
+expert is also compared row by row on both products against the block product of
+the oracle, within the fp32 accumulation bound.
 """
 import numpy as np
 import pytest
@@ -21,7 +27,7 @@ import oracle
 import synth
 import synth.gpu
 from any_precision_weight_amd.resident import ResidentWeights
-from gpu_util import check_out, check_route, ctx, dev, host, topk_margin_ok
+from gpu_util import check_out, check_route, ctx, dev, host, topk_margin_ok, ulp16
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -69,26 +75,53 @@ def _oracle_layer(cfg, layer, q, eval_tokens):
     return r, x, wr, bias
 
 
-def _single_layer_case(cfg, eval_tokens):
+def coverage_tokens(route, kt, T, n_random=32, seed=0):
+    """Tokens whose rows include, for every expert, its first and last row and, for
+    experts with more than 64 rows (the tile product, 256-row token tiles), the first
+    and last row of every token tile; plus n_random seeded random tokens."""
+    offsets, perm = route["offsets"], route["perm"]
+    rows = set()
+    for e in range(offsets.size - 1):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 == r0:
+            continue
+        rows.update((r0, r1 - 1))
+        if r1 - r0 > 64:
+            for t0 in range(r0, r1, 256):
+                rows.update((t0, min(t0 + 255, r1 - 1)))
+    toks = {int(perm[r]) // kt for r in rows}
+    rng = np.random.default_rng(seed)
+    toks.update(int(t) for t in rng.choice(T, size=min(n_random, T), replace=False))
+    return sorted(toks)
+
+
+def _single_layer_case(cfg, eval_tokens=None):
+    """eval_tokens None: coverage_tokens of the layer's routing; "all": every token."""
     q = synth.gen_qmap(cfg)
     rw = ResidentWeights(ctx(), 1, cfg.weight_experts)
     _upload_layer_gpu(rw, cfg, 0, 0, q)
     rw.commit()
     x, wr, bias = synth.gen_x(cfg), synth.gen_router(cfg), synth.gen_bias(cfg)
     assert topk_margin_ok(x, wr, bias, cfg.topk)
+    if eval_tokens is None:
+        route = oracle.route(x, wr, bias, cfg.topk, cfg.renormalize, n_shared=cfg.shared)
+        eval_tokens = coverage_tokens(route, cfg.assign, cfg.tokens)
+    elif eval_tokens == "all":
+        eval_tokens = list(range(cfg.tokens))
+    print(f"{cfg.name}: evaluating {len(eval_tokens)} tokens", flush=True)
     o = _run_layer(rw, 0, dev(x), dev(wr), None if bias is None else dev(bias), cfg, cfg.tokens)
     torch.cuda.synchronize()
     r, *_ = _oracle_layer(cfg, 0, q, np.array(eval_tokens, np.int32))
     check_route(o, r)
     ma, rl = check_out(host(o["out"])[eval_tokens], r["out"])
-    print(f"{cfg.name}: sampled tokens {eval_tokens}: max-abs {ma:.3e} rel-L2 {rl:.3e}", flush=True)
+    print(f"{cfg.name}: {len(eval_tokens)} tokens: max-abs {ma:.3e} rel-L2 {rl:.3e}", flush=True)
     rw.close()
     return r, q
 
 
 def test_mixtral8x22b_decode_skewed():
     cfg = synth.config_by_name("mixtral8x22b_decode_t256_zipf")
-    r, q = _single_layer_case(cfg, [0, 77, 255])
+    r, q = _single_layer_case(cfg)
     # the generator's hot experts (Zipf ranks 1 and 2) are the top-2 by Eq. 1 routing mass
     mass = oracle.routing_mass(r["ids"], r["w64"], cfg.experts)
     assert sorted(np.argsort(-mass, kind="stable")[:2].tolist()) == synth.hot_experts(cfg)
@@ -97,7 +130,46 @@ def test_mixtral8x22b_decode_skewed():
 
 def test_mixtral8x7b_prefill():
     cfg = synth.config_by_name("mixtral8x7b_prefill_t4096_zipf")
-    _single_layer_case(cfg, [0, 1234, 4095])
+    _single_layer_case(cfg)
+
+
+def test_mixtral8x7b_prefill_complete_tile_expert():
+    """Every row of one tile expert at the full prefill size (the expert with the
+    fewest rows: two or more 256-row token tiles, the last one partial): gate_up to
+    fp16 h and down to fp32 y, each against the oracle's block product of the GPU's
+    own input rows, within half an fp16 ulp plus the fp32 accumulation bound
+    K * 2^-24 * sum |x| |W|."""
+    cfg = synth.config_by_name("mixtral8x7b_prefill_t4096_zipf")
+    q = synth.gen_qmap(cfg)
+    rw = ResidentWeights(ctx(), 1, cfg.weight_experts)
+    _upload_layer_gpu(rw, cfg, 0, 0, q)
+    rw.commit()
+    x, wr, bias = synth.gen_x(cfg), synth.gen_router(cfg), synth.gen_bias(cfg)
+    o = _run_layer(rw, 0, dev(x), dev(wr), None if bias is None else dev(bias), cfg, cfg.tokens)
+    torch.cuda.synchronize()
+    counts, offsets, perm = host(o["counts"]), host(o["offsets"]), host(o["perm"])
+    e = int(np.argmin(np.where(counts > 64, counts, 1 << 30)))
+    r0, r1 = int(offsets[e]), int(offsets[e + 1])
+    assert r1 - r0 > 256 and (r1 - r0) % 256 != 0, counts
+    print(f"complete tile expert {e}: {r1 - r0} rows, q gate_up {q[e, 0]} down {q[e, 1]}", flush=True)
+    H, F, kt = cfg.hidden, cfg.ffn, cfg.assign
+
+    def check(kind, inp, got, out_f16):
+        P = synth.gen_planes(cfg, 0, e, kind)
+        lut = oracle.lut_level(synth.gen_parent_lut(cfg, 0, e, kind), int(q[e, kind]))
+        ref = oracle.block_gemm(P, lut, int(q[e, kind]), inp)
+        S = oracle.block_gemm(P, np.abs(lut.astype(np.float64)), int(q[e, kind]), np.abs(inp))
+        acc = inp.shape[1] * 2.0 ** -24 * S
+        tol = acc + (0.5 * ulp16(np.abs(ref) + acc) if out_f16 else 0.0)
+        d = np.abs(got - ref)
+        assert np.all(d <= tol), (kind, float((d - tol).max()))
+        return float(d.max())
+
+    xin = x[perm[r0:r1] // kt].astype(np.float64)
+    dg = check(0, xin, host(o["h"][r0:r1]).astype(np.float64), True)
+    dd = check(1, host(o["a"][r0:r1]).astype(np.float64), host(o["y"][r0:r1]).astype(np.float64), False)
+    print(f"complete tile expert {e}: gate_up max |d| {dg:.3e}, down max |d| {dd:.3e}", flush=True)
+    rw.close()
 
 
 def test_mixtral8x7b_prefill_fused_activation():
@@ -140,7 +212,7 @@ def test_32_layers_resident_with_map_switch():
     mean_b = float(np.mean([qb[l].mean() for l in range(L)]))
     print(f"32 layers: realised mean bits map A {mean_a:.3f}, map B {mean_b:.3f}", flush=True)
     assert 5.8 < mean_a < 6.2 and 3.8 < mean_b < 4.2
-    ev = np.array([0, 17, 31], np.int32)
+    ev = np.arange(T, dtype=np.int32)  # every token of the batch
     for layer in (5, 31):
         for q, outs in ((qa[layer], outs_a), (qb[layer], outs_b)):
             r, x, wr, _ = _oracle_layer(cfg, layer, q, ev)
@@ -150,9 +222,9 @@ def test_32_layers_resident_with_map_switch():
     rw.close()
 
 
-@pytest.mark.parametrize("name,tokens", [("qwen_60r4s_top4_decode_t64", [0, 31, 63]),
-                                         ("gemma_128r1s_top8_decode_t64", [0, 40, 63]),
-                                         ("qwen_60r4s_top4_prefill_t2048", [0, 1000, 2047])])
+@pytest.mark.parametrize("name,tokens", [("qwen_60r4s_top4_decode_t64", "all"),
+                                         ("gemma_128r1s_top8_decode_t64", "all"),
+                                         ("qwen_60r4s_top4_prefill_t2048", None)])
 def test_shared_expert_workloads(name, tokens):
     cfg = synth.config_by_name(name)
     r, q = _single_layer_case(cfg, tokens)
