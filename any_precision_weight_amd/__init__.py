@@ -30,6 +30,7 @@ EXPORTED = [
     "apmoe_table_commit", "apmoe_lut_build", "apmoe_tiled_plane_words", "apmoe_tile_planes", "apmoe_pack_planes", "apmoe_route", "apmoe_route_workspace", "apmoe_route_stats", "apmoe_gemm",
     "apmoe_gemm_act", "apmoe_act",
     "apmoe_combine", "apmoe_moe_workspace", "apmoe_moe_forward", "apmoe_page_out", "apmoe_page_in",
+    "apmoe_moe_forward_noalloc",
 ]
 
 
@@ -113,6 +114,7 @@ def _declare(L):
         "apmoe_combine": (S, [P, P, I32, P, P, I32, I32, I32, P, P]),
         "apmoe_moe_workspace": (S, [P, I32, I32, I32, I32, ctypes.POINTER(SZ)]),
         "apmoe_moe_forward": (S, [P, P, I32, P, P, P, I32, I32, I32, I32, P, SZ, P, P]),
+        "apmoe_moe_forward_noalloc": (S, [P, P, I32, P, P, P, I32, I32, I32, I32, P, P]),
         "apmoe_page_out": (S, [P, P, I32, I32, I32, I32, ctypes.POINTER(P), P, P, P]),
         "apmoe_page_in": (S, [P, P, I32, I32, I32, I32, ctypes.POINTER(P), ctypes.POINTER(P), P, P, P]),
     }
@@ -316,6 +318,18 @@ def moe_forward(ctx: Context, table: Table, layer: int, x, w_router, bias, T: in
                                    n_shared,
                                    int(renormalize), ptr(ws), ws_bytes, ptr(out), stream_handle(stream)),
            "apmoe_moe_forward", ctx.L)
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def moe_forward_noalloc(ctx: Context, table: Table, layer: int, x, w_router, bias, T: int, topk: int,
+                        renormalize: bool, out, stream=None, n_shared: int = 0) -> None:
+    """The whole layer with the library's static scratch as its workspace (no device
+    allocation by the call)."""
+    _check(ctx.L.apmoe_moe_forward_noalloc(ctx.handle, table.handle, layer, ptr(x), ptr(w_router), ptr(bias), T,
+                                           topk, n_shared, int(renormalize), ptr(out), stream_handle(stream)),
+           "apmoe_moe_forward_noalloc", ctx.L)
 
 
 # --------------------------------------------------------------------------- page movement

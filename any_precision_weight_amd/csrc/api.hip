@@ -52,8 +52,15 @@ struct apmoe_ctx {
     int cus;
     char arch[64];
     apmoe::SideStream side;  // runs a short tile launch beside the decode and mid launches
+    void *scratch = nullptr;  // this device's copy of the static scratch array (allocation-free entry point)
 };
 
+// Workspace of apmoe_moe_forward_noalloc: a static device array.  Every device the
+// library runs on holds its own copy from the code object's load until the process
+// ends.  In host code its name is only a stand-in: apmoe_create takes the device's
+// address with hipGetSymbolAddress and every use goes through that address.
+static constexpr size_t kScratchBytes = (size_t)APMOE_NOALLOC_SCRATCH_BYTES;
+static __device__ __attribute__((aligned(256))) char scratch[kScratchBytes];
 
 struct apmoe_table {
     int L, E;
@@ -210,11 +217,15 @@ apmoe_status apmoe_create(apmoe_ctx **out, int device)
         e = hipEventCreateWithFlags(&c->side.fork, hipEventDisableTiming);
     if (e == hipSuccess)
         e = hipEventCreateWithFlags(&c->side.join, hipEventDisableTiming);
+    const hipError_t e_side = e;
+    // this device's address of the static scratch array (device current)
+    if (e == hipSuccess)
+        e = hipGetSymbolAddress(&c->scratch, HIP_SYMBOL(scratch));
     if (cur >= 0 && cur != device)
         hipSetDevice(cur);
     if (e != hipSuccess) {
         apmoe_destroy(c);
-        return hip_fail(e, "side stream of the context");
+        return hip_fail(e, e_side != hipSuccess ? "side stream of the context" : "address of the static scratch");
     }
     *out = c;
     return ok();
@@ -979,6 +990,29 @@ apmoe_status apmoe_moe_forward(apmoe_ctx *ctx, const apmoe_table *tbl, int32_t l
     if (s != APMOE_OK)
         return s;
     return apmoe_combine(ctx, y, APMOE_F32, tw, inv, T, kt, H, out, stream);
+}
+
+apmoe_status apmoe_moe_forward_noalloc(apmoe_ctx *ctx, const apmoe_table *tbl, int32_t layer, const uint16_t *x,
+                                       const uint16_t *w_router, const float *bias, int32_t T, int32_t topk,
+                                       int32_t n_shared, int32_t renormalize, uint16_t *out, void *stream)
+{
+    apmoe_status s = check_ctx(ctx);
+    if (s != APMOE_OK)
+        return s;
+    size_t need = 0;
+    s = apmoe_moe_workspace(tbl, layer, T, topk, n_shared, &need);
+    if (s != APMOE_OK)
+        return s;
+    if (need > kScratchBytes)
+        return fail(APMOE_INVALID_ARG,
+                    "layer %d at T=%d needs %zu bytes of workspace, above the %zu-byte static scratch of the "
+                    "allocation-free entry point",
+                    layer, T, need, kScratchBytes);
+    if (!ctx->scratch)
+        return fail(APMOE_HIP_ERROR, "the context has no address of the static scratch");
+    // the same launches as apmoe_moe_forward, with this device's scratch as the workspace
+    return apmoe_moe_forward(ctx, tbl, layer, x, w_router, bias, T, topk, n_shared, renormalize, ctx->scratch,
+                             kScratchBytes, out, stream);
 }
 
 }  // extern "C"

@@ -380,6 +380,26 @@ apmoe_status apmoe_moe_forward(apmoe_ctx *ctx, const apmoe_table *tbl, int32_t l
                                int32_t n_shared, int32_t renormalize, void *ws, size_t ws_bytes, uint16_t *out,
                                void *stream);
 
+/*
+ * For callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  The same layer as
+ * apmoe_moe_forward (the same launches and bits) with the workspace in a static
+ * device array of APMOE_NOALLOC_SCRATCH_BYTES that the library holds on every
+ * device it runs on until the process ends; this call allocates nothing.  Its
+ * address is taken once per context at apmoe_create.  Inputs and out as for
+ * apmoe_moe_forward.  INVALID_ARG (nothing enqueued) when the layer needs more
+ * workspace than the array holds (apmoe_moe_workspace); other errors as for
+ * apmoe_moe_forward.  Every call on one device shares that device's array and
+ * leaves its contents behind (every byte a call reads is written by the same call
+ * first, so nothing needs clearing): calls that overlap on one device -- on
+ * different streams, or from different host threads -- race and must be ordered by
+ * the caller.
+ */
+#define APMOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+apmoe_status apmoe_moe_forward_noalloc(apmoe_ctx *ctx, const apmoe_table *tbl, int32_t layer, const uint16_t *x,
+                                       const uint16_t *w_router, const float *bias, int32_t T, int32_t topk,
+                                       int32_t n_shared, int32_t renormalize, uint16_t *out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif
