@@ -3,6 +3,8 @@
 // access, and the s_waitcnt immediates of the counted waits.
 #pragma once
 
+#include <type_traits>
+
 #include "internal.h"
 
 namespace apmoe {
@@ -63,6 +65,54 @@ __device__ inline void transpose8x8(uint32_t (&d)[8])
     swap_bits<BFI>(d[2], d[3], 1, 0x55555555u);
     swap_bits<BFI>(d[4], d[5], 1, 0x55555555u);
     swap_bits<BFI>(d[6], d[7], 1, 0x55555555u);
+}
+
+// (m & a) | (~m & b) in one v_bitop3_b32 (truth table 0xE4: the third operand
+// selects between the first two).
+__device__ inline uint32_t select_bits(uint32_t m, uint32_t a, uint32_t b)
+{
+    return __builtin_amdgcn_bitop3_b32(a, b, m, (unsigned char)0xE4);
+}
+
+// The same transpose for codes of Q bits: planes p >= Q are zero on input, and the
+// swaps whose words are known zero are folded at compile time.  Each remaining swap
+// is two shifts and two selects; a swap with a zero partner is a mask and a
+// shift-and-mask.  Q = 5..8: 45..48 instructions per 32 columns.
+template <int Q>
+__device__ inline void transpose_codes(uint32_t (&d)[8])
+{
+    // stage distance s: words (i, i + j) exchange the bits of i under m << s with the
+    // bits of i + j under m
+    auto stage = [&](auto jj, int s, uint32_t m, auto nz) {
+        constexpr int J = decltype(jj)::value;
+        constexpr uint32_t NZ = decltype(nz)::value;  // bit p: word p may be nonzero
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if (i & J)
+                continue;
+            const bool za = !((NZ >> i) & 1u), zb = !((NZ >> (i + J)) & 1u);
+            const uint32_t a = d[i], b = d[i + J];
+            if (za && zb)
+                continue;
+            if (zb) {
+                d[i] = a & ~(m << s);
+                d[i + J] = (a >> s) & m;
+            } else if (za) {
+                d[i] = (b << s) & (m << s);
+                d[i + J] = b & ~m;
+            } else {
+                d[i] = select_bits(m << s, b << s, a);
+                d[i + J] = select_bits(m, a >> s, b);
+            }
+        }
+    };
+    constexpr uint32_t nz0 = (1u << Q) - 1u;
+    // after a stage, word i (and i + J) may be nonzero if either input was
+    constexpr uint32_t nz1 = nz0 | ((nz0 >> 4) | (nz0 << 4)) & 0xFFu;
+    constexpr uint32_t nz2 = nz1 | ((nz1 >> 2) & 0x33u) | ((nz1 << 2) & 0xCCu);
+    stage(std::integral_constant<int, 4>{}, 4, 0x0F0F0F0Fu, std::integral_constant<uint32_t, nz0>{});
+    stage(std::integral_constant<int, 2>{}, 2, 0x33333333u, std::integral_constant<uint32_t, nz1>{});
+    stage(std::integral_constant<int, 1>{}, 1, 0x55555555u, std::integral_constant<uint32_t, nz2>{});
 }
 
 // LDS byte address of a pointer into a __shared__ array.

@@ -28,15 +28,25 @@
 // 16-byte chunk c at position c ^ jb, so 16 lanes reading one chunk of 16 rows hit
 // distinct banks.
 //
-// LDS LUT layout: the transposed code byte v has bit p = plane p's bit, i.e. v is
-// the q-bit code with its bits reversed; entry LUT_q[n][code] is stored at
-// v*256 + 4*(32*g + i) + 2*t for q <= 7, where i is the row within the 32-row tile
-// t and g the lane half.  The 256-byte stride lets one v_perm place v above the
-// lane's constant byte to form the address; the second copy fills the rest of
-// each 256-byte row.  Gathers are conflict-free: the LDS serves a wave in two
-// halves of 32 lanes (lanes 0-31, 32-63), and within a half the 32 rows i fall in
-// 32 distinct banks.  For q = 8 one copy at v*128 + 4*i + 2*t keeps the region at
-// 32 KB (two instructions per address).
+// LDS LUT layouts.  Single lookups (q = 5..8; q = 4 with the small LUT region): the
+// transposed code byte v has bit p = plane p's bit, i.e. v is the q-bit code with its
+// bits reversed; entry LUT_q[n][code] is stored at v*256 + 4*(32*g + i) + 2*t, where
+// i is the row within the 32-row tile t and g the lane half.  The 256-byte stride
+// lets one v_perm place v above the lane's constant byte to form the address; the
+// second copy fills the rest of each 256-byte row.  Gathers are conflict-free: the
+// LDS serves a wave in two halves of 32 lanes (lanes 0-31, 32-63), and within a half
+// the 32 rows i fall in 32 distinct banks.  With the small (32 KB) region q = 8 keeps
+// one copy at v*128 + 4*i + 2*t (two instructions per address); the large (64 KB)
+// region holds both copies at every q.
+//
+// Pair lookups (q = 3; q = 4 with the large region): one ds_read_b32 returns the
+// centroids of two adjacent columns, packed as the A operand needs them.  Two stages
+// of bit-field inserts (2-bit digits, then nibbles) turn the q plane words of 32
+// columns into 16 pair indices, one per byte: bit 2p + s of index v is plane p's bit
+// of column 2m + s (m the pair).  Entry v of row (t, i) sits at v*256 + 128*t + 4*i
+// and holds LUT_q[code of the even column] in its low half and the odd column's in
+// its high half; its address is again one v_perm.  This replaces the three-stage
+// 8x8 transpose, the per-weight address and the packing of two 16-bit gathers.
 #include "device.h"
 
 namespace apmoe {
@@ -49,7 +59,8 @@ constexpr int kRows = kGemmRowsPerBlock;  // 64
 constexpr int kStepCols = 128;            // columns per wave step (2 lane halves x 64)
 constexpr int kTokTile = 32;
 constexpr int kLptExperts = 16;           // launches with at most this many experts rank them on the device
-constexpr int kLutBytes = 32 * 1024;                       // LUT region, every q
+constexpr int kSmallLut = 32 * 1024;      // LUT region sizes (LUTB): q = 4 single lookups, q = 8 one copy
+constexpr int kLargeLut = 64 * 1024;      //   q = 4 pair lookups, q = 8 two copies
 template <int KP>
 constexpr int kRedBytesOf = (KP - 1) * 2 * 16 * kWave * sizeof(float);  // column-part reduction
 constexpr int kXRowBytes = kStepCols * 2;                   // one token row of one step (fp16)
@@ -85,42 +96,66 @@ __device__ inline void load_planes(u32x2 (&w)[Q], const __amdgpu_buffer_rsrc_t (
         w[p] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs[p], (int)(word * 4u), 0, kLoadNT));
 }
 
-// 4 MFMAs over one 32-column word of each needed plane: unpack, LUT gather, multiply.
-// q = 3, two weights per lookup: the transpose input is the 3 plane words and the
-// same words shifted down one column, so output byte b of d[j] (j even) holds the
-// transposed codes of columns 8b+j (bits 0..2) and 8b+j+1 (bits 3..5) -- an index
-// into the pair table of LUT_3 (entry = two fp16, the even column's in the low half).
-// One ds_read_b32 per pair yields two A-operand elements with no repacking.
-template <int W, int XOFF>
-__device__ inline void group_product_pair3(const u32x2 (&w)[3], const uint32_t (&xaddr)[8], uint32_t lut_base,
+// Pair lookups use the index of two adjacent columns (see the file header).
+template <int Q>
+constexpr uint32_t pair_index(int ce, int co)
+{
+    uint32_t v = 0;
+    for (int p = 0; p < Q; ++p)
+        v |= (uint32_t)((ce >> (Q - 1 - p)) & 1) << (2 * p) | (uint32_t)((co >> (Q - 1 - p)) & 1) << (2 * p + 1);
+    return v;
+}
+
+__device__ inline uint32_t bfi32(uint32_t m, uint32_t a, uint32_t b) { return (m & a) | (~m & b); }
+
+// 4 MFMAs over one 32-column word of each needed plane, q = 3 or 4, pair lookups:
+// digits of planes 0/1 and 2/3 interleaved into nibbles, nibbles into bytes; p[r]
+// byte k is the index of pair 4k + r' (r' = 0, 1, 2, 3 for r = 0, 1, 2, 3 below), the
+// columns 8k + 2r', 8k + 2r' + 1.  MFMA b takes the pairs of byte b in column order,
+// so its A operand holds columns 8b .. 8b + 7 like the B fragment.
+template <int Q, int W, int XOFF>
+__device__ inline void group_product_pairs(const u32x2 (&w)[Q], const uint32_t (&xaddr)[8], uint32_t lut_base,
                                            uint32_t lane_const, float16v &acc)
 {
+    static_assert(Q == 3 || Q == 4, "pair lookups");
     u32x4 xg[4];
 #pragma unroll
     for (int b = 0; b < 4; ++b)
         xg[b] = lds_b128(xaddr[4 * W + b] + XOFF);
-    uint32_t d[8];
-#pragma unroll
-    for (int p = 0; p < 3; ++p) {
-        d[p] = w[p][W];
-        d[3 + p] = w[p][W] >> 1;
+    const uint32_t w0 = w[0][W], w1 = w[1][W], w2 = w[2][W];
+    // nibble i of a0 / a1: digit 2i / 2i+1 of planes 0 (bits 0-1) and 1 (bits 2-3)
+    const uint32_t a0 = bfi32(0x33333333u, w0, w1 << 2);
+    const uint32_t a1 = bfi32(0x33333333u, w0 >> 2, w1);
+    uint32_t h0, h1;  // the same for planes 2 and 3 (plane 3 absent at q = 3)
+    if constexpr (Q == 4) {
+        const uint32_t w3 = w[Q == 4 ? 3 : 0][W];
+        h0 = bfi32(0x33333333u, w2, w3 << 2);
+        h1 = bfi32(0x33333333u, w2 >> 2, w3);
+    } else {
+        h0 = w2 & 0x33333333u;
+        h1 = (w2 >> 2) & 0x33333333u;
     }
-    d[6] = d[7] = 0u;
-    transpose8x8<true>(d);
+    uint32_t p[4];
+    p[0] = bfi32(0x0F0F0F0Fu, a0, h0 << 4);  // digit 4k     -> columns 8k, 8k+1
+    p[1] = bfi32(0x0F0F0F0Fu, a1, h1 << 4);  // digit 4k + 1 -> 8k+2, 8k+3
+    p[2] = bfi32(0x0F0F0F0Fu, a0 >> 4, h0);  // digit 4k + 2 -> 8k+4, 8k+5
+    p[3] = bfi32(0x0F0F0F0Fu, a1 >> 4, h1);  // digit 4k + 3 -> 8k+6, 8k+7
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
         u32x4 a;
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            const uint32_t addr = __builtin_amdgcn_perm(d[2 * jj], lane_const, 0x0C0C0000u | ((4u + b) << 8));
-            a[jj] = *reinterpret_cast<const __attribute__((address_space(3))) uint32_t *>((uintptr_t)(lut_base + addr));
+        for (int r = 0; r < 4; ++r) {
+            const uint32_t addr = __builtin_amdgcn_perm(p[r], lane_const, 0x0C0C0000u | ((4u + b) << 8));
+            a[r] = *reinterpret_cast<const __attribute__((address_space(3))) uint32_t *>((uintptr_t)(lut_base + addr));
         }
         acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, a), __builtin_bit_cast(half8, xg[b]), acc,
                                                      0, 0, 0);
     }
 }
 
-template <int Q, int W, int XOFF>
+// 4 MFMAs over one 32-column word of each needed plane, single lookups: 8x8 bit
+// transpose, one gather per weight, two gathers packed per A register.
+template <int Q, int W, int XOFF, int LUTB>
 __device__ inline void group_product(const u32x2 (&w)[Q], const uint32_t (&xaddr)[8], uint32_t lut_base,
                                      uint32_t lane_const, float16v &acc)
 {
@@ -132,14 +167,14 @@ __device__ inline void group_product(const u32x2 (&w)[Q], const uint32_t (&xaddr
 #pragma unroll
     for (int p = 0; p < 8; ++p)
         d[p] = p < Q ? w[p < Q ? p : 0][W] : 0u;
-    transpose8x8<Q == 8>(d);  // the form with fewer instructions after folding (counted per q)
+    transpose_codes<Q>(d);
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
         half8 a;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             uint32_t addr;
-            if (Q < 8)
+            if (Q < 8 || LUTB == kLargeLut)
                 addr = __builtin_amdgcn_perm(d[j], lane_const, 0x0C0C0000u | ((4u + b) << 8));
             else
                 addr = (((d[j] >> (8 * b)) & 0xFFu) << 7) | lane_const;
@@ -149,32 +184,45 @@ __device__ inline void group_product(const u32x2 (&w)[Q], const uint32_t (&xaddr
     }
 }
 
+template <int Q, int LUTB>
+constexpr bool kPairs = Q == 3 || (Q == 4 && LUTB == kLargeLut);
+
 // LUT level Q of the block's two 32-row tiles (first rows nA, nB) into LDS (layouts
-// in the file header; q = 3 as the pair table).  first_loads() runs once the LUT
-// requests are out and before their data is written, so the caller's first weight
-// requests overlap the LUT's latency.
-template <int Q, int KP, typename F>
+// in the file header).  first_loads() runs once the LUT requests are out and before
+// their data is written, so the caller's first weight requests overlap the LUT's
+// latency.
+template <int Q, int KP, int LUTB, typename F>
 __device__ __attribute__((always_inline)) inline void stage_lut(const __amdgpu_buffer_rsrc_t rl, int nA, int nB,
                                                                 int N, int tid, char *smem, F &&first_loads)
 {
-    if constexpr (Q == 3) {
-        // pair table of LUT_3: entry (row 32t+i, pair code v) at v*256 + 128t + 4i;
-        // thread -> row tid % 64 and kPairsPer of the 64 pair codes
-        constexpr int kPairsPer = 64 / (kThreadsOf<KP> / kRows);
-        const int nl = tid % kRows, part = tid / kRows;
+    if constexpr (kPairs<Q, LUTB>) {
+        // pair table: entry (row nl = 32t + i, index v(ce, co)) at v*256 + 4*nl holds
+        // LUT[ce] | LUT[co] << 16.  Thread -> row nl = tid % 64 with its row's 2^Q
+        // centroids in registers; wave wv writes the entries of the odd-column codes
+        // co = wv (mod waves), every even-column code ce: 64 consecutive rows per
+        // store, all indices compile-time constants.
+        constexpr int C = 1 << Q, NW = kThreadsOf<KP> / kWave;
+        const int nl = tid % kRows;
+        const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
         const int n = (nl < 32 ? nA : nB) + (nl & 31);
-        const u32x4 lv = n < N ? __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                         rl, (int)(((uint32_t)n << 3) * 2u), 0, 0))
-                               : u32x4{0, 0, 0, 0};
-        first_loads();
-        const uint32_t slot = (uint32_t)(128 * (nl >> 5) + 4 * (nl & 31));
+        u32x4 lv[C / 8];
 #pragma unroll
-        for (int kk = 0; kk < kPairsPer; ++kk) {
-            const uint32_t v = (uint32_t)(kPairsPer * part + kk);
-            const uint32_t ce = bitrev(v & 7u, 3), co = bitrev(v >> 3, 3);  // codes of the even / odd column
-            const uint32_t lo = (lv[ce >> 1] >> (16 * (ce & 1))) & 0xFFFFu;
-            const uint32_t hi = (lv[co >> 1] >> (16 * (co & 1))) & 0xFFFFu;
-            *reinterpret_cast<uint32_t *>(smem + v * 256 + slot) = lo | (hi << 16);
+        for (int h = 0; h < C / 8; ++h)
+            lv[h] = n < N ? __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                          rl, (int)((((uint32_t)n << Q) + 8u * h) * 2u), 0, 0))
+                          : u32x4{0, 0, 0, 0};
+        first_loads();
+        char *row = smem + 4 * nl;
+#pragma unroll
+        for (int co = 0; co < C; ++co) {
+            if (co % NW != wv)
+                continue;
+            const uint32_t hi = (lv[co >> 3][(co >> 1) & 3] >> (16 * (co & 1))) << 16;
+#pragma unroll
+            for (int ce = 0; ce < C; ++ce) {
+                const uint32_t lo = (lv[ce >> 3][(ce >> 1) & 3] >> (16 * (ce & 1))) & 0xFFFFu;
+                *reinterpret_cast<uint32_t *>(row + pair_index<Q>(ce, co) * 256) = lo | hi;
+            }
         }
     } else {
         // 16-byte loads (8 entries of one row), lane -> row so that one wave touches 64 rows
@@ -207,7 +255,7 @@ __device__ __attribute__((always_inline)) inline void stage_lut(const __amdgpu_b
                 for (int e = 0; e < 8; ++e) {
                     const uint16_t v = (uint16_t)(lv[jj][e >> 1] >> (16 * (e & 1)));
                     const uint32_t vp = bitrev((uint32_t)(8 * ch + e), Q);
-                    if (Q < 8) {
+                    if (Q < 8 || LUTB == kLargeLut) {
                         *reinterpret_cast<uint16_t *>(smem + vp * 256 + 4 * il + 2 * tl) = v;
                         *reinterpret_cast<uint16_t *>(smem + vp * 256 + 4 * (32 + il) + 2 * tl) = v;
                     } else {
@@ -219,7 +267,7 @@ __device__ __attribute__((always_inline)) inline void stage_lut(const __amdgpu_b
     }
 }
 
-template <int Q, int TOKL, int KP>
+template <int Q, int TOKL, int KP, int LUTB>
 __device__ void gemm_block(const GemmParams &P, const DevBlock &blk, int rb, int r0, int Me, char *smem)
 {
     const int tid = threadIdx.x;
@@ -254,16 +302,16 @@ __device__ void gemm_block(const GemmParams &P, const DevBlock &blk, int rb, int
     // buffer (zeros, no memory traffic), and it still takes part in the barriers
     const uint32_t first_word = has_steps ? lane_word : kNoWord;
     u32x2 wc[Q];
-    stage_lut<Q, KP>(rl, nA, nB, N, tid, smem, [&] { load_planes<Q>(wc, rs, first_word); });
+    stage_lut<Q, KP, LUTB>(rl, nA, nB, N, tid, smem, [&] { load_planes<Q>(wc, rs, first_word); });
     __syncthreads();
 
     // LDS byte addresses (compile-time constants for the static array)
     const uint32_t lds_base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char *)smem);
-    const uint32_t lane_const = Q == 3  ? (uint32_t)(128 * t + 4 * i)
-                                : Q < 8 ? (uint32_t)(4 * (32 * g + i) + 2 * t)
-                                        : (uint32_t)(4 * i + 2 * t);
-    char *xs = smem + kLutBytes;
-    const uint32_t xs_base = lds_base + kLutBytes;
+    const uint32_t lane_const = kPairs<Q, LUTB>             ? (uint32_t)(128 * t + 4 * i)
+                                : Q < 8 || LUTB == kLargeLut ? (uint32_t)(4 * (32 * g + i) + 2 * t)
+                                                             : (uint32_t)(4 * i + 2 * t);
+    char *xs = smem + LUTB;
+    const uint32_t xs_base = lds_base + LUTB;
     float *red = reinterpret_cast<float *>(xs);  // used after the last token tile is read
     constexpr int kXBuf = KP * TOKL * kXRowBytes;  // one token buffer: KP parts x TOKL rows
     constexpr int kDma = TOKL / 8;                 // token copies per wave and workgroup step
@@ -329,12 +377,12 @@ __device__ void gemm_block(const GemmParams &P, const DevBlock &blk, int rb, int
             load_planes<Q>(nxt, rs, word);
             __builtin_amdgcn_sched_barrier(0);
             if (step < nsteps) {
-                if constexpr (Q == 3) {
-                    group_product_pair3<0, B * kXBuf>(cur, xaddr, lds_base, lane_const, acc);
-                    group_product_pair3<1, B * kXBuf>(cur, xaddr, lds_base, lane_const, acc);
+                if constexpr (kPairs<Q, LUTB>) {
+                    group_product_pairs<Q, 0, B * kXBuf>(cur, xaddr, lds_base, lane_const, acc);
+                    group_product_pairs<Q, 1, B * kXBuf>(cur, xaddr, lds_base, lane_const, acc);
                 } else {
-                    group_product<Q, 0, B * kXBuf>(cur, xaddr, lds_base, lane_const, acc);
-                    group_product<Q, 1, B * kXBuf>(cur, xaddr, lds_base, lane_const, acc);
+                    group_product<Q, 0, B * kXBuf, LUTB>(cur, xaddr, lds_base, lane_const, acc);
+                    group_product<Q, 1, B * kXBuf, LUTB>(cur, xaddr, lds_base, lane_const, acc);
                 }
             }
             __builtin_amdgcn_s_waitcnt(wait_vm<Q>());
@@ -411,17 +459,17 @@ __device__ void gemm_block(const GemmParams &P, const DevBlock &blk, int rb, int
     }
 }
 
-template <int TOKL, int KP>
+template <int TOKL, int KP, int LUTB>
 __device__ __attribute__((always_inline)) inline void dispatch_q(const GemmParams &P, const DevBlock &blk, int rb,
                                                                  int r0, int Me, char *smem)
 {
     switch (blk.q) {
-    case 3: gemm_block<3, TOKL, KP>(P, blk, rb, r0, Me, smem); break;
-    case 4: gemm_block<4, TOKL, KP>(P, blk, rb, r0, Me, smem); break;
-    case 5: gemm_block<5, TOKL, KP>(P, blk, rb, r0, Me, smem); break;
-    case 6: gemm_block<6, TOKL, KP>(P, blk, rb, r0, Me, smem); break;
-    case 7: gemm_block<7, TOKL, KP>(P, blk, rb, r0, Me, smem); break;
-    case 8: gemm_block<8, TOKL, KP>(P, blk, rb, r0, Me, smem); break;
+    case 3: gemm_block<3, TOKL, KP, LUTB>(P, blk, rb, r0, Me, smem); break;
+    case 4: gemm_block<4, TOKL, KP, LUTB>(P, blk, rb, r0, Me, smem); break;
+    case 5: gemm_block<5, TOKL, KP, LUTB>(P, blk, rb, r0, Me, smem); break;
+    case 6: gemm_block<6, TOKL, KP, LUTB>(P, blk, rb, r0, Me, smem); break;
+    case 7: gemm_block<7, TOKL, KP, LUTB>(P, blk, rb, r0, Me, smem); break;
+    case 8: gemm_block<8, TOKL, KP, LUTB>(P, blk, rb, r0, Me, smem); break;
     default: break;  // unreachable: commit validates q
     }
 }
@@ -429,9 +477,9 @@ __device__ __attribute__((always_inline)) inline void dispatch_q(const GemmParam
 // KIND (APMOE_GATE_UP / APMOE_DOWN) only names the launch, so profiles tell them apart.
 // The LDS region is a static array (its address is a compile-time constant, so LUT
 // gathers need no base add): LUT, then the token buffers, which the part sums reuse.
-template <int TOKL, int KP>
-constexpr int kLdsBytes = kLutBytes + (kRedBytesOf<KP> > 2 * KP * TOKL * kXRowBytes ? kRedBytesOf<KP>
-                                                                                    : 2 * KP * TOKL * kXRowBytes);
+template <int TOKL, int KP, int LUTB>
+constexpr int kLdsBytes = LUTB + (kRedBytesOf<KP> > 2 * KP * TOKL * kXRowBytes ? kRedBytesOf<KP>
+                                                                               : 2 * KP * TOKL * kXRowBytes);
 
 // Workgroup -> (expert e, row block rb).  Workgroup b runs on XCD b % 8, and XCD x
 // takes the x-th eighth of every expert's row blocks, so every XCD streams an equal
@@ -470,10 +518,10 @@ __device__ __attribute__((always_inline)) inline bool work_item(const GemmParams
     return true;
 }
 
-template <int KIND, int TOKL, int KP>
+template <int KIND, int TOKL, int KP, int LUTB>
 __global__ void __launch_bounds__(kThreadsOf<KP>) __attribute__((amdgpu_waves_per_eu(3))) gemm_kernel(GemmParams P)
 {
-    __shared__ __attribute__((aligned(16))) char smem[kLdsBytes<TOKL, KP>];
+    __shared__ __attribute__((aligned(16))) char smem[kLdsBytes<TOKL, KP, LUTB>];
     int e, rb;
     const auto key_of = [&](int u) {
         // passes over the weights x (2q + 7), a fit of the measured time per q
@@ -487,7 +535,7 @@ __global__ void __launch_bounds__(kThreadsOf<KP>) __attribute__((amdgpu_waves_pe
     if (Me <= 0 || Me > P.max_rows)
         return;  // expert without tokens (no weight reads), or one for the tile product
     const DevBlock blk = P.table[2 * e + P.kind];
-    dispatch_q<TOKL, KP>(P, blk, rb, r0, Me, smem);
+    dispatch_q<TOKL, KP, LUTB>(P, blk, rb, r0, Me, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -555,7 +603,7 @@ __device__ inline void mid_group(const uint32_t (&cur)[Q], const uint32_t (&xadd
 #pragma unroll
     for (int p = 0; p < 8; ++p)
         d[p] = p < Q ? cur[p < Q ? p : 0] : 0u;
-    transpose8x8<Q == 8 || Q == 3>(d);
+    transpose_codes<Q>(d);
     half8 a[4];
     u32x4 xb[4][TT];
     auto request = [&](auto bb) {
@@ -836,14 +884,24 @@ __attribute__((amdgpu_waves_per_eu(MODE == kMidLow ? 4 : 2, MODE == kMidLow ? 4 
     mid_dispatch_q<MODE, kMidTT>(P, blk, rb, r0, Me, smem);
 }
 
+// LUT region of the decode launch.  The large region (pair lookups at q = 4, one
+// instruction per q = 8 address) halves the workgroups per CU, and measured slower at
+// every q but 4 (q = 5: 137 -> 166 us on the Mixtral decode gate_up): the small one is
+// the default; a build may choose the large one (-DAPMOE_DECODE_LUTB=65536).
+#ifndef APMOE_DECODE_LUTB
+#define APMOE_DECODE_LUTB 32768
+#endif
+constexpr int kDecodeLut = APMOE_DECODE_LUTB;
+static_assert(kDecodeLut == kSmallLut || kDecodeLut == kLargeLut, "LUT region");
+
 template <int KIND, int KP>
 void launch_kind(const GemmParams &P, hipStream_t s)
 {
     const dim3 grid(kXcds * P.E * ((P.row_blocks + kXcds - 1) / kXcds));
     if (P.tokl == 8)
-        hipLaunchKernelGGL((gemm_kernel<KIND, 8, KP>), grid, dim3(kThreadsOf<KP>), 0, s, P);
+        hipLaunchKernelGGL((gemm_kernel<KIND, 8, KP, kDecodeLut>), grid, dim3(kThreadsOf<KP>), 0, s, P);
     else
-        hipLaunchKernelGGL((gemm_kernel<KIND, 16, KP>), grid, dim3(kThreadsOf<KP>), 0, s, P);
+        hipLaunchKernelGGL((gemm_kernel<KIND, 16, KP, kDecodeLut>), grid, dim3(kThreadsOf<KP>), 0, s, P);
 }
 
 }  // namespace

@@ -162,7 +162,7 @@ __device__ inline void word_codes(const u32x2 (&w)[Q], uint32_t (&d)[8])
 #pragma unroll
     for (int p = 0; p < 8; ++p)
         d[p] = p < Q ? w[p < Q ? p : 0][W] : 0u;
-    transpose8x8<Q == 8 || Q == 3>(d);  // the form with fewer instructions after folding (counted per q)
+    transpose_codes<Q>(d);
 }
 
 // Token stages are copied global -> LDS by the buffer unit (buffer_load ... lds):
