@@ -18,6 +18,9 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libapmoe.so")
 SAFE_LIB = os.path.join(PKG, "libapmoe_safe.so")
+# a plain HBM read stream for the benchmark's ceiling (not part of the layer)
+PROBE_SRC = "hbm_probe.hip"
+PROBE_LIB = os.path.join(PKG, "libhbmprobe.so")
 SOURCES = ["api.hip", "route.hip", "gemm.hip", "gemm_tile.hip", "elementwise.hip"]
 ARCH = "gfx950"
 
@@ -55,14 +58,15 @@ def build(verbose: bool = False, safe: bool = True) -> str:
     variants = ["main", "safe"] if safe else ["main"]
     for v in variants:
         os.makedirs(os.path.join(BUILD, v), exist_ok=True)
-    jobs = [(src, v) for v in variants for src in SOURCES]
+    jobs = [(src, v) for v in variants for src in SOURCES] + [(PROBE_SRC, "main")]
     workers = min(len(jobs), int(os.environ.get("MAX_JOBS", "8")))
     with cf.ThreadPoolExecutor(max_workers=workers) as ex:
         objs = list(ex.map(_compile, jobs))
     n = len(SOURCES)
     _link(objs[:n], LIB)
     if safe:
-        _link(objs[n:], SAFE_LIB)
+        _link(objs[n:2 * n], SAFE_LIB)
+    _link(objs[-1:], PROBE_LIB)
     if verbose:
         print("built", LIB, "and", SAFE_LIB if safe else "(no safe-wait build)")
     return LIB

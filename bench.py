@@ -430,14 +430,28 @@ def measure(timer, wl, label):
 
 
 def stream_ceiling():
-    """Practical HBM rates of this GPU: a read-only reduction and a device copy of
-    2 GiB (beyond the 256 MB last-level cache), best of 10, via PyTorch."""
+    """Practical HBM rates of this GPU over 2 GiB (beyond the 256 MB last-level
+    cache), best of 10: a plain read stream (libhbmprobe.so: 16-byte non-temporal
+    loads, 4096 workgroups) and a device copy (PyTorch)."""
+    import ctypes
+
     import torch
     n = 2 << 30
     a = torch.empty(n // 4, dtype=torch.float32, device="cuda").fill_(1.0)
     b = torch.empty_like(a)
+    probe = ctypes.CDLL(os.path.join(ROOT, "any_precision_weight_amd", "libhbmprobe.so"))
+    probe.hbm_read_probe.restype = ctypes.c_int
+    probe.hbm_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    blocks = 4096
+    sink = torch.empty(blocks * 256, dtype=torch.int32, device="cuda")
+
+    def read():
+        rc = probe.hbm_read_probe(a.data_ptr(), n, sink.data_ptr(), blocks, torch.cuda.current_stream().cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"hbm_read_probe: hipError {rc}")
+
     res = {}
-    for name, fn, nbytes in (("read_gbps", lambda: a.sum(), n), ("copy_gbps", lambda: b.copy_(a), 2 * n)):
+    for name, fn, nbytes in (("read_gbps", read, n), ("copy_gbps", lambda: b.copy_(a), 2 * n)):
         for _ in range(3):
             fn()
         best = 1e30
@@ -449,7 +463,7 @@ def stream_ceiling():
             e1.synchronize()
             best = min(best, e0.elapsed_time(e1))
         res[name] = round(nbytes / (best * 1e-3) / 1e9, 1)
-    del a, b
+    del a, b, sink
     torch.cuda.empty_cache()
     return res
 
