@@ -427,13 +427,15 @@ def test_gemm_tile_non_gather_rows():
 # weight decoded once for two 32-token tiles): the boundaries 32 / 33 and 64 / 65
 # between the three products, weight-row tails (N % 128 of 72, 8 and 40), K = 128
 # (one step) and odd numbers of steps; the other counts take the decode product (one
-# or two passes) and the tile product in the same call.  Blocks at q = 8 (the last
-# expert) take a launch of their own (64 KB LUT region).
+# or two passes) and the tile product (one to three token tiles) in the same call.
+# Blocks at q = 8 (the last expert) take a launch of their own (64 KB LUT region)
+# when the launch has many row blocks.
 MID_CASES = [
     (200, 384, [32, 64, 65, 16, 17, 33]),
     (136, 128, [128, 33, 0, 100, 1, 65]),
     (40, 640, [64, 127, 17, 96, 16, 50]),
     (256, 1152, [90, 33, 128, 0, 64, 20]),
+    (168, 384, [129, 128, 65, 64, 300, 97]),
 ]
 
 
@@ -585,12 +587,12 @@ def test_layer_shared_experts(T, renorm):
 
 
 @pytest.mark.parametrize("q", [3, 4, 5, 6, 7, 8])
-@pytest.mark.parametrize("T", [8, 100, 600])
+@pytest.mark.parametrize("T", [8, 100, 220, 600])
 def test_gemm_act_matches_two_steps(T, q):
     """The activation fused into the gate_up epilogue (decode product at T = 8, mid
     product for experts of 33..64 rows at T = 100, tile product above 64 rows at
-    T = 600) gives exactly the bits of gate_up to fp16 h followed by the activation
-    launch."""
+    T = 220 (one token tile) and T = 600 (two)) gives exactly the bits of gate_up to
+    fp16 h followed by the activation launch."""
     cfg = synth.CONFIGS[0]
     L = Layer(cfg, T=T, qmap=np.full((cfg.weight_experts, 2), q, np.int32))
     o = L.run()
