@@ -197,32 +197,39 @@ __device__ inline void phase_barrier()
     asm volatile("s_barrier" ::: "memory");
 }
 
-// One LUT entry of the lane's row: code byte b of dj (transposed code) -> fp16.  The
-// LUT region starts at LDS address lut_base (a compile-time constant: the static
-// array's address, folded into the instruction's offset).
-__device__ inline _Float16 lookup1(uint32_t dj, int b, uint32_t lane_const, uint32_t lut_base)
+// One LUT entry of the lane's row: code byte b of dj (transposed code) -> the fp16
+// bits, zero-extended.  The LUT region starts at LDS address lut_base (a
+// compile-time constant: the static array's address, folded into the instruction's
+// offset).
+__device__ inline uint32_t lookup1(uint32_t dj, int b, uint32_t lane_const, uint32_t lut_base)
 {
     const uint32_t addr = __builtin_amdgcn_perm(dj, lane_const, 0x0C0C0000u | ((4u + b) << 8));
-    return *(const __attribute__((address_space(3))) _Float16 *)(uintptr_t)(lut_base + addr);
+    return *(const __attribute__((address_space(3))) uint16_t *)(uintptr_t)(lut_base + addr);
 }
 
 // Producer side of one stage: the lane's 32 weights of word W of `wc` -> four fp16 A
-// fragments in the A buffer.
+// fragments in the A buffer.  The 32 lookups land in registers of their own and are
+// paired only after the last one is requested, so the wave waits for the LDS once.
 template <int Q, int W>
 __device__ inline void produce_a(const u32x2 (&wc)[Q], uint32_t lane_const, uint32_t lut_base, uint32_t a_dst)
 {
     uint32_t d[8];
     word_codes<Q, W>(wc, d);
-    half8 a[4];
+    uint32_t v[4][8];
 #pragma unroll
     for (int b = 0; b < 4; ++b)
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-            a[b][j] = lookup1(d[j], b, lane_const, lut_base);
+            v[b][j] = lookup1(d[j], b, lane_const, lut_base);
     __builtin_amdgcn_sched_barrier(0);  // every lookup is requested before the first is used
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
-        lds_store_b128(a_dst + 1024u * b, __builtin_bit_cast(u32x4, a[b]));
+    for (int b = 0; b < 4; ++b) {
+        u32x4 a;
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+            a[m] = v[b][2 * m] | (v[b][2 * m + 1] << 16);
+        lds_store_b128(a_dst + 1024u * b, a);
+    }
 }
 
 // Consumer side of one stage: 4 k-groups x 2 row sets x TTN token tiles.  A
