@@ -8,6 +8,7 @@
 // take effect only at safe boundaries -- here, between two launches on a stream.
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <new>
@@ -53,7 +54,20 @@ struct apmoe_ctx {
     char arch[64];
     apmoe::SideStream side;  // runs a short tile launch beside the decode and mid launches
     void *scratch = nullptr;  // this device's copy of the static scratch array (allocation-free entry point)
+    // Completion counters of the fused launches, zero between calls (each launch sets
+    // the ones it counted on back to zero): [0] the route, then kCombineCounters for
+    // the output accumulation fused into the down product.
+    int32_t *sync = nullptr;
+    bool fuse = true;  // APMOE_UNFUSED=1 at apmoe_create: every layer step in its own launches
 };
+
+static constexpr int kRouteCounter = 0;
+static constexpr int kCombineCounter0 = 64;
+static constexpr int kCombineCounters = 32 * 1024;  // tokens x 64-column blocks of one fused down call
+static constexpr size_t kSyncBytes = (size_t)(kCombineCounter0 + kCombineCounters) * sizeof(int32_t);
+// Largest assignment count (T * (topk + n_shared)) routed in one fused launch: the last
+// workgroup groups them with 256 threads.
+static constexpr int kFusedRouteMax = 2048;
 
 // Workspace of apmoe_moe_forward_noalloc: a static device array.  Every device the
 // library runs on holds its own copy from the code object's load until the process
@@ -221,11 +235,19 @@ apmoe_status apmoe_create(apmoe_ctx **out, int device)
     // this device's address of the static scratch array (device current)
     if (e == hipSuccess)
         e = hipGetSymbolAddress(&c->scratch, HIP_SYMBOL(scratch));
+    // completion counters of the fused launches, zeroed once here
+    if (e == hipSuccess)
+        e = hipMalloc(reinterpret_cast<void **>(&c->sync), kSyncBytes);
+    if (e == hipSuccess)
+        e = hipMemset(c->sync, 0, kSyncBytes);
+    const char *unfused = getenv("APMOE_UNFUSED");
+    c->fuse = !(unfused && unfused[0] == '1');
     if (cur >= 0 && cur != device)
         hipSetDevice(cur);
     if (e != hipSuccess) {
         apmoe_destroy(c);
-        return hip_fail(e, e_side != hipSuccess ? "side stream of the context" : "address of the static scratch");
+        return hip_fail(e, e_side != hipSuccess ? "side stream of the context"
+                                                : "static scratch address or counters of the context");
     }
     *out = c;
     return ok();
@@ -240,6 +262,8 @@ apmoe_status apmoe_destroy(apmoe_ctx *ctx)
             hipEventDestroy(ctx->side.fork);
         if (ctx->side.join)
             hipEventDestroy(ctx->side.join);
+        if (ctx->sync)
+            hipFree(ctx->sync);
     }
     delete ctx;
     return ok();
@@ -548,6 +572,11 @@ apmoe_status apmoe_route(apmoe_ctx *ctx, const uint16_t *x, const uint16_t *w_ro
     if ((int64_t)T * kt > (int64_t)1 << 30)
         return fail(APMOE_INVALID_ARG, "T*topk too large");
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (ctx->fuse && T > 0 && T * kt <= kFusedRouteMax) {
+        hipError_t e = apmoe::launch_route_fused(x, w_router, bias, T, H, E, topk, n_shared, renormalize, topk_ids,
+                                                 topk_w, counts, offsets, perm, inv_perm, ctx->sync + kRouteCounter, st);
+        return e == hipSuccess ? ok() : hip_fail(e, "route launch");
+    }
     hipError_t e =
         apmoe::launch_route_topk(x, w_router, bias, T, H, E, topk, n_shared, renormalize, topk_ids, topk_w, st);
     if (e != hipSuccess)
@@ -770,7 +799,8 @@ static apmoe_status gemm_limits(const apmoe_table *tbl, int layer, int kind, int
 
 static apmoe_status gemm_common(apmoe_ctx *ctx, const apmoe_table *tbl, int32_t layer, int32_t kind,
                                 const uint16_t *in, int32_t gather, const int32_t *perm, const int32_t *offsets,
-                                int32_t T, int32_t topk, void *out, int32_t out_dtype, int act, void *stream)
+                                int32_t T, int32_t topk, void *out, int32_t out_dtype, int act, void *stream,
+                                const apmoe::CombineArgs *comb = nullptr)
 {
     apmoe_status s = check_ctx(ctx);
     if (s != APMOE_OK)
@@ -812,7 +842,7 @@ static apmoe_status gemm_common(apmoe_ctx *ctx, const apmoe_table *tbl, int32_t 
         for (n = 0; n < tbl->E; ++n)
             order[n] = (uint8_t)n;
     hipError_t e = apmoe::launch_gemm(slice, kind, tbl->E, N, K, max_q, order, in, in_bytes, gather, perm, offsets,
-                                      topk, T * topk, out, out_dtype == APMOE_F32, act,
+                                      topk, T * topk, out, out_dtype == APMOE_F32, act, comb,
                                       reinterpret_cast<hipStream_t>(stream), ctx->cus, ctx->side);
     return e == hipSuccess ? ok() : hip_fail(e, "gemm launch");
 }
@@ -986,6 +1016,17 @@ apmoe_status apmoe_moe_forward(apmoe_ctx *ctx, const apmoe_table *tbl, int32_t l
     s = apmoe_gemm_act(ctx, tbl, layer, x, 1, perm, offsets, T, kt, a, stream);
     if (s != APMOE_OK)
         return s;
+    // With at most kDecodeMaxRows tokens every expert takes the decode product, and the
+    // output accumulation runs in its epilogue (same bits as the separate launch).
+    const int nb = (H + 63) / 64;
+    if (ctx->fuse && T <= apmoe::kDecodeMaxRows && (int64_t)T * nb <= kCombineCounters) {
+        apmoe::CombineArgs comb;
+        comb.w = tw;
+        comb.inv_perm = inv;
+        comb.out = out;
+        comb.cnt = ctx->sync + kCombineCounter0;
+        return gemm_common(ctx, tbl, layer, APMOE_DOWN, a, 0, perm, offsets, T, kt, y, APMOE_F32, 0, stream, &comb);
+    }
     s = apmoe_gemm(ctx, tbl, layer, APMOE_DOWN, a, 0, perm, offsets, T, kt, y, APMOE_F32, stream);
     if (s != APMOE_OK)
         return s;

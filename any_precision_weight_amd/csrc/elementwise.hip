@@ -46,20 +46,22 @@ __global__ void __launch_bounds__(256) combine_kernel(const void *__restrict__ y
         if (F32) {
             const float4 *yp = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(y) + r * H + n);
             const float4 y0 = yp[0], y1 = yp[1];
-            acc[0] += wj * y0.x;
-            acc[1] += wj * y0.y;
-            acc[2] += wj * y0.z;
-            acc[3] += wj * y0.w;
-            acc[4] += wj * y1.x;
-            acc[5] += wj * y1.y;
-            acc[6] += wj * y1.z;
-            acc[7] += wj * y1.w;
+            // one fused multiply-add per term (the down product's fused accumulation does
+            // the same, for the same bits)
+            acc[0] = __builtin_fmaf(wj, y0.x, acc[0]);
+            acc[1] = __builtin_fmaf(wj, y0.y, acc[1]);
+            acc[2] = __builtin_fmaf(wj, y0.z, acc[2]);
+            acc[3] = __builtin_fmaf(wj, y0.w, acc[3]);
+            acc[4] = __builtin_fmaf(wj, y1.x, acc[4]);
+            acc[5] = __builtin_fmaf(wj, y1.y, acc[5]);
+            acc[6] = __builtin_fmaf(wj, y1.z, acc[6]);
+            acc[7] = __builtin_fmaf(wj, y1.w, acc[7]);
         } else {
             const half8 yv = __builtin_bit_cast(
                 half8, *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(y) + r * H + n));
 #pragma unroll
             for (int i = 0; i < 8; ++i)
-                acc[i] += wj * (float)yv[i];
+                acc[i] = __builtin_fmaf(wj, (float)yv[i], acc[i]);
         }
     }
     half8 o;

@@ -74,6 +74,7 @@ struct GemmParams {
     void *out;
     int kind, E, N, K, topk, gather, out_f32, row_blocks;
     int act;               // gate_up with the activation fused: out = a [rows][N/2] fp16
+    CombineArgs comb;      // down product with the output accumulation fused (comb.out != NULL)
     int max_rows;          // decode product: experts with more rows belong to the mid / tile products
     int min_rows;          // mid product: experts with at most this many rows belong to the decode product
     int tokl;              // token rows per pass (8 or 16): the LDS token buffers' size
@@ -267,6 +268,70 @@ __device__ __attribute__((always_inline)) inline void stage_lut(const __amdgpu_b
     }
 }
 
+// Output accumulation fused into the down product (PagedWeight, Section 3.3: the fused
+// kernel ends with the output accumulation), for calls whose experts all take the
+// decode product.  A workgroup has written rows r0 .. r0 + Me - 1 of y for output
+// columns 64 rb .. 64 rb + 63 (fp32).  Token t's output at those columns needs the kt
+// rows inv_perm[t kt + j], written by the workgroups of t's kt experts with the same rb,
+// which count themselves on cnt[t][rb]; the one that counts last sums
+//   out[t][n] = sum_{j < kt} w[t kt + j] * y[inv_perm[t kt + j]][n]
+// in j order with one fp32 fma per term from zero and stores it fp16 -- the arithmetic
+// of the separate combine launch, so the same bits -- then sets the counter back to
+// zero for the next call.
+// Each XCD has its own L2.  The rows of y are stored and read with agent-scope
+// (device-coherent, sc1) accesses, so no L2 is written back or invalidated: a writing
+// wave waits for its stores to complete before the workgroup barrier, the count is an
+// agent-scope atomic issued after that barrier, and the last workgroup issues its
+// reads after the count has returned.  (Agent-scope release and acquire fences instead
+// write back and invalidate a whole L2 per workgroup; the layer was 12-20% slower.)
+__device__ __attribute__((always_inline)) inline void combine_epilogue(const GemmParams &P, int rb, int r0, int Me,
+                                                                       char *smem)
+{
+    const int tid = threadIdx.x, lane = tid % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int N = P.N, kt = P.topk;
+    const int NB = (N + kRows - 1) / kRows;
+    int *fin = reinterpret_cast<int *>(smem);  // [0]: tokens this workgroup finishes, then their ids
+    __builtin_amdgcn_s_waitcnt(wait_vm<0>());  // this wave's rows of y are stored (device-coherent)
+    __syncthreads();
+    if (wave == 0) {
+        const bool mine = lane < Me;  // Me <= kDecodeMaxRows <= 64
+        int t = 0, old = -1;
+        if (mine) {
+            t = P.perm[r0 + lane] / kt;
+            old = __hip_atomic_fetch_add(P.comb.cnt + (size_t)t * NB + rb, 1, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+        }
+        const bool last = mine && old == kt - 1;
+        const uint64_t m = __ballot(last);
+        if (last)
+            fin[1 + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u))] = t;
+        if (lane == 0)
+            fin[0] = (int)__builtin_popcountll(m);
+    }
+    __syncthreads();
+    const int nf = fin[0];
+    if (nf == 0)
+        return;
+    float *y = reinterpret_cast<float *>(P.out);
+    for (int o = tid; o < nf * kRows; o += (int)blockDim.x) {
+        const int t = fin[1 + o / kRows];
+        const int n = rb * kRows + o % kRows;
+        if (n < N) {
+            float acc = 0.f;
+            for (int j = 0; j < kt; ++j) {
+                const int a = t * kt + j;
+                const float yv = __hip_atomic_load(y + (size_t)P.comb.inv_perm[a] * N + n, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+                acc = __builtin_fmaf(P.comb.w[a], yv, acc);
+            }
+            reinterpret_cast<_Float16 *>(P.comb.out)[(size_t)t * N + n] = (_Float16)acc;
+        }
+    }
+    if (tid < nf)
+        __hip_atomic_store(P.comb.cnt + (size_t)fin[1 + tid] * NB + rb, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 template <int Q, int TOKL, int KP, int LUTB>
 __device__ void gemm_block(const GemmParams &P, const DevBlock &blk, int rb, int r0, int Me, char *smem)
 {
@@ -427,7 +492,9 @@ __device__ void gemm_block(const GemmParams &P, const DevBlock &blk, int rb, int
                 for (int v = 0; v < 16; ++v) {
                     const int d = 8 * (v >> 2) + (v & 3);
                     if (d < nleft) {
-                        if (P.out_f32)
+                        if (P.comb.out)  // read by another workgroup, maybe on another XCD
+                            __hip_atomic_store(of + d, acc[v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        else if (P.out_f32)
                             of[d] = acc[v];
                         else
                             oh[d] = (_Float16)acc[v];
@@ -457,6 +524,8 @@ __device__ void gemm_block(const GemmParams &P, const DevBlock &blk, int rb, int
         }
         __syncthreads();
     }
+    if (P.comb.out)
+        combine_epilogue(P, rb, r0, Me, smem);
 }
 
 template <int TOKL, int KP, int LUTB>
@@ -910,10 +979,11 @@ static hipError_t launch_mid(const GemmParams &P, int max_q, int act, int N, int
 
 hipError_t launch_gemm(const DevBlock *table, int kind, int E, int N, int K, int max_q, const uint8_t *order,
                        const uint16_t *in, size_t in_bytes, int gather, const int32_t *perm, const int32_t *offsets,
-                       int topk, int R, void *out, int out_f32, int act, hipStream_t s, int cus,
-                       const SideStream &side)
+                       int topk, int R, void *out, int out_f32, int act, const CombineArgs *comb, hipStream_t s,
+                       int cus, const SideStream &side)
 {
     GemmParams P;
+    P.comb = comb ? *comb : CombineArgs{};
     P.table = table;
     P.in = in;
     P.perm = perm;
@@ -948,6 +1018,8 @@ hipError_t launch_gemm(const DevBlock *table, int kind, int E, int N, int K, int
     // Gemma-like 64-token steps 1.6-1.8% faster; an 8-expert 32-token layer with them
     // was 30% slower.
     const int tokens = topk > 0 ? R / topk : R;
+    if (P.comb.out && (kind != APMOE_DOWN || !out_f32 || act || tokens > kDecodeMaxRows))
+        return hipErrorInvalidValue;  // the fused accumulation needs every expert on the decode product
     P.tokl = tokens <= 16 || (E > kLptExperts && tokens <= 64) ? 8 : 16;
     P.max_rows = kDecodeMaxRows;
     P.min_rows = 0;

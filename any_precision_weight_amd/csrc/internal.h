@@ -47,6 +47,9 @@ hipError_t launch_route_topk(const uint16_t *x, const uint16_t *wr, const float 
                              int n_shared, int renormalize, int32_t *ids, float *w, hipStream_t s);
 hipError_t launch_route_sort(const int32_t *ids, int R, int E, int32_t *counts, int32_t *offsets, int32_t *perm,
                              int32_t *inv_perm, hipStream_t s);
+hipError_t launch_route_fused(const uint16_t *x, const uint16_t *wr, const float *bias, int T, int H, int E,
+                              int topk, int n_shared, int renormalize, int32_t *ids, float *w, int32_t *counts,
+                              int32_t *offsets, int32_t *perm, int32_t *inv_perm, int32_t *done, hipStream_t s);
 hipError_t launch_route_stats(const float *w, const int32_t *perm, const int32_t *offsets, int E, double *mass,
                               double *total, int64_t *selections, hipStream_t s);
 
@@ -69,10 +72,20 @@ int tile_grid(int N, int E, int R);
 // order: the E experts by committed q, highest first, lower index on ties (a
 // scheduling hint: the decode and mid products of a launch with more than 16 experts start
 // the experts in this order; any permutation gives the same result).
+// The output accumulation fused into the down product (decode product only: the call
+// must have no expert above kDecodeMaxRows rows, i.e. R / topk <= kDecodeMaxRows tokens).
+// cnt: (R / topk) x ceil(N / 64) device counters, zero before the call and after it.
+struct CombineArgs {
+    const float *w = nullptr;          // routing weights [T][topk]
+    const int32_t *inv_perm = nullptr;  // [T * topk]
+    uint16_t *out = nullptr;           // fp16 [T][N]; NULL: no fused accumulation
+    int32_t *cnt = nullptr;
+};
+
 hipError_t launch_gemm(const DevBlock *table, int kind, int E, int N, int K, int max_q, const uint8_t *order,
                        const uint16_t *in, size_t in_bytes, int gather, const int32_t *perm, const int32_t *offsets,
-                       int topk, int R, void *out, int out_f32, int act, hipStream_t s, int cus,
-                       const SideStream &side);
+                       int topk, int R, void *out, int out_f32, int act, const CombineArgs *comb, hipStream_t s,
+                       int cus, const SideStream &side);
 hipError_t launch_gemm_tile(const DevBlock *table, int kind, int E, int N, int K, const uint16_t *in, size_t in_bytes,
                             int gather, const int32_t *perm, const int32_t *offsets, int topk, void *out, int out_f32,
                             int act, int R, hipStream_t s);

@@ -27,17 +27,16 @@ __device__ inline bool better(double za, int ea, double zb, int eb)
 // its nch partial sums in ascending c.  Every expert uses the same order.
 constexpr int kRouteThreads = 256;
 
-__global__ void __launch_bounds__(kRouteThreads) route_topk_kernel(const uint16_t *__restrict__ x,
-                                                                   const uint16_t *__restrict__ wr,
-                                                                   const float *__restrict__ bias, int T, int H,
-                                                                   int E, int topk, int n_shared, int renormalize,
-                                                                   int32_t *__restrict__ ids,
-                                                                   float *__restrict__ wout)
+template <bool COHERENT>
+__device__ __attribute__((always_inline)) inline void route_token(const uint16_t *__restrict__ x,
+                                                                 const uint16_t *__restrict__ wr,
+                                                                 const float *__restrict__ bias, int t, int H, int E,
+                                                                 int topk, int n_shared, int renormalize,
+                                                                 int32_t *__restrict__ ids, float *__restrict__ wout)
 {
     __shared__ double part[kRouteThreads];
     __shared__ double zs[APMOE_MAX_EXPERTS];
     const int tid = threadIdx.x;
-    const int t = blockIdx.x;
     int nch = 1;
     while (nch * 2 * E <= kRouteThreads)
         nch *= 2;
@@ -116,38 +115,56 @@ __global__ void __launch_bounds__(kRouteThreads) route_topk_kernel(const uint16_
         }
         const int kt = topk + n_shared;  // row: routed choices, then the shared experts (weight 1)
         for (int j = 0; j < topk; ++j) {
-            ids[(size_t)t * kt + j] = esel[j];
+            if (COHERENT)  // read by the grouping workgroup, maybe on another XCD
+                __hip_atomic_store(ids + (size_t)t * kt + j, esel[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            else
+                ids[(size_t)t * kt + j] = esel[j];
             wout[(size_t)t * kt + j] = (float)(exp(zsel[j] - zmax) / den);
         }
         for (int s = 0; s < n_shared; ++s) {
-            ids[(size_t)t * kt + topk + s] = E + s;
+            if (COHERENT)
+                __hip_atomic_store(ids + (size_t)t * kt + topk + s, E + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            else
+                ids[(size_t)t * kt + topk + s] = E + s;
             wout[(size_t)t * kt + topk + s] = 1.0f;
         }
     }
 }
 
-// Stable counting sort of the R = T*topk assignments by expert, in one
-// workgroup: per 1024-assignment chunk, every wave ranks its lanes inside each
-// expert with ballots, and waves are ordered by a prefix over per-wave counts.
-constexpr int kSortThreads = 1024;
-constexpr int kSortWaves = kSortThreads / kWave;
-
-__global__ void __launch_bounds__(kSortThreads) route_sort_kernel(const int32_t *__restrict__ ids, int R, int E,
-                                                                  int32_t *__restrict__ counts,
-                                                                  int32_t *__restrict__ offsets,
-                                                                  int32_t *__restrict__ perm,
-                                                                  int32_t *__restrict__ inv_perm)
+__global__ void __launch_bounds__(kRouteThreads) route_topk_kernel(const uint16_t *__restrict__ x,
+                                                                   const uint16_t *__restrict__ wr,
+                                                                   const float *__restrict__ bias, int H, int E,
+                                                                   int topk, int n_shared, int renormalize,
+                                                                   int32_t *__restrict__ ids,
+                                                                   float *__restrict__ wout)
 {
+    route_token<false>(x, wr, bias, (int)blockIdx.x, H, E, topk, n_shared, renormalize, ids, wout);
+}
+
+// Stable counting sort of the R = T*topk assignments by expert, in one
+// workgroup of NT threads: per NT-assignment chunk, every wave ranks its lanes inside
+// each expert with ballots, and waves are ordered by a prefix over per-wave counts.
+template <int NT, bool COHERENT>
+__device__ __attribute__((always_inline)) inline void sort_assignments(const int32_t *__restrict__ ids, int R, int E,
+                                                                       int32_t *__restrict__ counts,
+                                                                       int32_t *__restrict__ offsets,
+                                                                       int32_t *__restrict__ perm,
+                                                                       int32_t *__restrict__ inv_perm)
+{
+    constexpr int kWaves = NT / kWave;
     __shared__ int cnt[APMOE_MAX_EXPERTS];
     __shared__ int off[APMOE_MAX_EXPERTS + 1];
-    __shared__ int wcnt[kSortWaves][APMOE_MAX_EXPERTS];
+    __shared__ int wcnt[kWaves][APMOE_MAX_EXPERTS];
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
 
-    for (int e = tid; e < E; e += kSortThreads)
+    for (int e = tid; e < E; e += NT)
         cnt[e] = 0;
     __syncthreads();
-    for (int a = tid; a < R; a += kSortThreads) {
-        const int e = ids[a];
+    auto id = [&](int a) {
+        return COHERENT ? __hip_atomic_load(ids + a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : ids[a];
+    };
+    for (int a = tid; a < R; a += NT) {
+        const int e = id(a);
         if (e >= 0 && e < E)
             atomicAdd(&cnt[e], 1);
     }
@@ -158,19 +175,19 @@ __global__ void __launch_bounds__(kSortThreads) route_sort_kernel(const int32_t 
             off[e + 1] = off[e] + cnt[e];
     }
     __syncthreads();
-    for (int e = tid; e <= E; e += kSortThreads) {
+    for (int e = tid; e <= E; e += NT) {
         offsets[e] = off[e];
         if (e < E)
             counts[e] = cnt[e];
     }
     __syncthreads();
-    for (int e = tid; e < E; e += kSortThreads)
+    for (int e = tid; e < E; e += NT)
         cnt[e] = 0;  // running position inside each expert
     __syncthreads();
 
-    for (int base = 0; base < R; base += kSortThreads) {
+    for (int base = 0; base < R; base += NT) {
         const int a = base + tid;
-        int e = a < R ? ids[a] : -1;
+        int e = a < R ? id(a) : -1;
         if (e < 0 || e >= E)
             e = -1;  // never produced by the router; keeps every index in range
         // rank among lower lanes of this wave with the same expert, and whether
@@ -197,14 +214,61 @@ __global__ void __launch_bounds__(kSortThreads) route_sort_kernel(const int32_t 
             inv_perm[a] = pos;
         }
         __syncthreads();
-        for (int i = tid; i < E; i += kSortThreads) {
+        for (int i = tid; i < E; i += NT) {
             int s = 0;
-            for (int w = 0; w < kSortWaves; ++w)
+            for (int w = 0; w < kWaves; ++w)
                 s += wcnt[w][i];
             cnt[i] += s;
         }
         __syncthreads();
     }
+}
+
+constexpr int kSortThreads = 1024;
+
+__global__ void __launch_bounds__(kSortThreads) route_sort_kernel(const int32_t *__restrict__ ids, int R, int E,
+                                                                  int32_t *__restrict__ counts,
+                                                                  int32_t *__restrict__ offsets,
+                                                                  int32_t *__restrict__ perm,
+                                                                  int32_t *__restrict__ inv_perm)
+{
+    sort_assignments<kSortThreads, false>(ids, R, E, counts, offsets, perm, inv_perm);
+}
+
+// Route in one launch: workgroup t selects token t's experts as route_topk_kernel
+// does, then counts itself done on `done` (a device counter that is zero between
+// launches); the workgroup that counts last -- every token's selection is then
+// stored -- groups the assignments as route_sort_kernel does and sets `done` back to
+// zero.  Each XCD has its own L2: the selected ids are stored and read with
+// agent-scope (device-coherent, sc1) accesses, a workgroup's waves wait for those
+// stores to complete before the barrier that precedes its count, and the last
+// workgroup reads them after its count has returned -- no L2 is written back or
+// invalidated.  Same bits as the two launches: the selections are the same code, and
+// the grouping is a stable sort, whose result does not depend on the thread count.
+__global__ void __launch_bounds__(kRouteThreads) route_fused_kernel(const uint16_t *__restrict__ x,
+                                                                    const uint16_t *__restrict__ wr,
+                                                                    const float *__restrict__ bias, int T, int H,
+                                                                    int E, int topk, int n_shared, int renormalize,
+                                                                    int32_t *__restrict__ ids,
+                                                                    float *__restrict__ wout, int Et,
+                                                                    int32_t *__restrict__ counts,
+                                                                    int32_t *__restrict__ offsets,
+                                                                    int32_t *__restrict__ perm,
+                                                                    int32_t *__restrict__ inv_perm,
+                                                                    int32_t *__restrict__ done)
+{
+    __shared__ int last;
+    route_token<true>(x, wr, bias, (int)blockIdx.x, H, E, topk, n_shared, renormalize, ids, wout);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's selections are stored (device-coherent)
+    __syncthreads();
+    if (threadIdx.x == 0)
+        last = __hip_atomic_fetch_add(done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == T - 1;
+    __syncthreads();
+    if (!last)
+        return;
+    sort_assignments<kRouteThreads, true>(ids, T * (topk + n_shared), Et, counts, offsets, perm, inv_perm);
+    if (threadIdx.x == 0)
+        __hip_atomic_store(done, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 
@@ -256,8 +320,17 @@ hipError_t launch_route_topk(const uint16_t *x, const uint16_t *wr, const float 
 {
     if (T <= 0)
         return hipSuccess;
-    hipLaunchKernelGGL(route_topk_kernel, dim3(T), dim3(kRouteThreads), 0, s, x, wr, bias, T, H, E, topk,
-                       n_shared, renormalize, ids, w);
+    hipLaunchKernelGGL(route_topk_kernel, dim3(T), dim3(kRouteThreads), 0, s, x, wr, bias, H, E, topk, n_shared,
+                       renormalize, ids, w);
+    return hipGetLastError();
+}
+
+hipError_t launch_route_fused(const uint16_t *x, const uint16_t *wr, const float *bias, int T, int H, int E,
+                              int topk, int n_shared, int renormalize, int32_t *ids, float *w, int32_t *counts,
+                              int32_t *offsets, int32_t *perm, int32_t *inv_perm, int32_t *done, hipStream_t s)
+{
+    hipLaunchKernelGGL(route_fused_kernel, dim3(T), dim3(kRouteThreads), 0, s, x, wr, bias, T, H, E, topk, n_shared,
+                       renormalize, ids, w, E + n_shared, counts, offsets, perm, inv_perm, done);
     return hipGetLastError();
 }
 

@@ -114,8 +114,10 @@ int32_t apmoe_version(void);
 
 /* Bind a context to HIP device `device`.  Fails with APMOE_UNSUPPORTED on a
  * device that is not gfx950.  The context owns one stream of its own (default
- * priority) and two events, destroyed by apmoe_destroy; APMOE_HIP_ERROR if they
- * cannot be created. */
+ * priority), two events and about 128 KB of device memory for the completion counters of
+ * the fused launches (zeroed here, on `device`), released by apmoe_destroy;
+ * APMOE_HIP_ERROR if they cannot be created.  APMOE_UNFUSED=1 in the environment at
+ * this call gives a context whose layer steps always run as separate launches. */
 apmoe_status apmoe_create(apmoe_ctx **out, int device);
 apmoe_status apmoe_destroy(apmoe_ctx *ctx);
 
@@ -260,6 +262,13 @@ apmoe_status apmoe_page_in(apmoe_ctx *ctx, apmoe_table *tbl, int32_t layer, int3
  *   The later steps take kt as their topk and Et as the layer's expert count.
  * Limits: 1 <= E, E + n_shared <= 256, 1 <= topk <= min(E, 8), 0 <= n_shared <= 8,
  * T >= 0 (T = 0 writes counts and offsets only), H % 8 == 0.
+ * Launches: with T * kt <= 2048, one -- every token's selection, then the grouping by
+ * the workgroup that finishes last, which it finds with a completion counter of the
+ * context (zero between calls); above, two (selection, then grouping).  The outputs
+ * are the same bits either way.  Calls on one context that may run at the same time
+ * (different streams, host threads) share that counter and must be ordered by the
+ * caller (or use a context each).  APMOE_UNFUSED=1 in the environment at apmoe_create
+ * gives a context that always takes the two launches.
  */
 apmoe_status apmoe_route(apmoe_ctx *ctx, const uint16_t *x, const uint16_t *w_router, const float *bias, int32_t T,
                          int32_t H, int32_t E, int32_t topk, int32_t n_shared, int32_t renormalize,
@@ -268,7 +277,8 @@ apmoe_status apmoe_route(apmoe_ctx *ctx, const uint16_t *x, const uint16_t *w_ro
 
 /* Device workspace of apmoe_route for these arguments: always 0 bytes.  The
  * per-token selection runs in one workgroup per token and the expert-grouping sort
- * in the LDS of one workgroup, so the route writes only its outputs.  INVALID_ARG
+ * in the LDS of one workgroup; besides its outputs the route touches only the
+ * context's completion counter (allocated and zeroed by apmoe_create).  INVALID_ARG
  * for arguments apmoe_route would refuse. */
 apmoe_status apmoe_route_workspace(apmoe_ctx *ctx, int32_t T, int32_t E, int32_t topk, int32_t n_shared,
                                    size_t *bytes);
@@ -367,7 +377,14 @@ apmoe_status apmoe_moe_workspace(const apmoe_table *tbl, int32_t layer, int32_t 
  * Whole layer (Section 3.3 "Fused Mixed-Precision MoE Kernel": routing, expert
  * activation, down projection and output accumulation, each gate_up / down module
  * at its committed bitwidth) in four steps: route, gate_up with the activation
- * fused (apmoe_gemm_act, fp16 a), down (fp32 y), combine.
+ * fused (apmoe_gemm_act, fp16 a), down (fp32 y), combine.  With at most 32 tokens
+ * (every expert then takes the decode product) the output accumulation runs in the
+ * down product's epilogue -- the workgroup that finishes a token's last contribution
+ * to a 64-column block sums it, with the arithmetic of apmoe_combine -- so the
+ * small-batch layer is three launches (with the one-launch route); the same bits as
+ * the four steps.  The completion counters of these fused launches belong to the
+ * context: calls on one context that may run at the same time must be ordered by the
+ * caller.  APMOE_UNFUSED=1 at apmoe_create: every step in its own launches.
  * The table's experts of the layer are the routed ones (w_router rows) followed by
  * n_shared shared experts.
  * ws is caller-owned device memory of at least apmoe_moe_workspace bytes, 256-byte
