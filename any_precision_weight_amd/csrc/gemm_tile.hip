@@ -185,6 +185,15 @@ __device__ inline void x_stage(char *dst, __amdgpu_buffer_rsrc_t rx, const XStag
                                                  X.off[u], step_off, 0, 0);
 }
 
+// Instruction u of x_stage alone.
+__device__ inline void x_stage_u(char *dst, __amdgpu_buffer_rsrc_t rx, const XStage &X, int n, int nst, int u)
+{
+    n = n < nst ? n : nst - 1;
+    const uint32_t step_off = (uint32_t)((n >> 1) * kStepCols * 2 + (n & 1) * 64);  // scalar offset
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (__attribute__((address_space(3))) void *)(dst + 1024 * u), 16,
+                                             X.off[u], step_off, 0, 0);
+}
+
 // Workgroup barrier for the phase pipeline.  The wave's LDS accesses are complete
 // (lgkmcnt 0) and at most VM vector-memory requests -- token copies into LDS among
 // them -- are outstanding; a memory fence here would wait for every token copy, so
@@ -209,9 +218,11 @@ __device__ inline uint32_t lookup1(uint32_t dj, int b, uint32_t lane_const, uint
 
 // Producer side of one stage: the lane's 32 weights of word W of `wc` -> four fp16 A
 // fragments in the A buffer.  The 32 lookups land in registers of their own and are
-// paired only after the last one is requested, so the wave waits for the LDS once.
-template <int Q, int W>
-__device__ inline void produce_a(const u32x2 (&wc)[Q], uint32_t lane_const, uint32_t lut_base, uint32_t a_dst)
+// paired only after the last one is requested, so the wave waits for the LDS once;
+// `issue` (the phase's vector-memory requests) is sent while they are in flight.
+template <int Q, int W, class Issue>
+__device__ inline void produce_a(const u32x2 (&wc)[Q], uint32_t lane_const, uint32_t lut_base, uint32_t a_dst,
+                                 Issue &&issue)
 {
     uint32_t d[8];
     word_codes<Q, W>(wc, d);
@@ -219,8 +230,15 @@ __device__ inline void produce_a(const u32x2 (&wc)[Q], uint32_t lane_const, uint
 #pragma unroll
     for (int b = 0; b < 4; ++b)
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            v[b][j] = lookup1(d[j], b, lane_const, lut_base);
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int j = 4 * h; j < 4 * h + 4; ++j)
+                v[b][j] = lookup1(d[j], b, lane_const, lut_base);
+            __builtin_amdgcn_sched_barrier(0);
+            issue(2 * b + h);  // request u of the phase after the u-th group of four gathers
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    issue(8);  // the plane words (even phases)
     __builtin_amdgcn_sched_barrier(0);  // every lookup is requested before the first is used
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
@@ -363,47 +381,61 @@ __device__ __attribute__((always_inline)) void tile_block(const TileParams &P, c
         constexpr int D = L::kD;
         char *x_dst = smem + L::kX + 8192 * pw;
         u32x2 pa[Q], pb[Q];  // plane words of even / odd steps
-        // Phase n: request token stage n + D into buffer (n + D) % NXB (last read by the
-        // consumers in phase n - 1), then -- in even phases -- the plane words of step
-        // n/2 + 1, then produce A of stage n.  At the end of phase n token stage n must
-        // have landed; the requests issued after it are 8 D token copies plus the plane
-        // words of the even phases among n - D .. n (the oldest of those are due two
-        // phases later anyway): wait until at most that many are outstanding.
+        // Phase n: produce A of stage n; request token stage n + D into buffer (n + D) % NXB
+        // (last read by the consumers in phase n - 1) and, in even phases, the plane
+        // words of step n/2 + 1, in that order.  The requests go out while the stage's
+        // LUT gathers are in flight: the four producers' copies queue at the CU's vector-
+        // memory unit (≈64 B/clk), and sent first they held each producer's gathers back
+        // by ≈550 clk per phase.  With D = 0 the copies go first, as they must land in the
+        // phase they are sent in.  At the end of phase n token stage n must have landed;
+        // the requests issued after it are the plane words of its own phase (if even),
+        // then those of the D later phases, 8 copies each plus the plane words of the
+        // even ones: wait until at most that many are outstanding.
         constexpr int kWaitOdd = 8 * D + Q * (D == 0 ? 0 : 1);
         constexpr int kWaitEven = 8 * D + Q;
         auto xbuf = [&](int n) -> char * { return x_dst + (n % L::kNxb) * kStageBytes; };
+        auto phase = [&](auto wtag, const u32x2(&wc)[Q], uint32_t dst, int st, u32x2 *next, int next_step) {
+            constexpr int W = decltype(wtag)::value;
+            // request u < 8: copy instruction u of token stage st; request 8: the plane words
+            auto iss = [&](int u) {
+                if (u < 8)
+                    x_stage_u(xbuf(st), rx, X, st, nst, u);
+                else if (next)
+                    load_planes<Q, KIND == APMOE_DOWN>(*reinterpret_cast<u32x2(*)[Q]>(next), rs, step_word(next_step));
+            };
+            if constexpr (D == 0) {
+                for (int u = 0; u < 8; ++u)
+                    iss(u);
+                __builtin_amdgcn_sched_barrier(0);
+                iss(8);
+                produce_a<Q, W>(wc, lane_const, base, dst, [](int) {});
+            } else {
+                produce_a<Q, W>(wc, lane_const, base, dst, iss);
+            }
+        };
+        using W0 = std::integral_constant<int, 0>;
+        using W1 = std::integral_constant<int, 1>;
         load_planes<Q, KIND == APMOE_DOWN>(pa, rs, step_word(0));
 #pragma unroll
         for (int n = 0; n < D; ++n)
             x_stage(xbuf(n), rx, X, n, nst);
         phase_barrier<Q + 8 * D>();  // the LUT written by all waves is visible
         // phase 0: stage 0 = word 0 of step 0
-        x_stage(xbuf(D), rx, X, D, nst);
-        __builtin_amdgcn_sched_barrier(0);
-        load_planes<Q, KIND == APMOE_DOWN>(pb, rs, step_word(1));
-        produce_a<Q, 0>(pa, lane_const, base, a_dst);
+        phase(W0{}, pa, a_dst, D, pb, 1);
         phase_barrier<kWaitEven>();
         for (int m = 0; m < KT2 / 2; ++m) {
             const int n = 4 * m;
             // phase n+1: stage n+1 = word 1 of step 2m -> A buffer 1
-            x_stage(xbuf(n + 1 + D), rx, X, n + 1 + D, nst);
-            produce_a<Q, 1>(pa, lane_const, base, a_dst + kAStageBytes);
+            phase(W1{}, pa, a_dst + kAStageBytes, n + 1 + D, nullptr, 0);
             phase_barrier<kWaitOdd>();
             // phase n+2: stage n+2 = word 0 of step 2m+1 -> A buffer 0
-            x_stage(xbuf(n + 2 + D), rx, X, n + 2 + D, nst);
-            __builtin_amdgcn_sched_barrier(0);  // the plane requests follow the token copies
-            load_planes<Q, KIND == APMOE_DOWN>(pa, rs, step_word(2 * m + 2));
-            produce_a<Q, 0>(pb, lane_const, base, a_dst);
+            phase(W0{}, pb, a_dst, n + 2 + D, pa, 2 * m + 2);
             phase_barrier<kWaitEven>();
             // phase n+3: stage n+3 = word 1 of step 2m+1 -> A buffer 1
-            x_stage(xbuf(n + 3 + D), rx, X, n + 3 + D, nst);
-            produce_a<Q, 1>(pb, lane_const, base, a_dst + kAStageBytes);
+            phase(W1{}, pb, a_dst + kAStageBytes, n + 3 + D, nullptr, 0);
             phase_barrier<kWaitOdd>();
             // phase n+4: stage n+4 = word 0 of step 2m+2 -> A buffer 0
-            x_stage(xbuf(n + 4 + D), rx, X, n + 4 + D, nst);
-            __builtin_amdgcn_sched_barrier(0);
-            load_planes<Q, KIND == APMOE_DOWN>(pb, rs, step_word(2 * m + 3));
-            produce_a<Q, 0>(pa, lane_const, base, a_dst);
+            phase(W0{}, pa, a_dst, n + 4 + D, pb, 2 * m + 3);
             phase_barrier<kWaitEven>();
         }
         if (P.act)
