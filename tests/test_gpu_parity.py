@@ -312,6 +312,36 @@ def test_gemm_decode_multipass_exact(counts):
     tbl.close()
 
 
+@pytest.mark.parametrize("counts", [[2, 5, 0, 9, 4, 12], [17, 1, 3, 0, 0, 11]])
+def test_gemm_decode_two_parts_exact(counts):
+    """32 tokens with 16-row token buffers and two column parts (N/64 row blocks per
+    expert, more than 1024 in all, the headline's launch shape), every q, one expert
+    with 17 rows (two passes): every expert's rows exact against the integer matmul
+    (identity LUTs), and the fused activation equals gate_up to fp16 followed by the
+    activation launch."""
+    N, K = 11264, 256
+    tbl, keep, P, L, offsets, perm, T = _gemm_setup(GEMM_QS, counts, N, K, True, 53)
+    assert 16 < T <= 32 and N // 64 * len(GEMM_QS) > 1024
+    x = RNG.integers(-2, 3, (T, K)).astype(np.float16)
+    got = _gemm_run(tbl, x, offsets, perm, T, N, apw.F32)
+    for e, q in enumerate(GEMM_QS):
+        rows = perm[offsets[e]:offsets[e + 1]]
+        codes = oracle.unpack_codes(P[e], q).astype(np.int64)
+        ref = x[rows].astype(np.int64) @ codes.T
+        assert np.array_equal(got[offsets[e]:offsets[e + 1]], ref.astype(np.float32)), (e, q, counts[e])
+    R = int(offsets[-1])
+    h = torch.empty((R, N), dtype=torch.float16, device="cuda")
+    a2 = torch.empty((R, N // 2), dtype=torch.float16, device="cuda")
+    a1 = torch.full((R, N // 2), float("nan"), dtype=torch.float16, device="cuda")
+    xd, pd, od = dev(x), dev(perm), dev(offsets)
+    apw.gemm(ctx(), tbl, 0, apw.GATE_UP, xd, True, pd, od, T, 1, h, apw.F16)
+    apw.act(ctx(), h, R, N // 2, a2)
+    apw.gemm_act(ctx(), tbl, 0, xd, True, pd, od, T, 1, a1)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(a1).view(np.uint16), host(a2).view(np.uint16))
+    tbl.close()
+
+
 def test_gemm_many_experts_exact():
     """Above 16 experts the decode and mid products start the experts in the host's
     order of the committed q map (a scheduling hint): 40 experts, q cycling 3..8,
