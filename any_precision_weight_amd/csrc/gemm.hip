@@ -17,7 +17,9 @@
 // the A operand of v_mfma_f32_32x32x16_f16 against the expert's tokens (B operand).
 // The reduction over columns is a sum, so the order in which columns are assigned
 // to MFMA k-slots is free as long as A and B agree.  Plane words of the next step
-// are requested one step ahead.
+// are requested one step ahead.  For the down product of a batch whose experts all
+// take this product, the workgroups also accumulate the layer output
+// (combine_epilogue below).
 //
 // Token rows reach the B operand through LDS.  A workgroup step is one step of each
 // column part; its token tile (2 parts x TOKL token rows x 128 columns, fp16) is

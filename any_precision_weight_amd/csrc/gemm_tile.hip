@@ -15,24 +15,25 @@
 //     stage a lane loads, for each needed plane, one word of its row (same tiled
 //     layout as the decode product), turns the 32 columns into codes with an 8x8 bit
 //     transpose, looks them up in LUT_q (LDS) and writes the four fp16 A fragments to
-//     the stage's A buffer; it also copies its quarter of the stage's token rows
-//     global -> registers (two stages ahead) -> LDS.
+//     the stage's A buffer; it also copies its quarter of a later stage's token rows
+//     global -> LDS (buffer_load ... lds), one copy after each group of four lookups.
 //   consumer wave c (waves 0..3) multiplies weight rows 64(c%2)..+63 (two A row
 //     sets) by tokens 128(c/2)..+127 (four token tiles) with v_mfma_f32_32x32x16_f16,
 //     2 x 4 x 16 fp32 accumulators per lane; each B fragment serves two A fragments.
 // Stage n (word n%2 of 128-column step n/2) is produced in phase n and consumed in
 // phase n+1; one workgroup barrier ends each phase, and stage buffers alternate.
 //
-// LDS (160 KB, one workgroup per CU):
-//   [0, 64 KB)    LUT_q of the tile's 128 rows: entry (row nl, code) at
-//                 v*256 + 4*(nl % 64) + 2*(nl / 64), v = code with its q bits reversed
-//                 (the transposed code byte), so a lookup address is one v_perm.
-//   [64, 128 KB)  two 32 KB token stages of 256 rows x 64 columns fp16; row tr holds
-//                 eight 16-byte chunks (chunk c = columns 64*(c/4) + 32*s + 8*(c%4) of
-//                 the step, s the stage's word), stored at chunk c ^ ((tr/2) % 8) so that
-//                 16 lanes reading one chunk of 16 consecutive rows hit distinct banks.
-//   [128, 160 KB) two 16 KB A stages: fragment (producer p, k-group b) of lane L at
-//                 ((4p + b) * 64 + L) * 16.
+// LDS (160 KB, one workgroup per CU), in this order (Layout below):
+//   LUT_q of the tile's 128 rows, 2^q x 256 bytes (64 KB at q = 8): entry (row nl,
+//     code) at v*256 + 4*(nl % 64) + 2*(nl / 64), v = code with its q bits reversed
+//     (the transposed code byte), so a lookup address is one v_perm.
+//   NXB token stages of 32 KB (three where the LUT leaves room, q <= 7; two at q = 8),
+//     each 256 rows x 64 columns fp16; row tr holds eight 16-byte chunks (chunk c =
+//     columns 64*(c/4) + 32*s + 8*(c%4) of the step, s the stage's word), stored at
+//     chunk c ^ ((tr/2) % 8) so that 16 lanes reading one chunk of 16 consecutive rows
+//     hit distinct banks.
+//   two 16 KB A stages: fragment (producer p, k-group b) of lane L at
+//     ((4p + b) * 64 + L) * 16.
 //
 // Tile order: weight-row groups of 8 tiles, each with the token tiles of every served
 // expert; consecutive tiles run on the same XCD (workgroup b runs on XCD b % 8), so a
@@ -383,11 +384,12 @@ __device__ __attribute__((always_inline)) void tile_block(const TileParams &P, c
         u32x2 pa[Q], pb[Q];  // plane words of even / odd steps
         // Phase n: produce A of stage n; request token stage n + D into buffer (n + D) % NXB
         // (last read by the consumers in phase n - 1) and, in even phases, the plane
-        // words of step n/2 + 1, in that order.  The requests go out while the stage's
-        // LUT gathers are in flight: the four producers' copies queue at the CU's vector-
-        // memory unit (≈64 B/clk), and sent first they held each producer's gathers back
-        // by ≈550 clk per phase.  With D = 0 the copies go first, as they must land in the
-        // phase they are sent in.  At the end of phase n token stage n must have landed;
+        // words of step n/2 + 1, in that order.  The copies go out one after each group
+        // of four LUT gathers and the plane words after the last gather: the four
+        // producers' copies share the CU's vector-memory unit (≈64 B/clk), and issued as
+        // one burst before the transpose they held a producer back for hundreds of clocks
+        // per phase.  With D = 0 the copies go first, as they must land in the phase they
+        // are sent in.  At the end of phase n token stage n must have landed;
         // the requests issued after it are the plane words of its own phase (if even),
         // then those of the D later phases, 8 copies each plus the plane words of the
         // even ones: wait until at most that many are outstanding.
