@@ -262,7 +262,7 @@ apmoe_status apmoe_page_in(apmoe_ctx *ctx, apmoe_table *tbl, int32_t layer, int3
  *   The later steps take kt as their topk and Et as the layer's expert count.
  * Limits: 1 <= E, E + n_shared <= 256, 1 <= topk <= min(E, 8), 0 <= n_shared <= 8,
  * T >= 0 (T = 0 writes counts and offsets only), H % 8 == 0.
- * Launches: with T * kt <= 2048, one -- every token's selection, then the grouping by
+ * Launches: with T * kt <= 256, one -- every token's selection, then the grouping by
  * the workgroup that finishes last, which it finds with a completion counter of the
  * context (zero between calls); above, two (selection, then grouping).  The outputs
  * are the same bits either way.  Calls on one context that may run at the same time

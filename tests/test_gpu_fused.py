@@ -55,16 +55,19 @@ def _route(c, x_d, wr_d, bias_d, T, H, E, k, ns, renorm):
     return {n: host(t) for n, t in o.items()}
 
 
-# (T, H, E, k, n_shared, bias, renorm): one token; the Mixtral decode batches; a shared-
-# expert layer; 2048 assignments (the largest fused route) and 2050 (the two launches)
+# (T, H, E, k, n_shared, bias, renorm): one token; the Mixtral decode batches; shared-
+# expert layers; 256 assignments (the largest fused route, twice) and 258, 512 and 2050
+# (the two launches)
 ROUTE_CASES = [
     (1, 4096, 8, 2, 0, False, True),
     (16, 4096, 8, 2, 0, False, True),
     (32, 4096, 8, 2, 0, True, True),
+    (16, 2048, 60, 4, 4, False, True),
+    (28, 256, 128, 8, 1, True, False),
+    (32, 1024, 60, 4, 4, True, True),
+    (128, 512, 8, 2, 0, False, True),
+    (129, 512, 8, 2, 0, True, True),
     (64, 2048, 60, 4, 4, False, True),
-    (37, 256, 128, 8, 1, True, False),
-    (256, 1024, 8, 2, 0, False, True),
-    (1024, 256, 8, 2, 0, True, True),
     (1025, 256, 8, 2, 0, False, True),
 ]
 
