@@ -155,7 +155,11 @@ def block_bytes(n: int, k: int, b: int) -> int:
 
 
 class Context:
-    """apmoe_create / apmoe_destroy."""
+    """apmoe_create / apmoe_destroy.  A context owns a side stream and the completion
+    counters of the fused launches: calls on one context that may run at the same time
+    must be ordered by the caller (or use a context each).  APMOE_UNFUSED=1 in the
+    environment when the context is created gives one that runs every layer step in
+    its own launches."""
 
     def __init__(self, device: int = 0, library: ctypes.CDLL | None = None):
         self.L = lib() if library is None else library
