@@ -138,3 +138,34 @@ def test_layer_fused_against_oracle():
     ev = [0, 3, 9, 14, 17, 22, 28, 31]
     ref = L.oracle(eval_tokens=ev)
     check_out(got[ev], ref["out"])
+
+
+def test_two_contexts_on_two_streams():
+    """Each context owns its completion counters: two contexts running fused layers on
+    two streams at the same time (calls interleaved, no synchronisation between them)
+    give the bits of the separate launches."""
+    L = _layer("mixtral8x7b_decode_t16")
+    cfg = L.cfg
+    Ts = [16, 32, 7, 32, 24, 1]
+    refs = [_forward(unfused_ctx(), L, T) for T in Ts]
+    c2 = apw.Context(0)
+    try:
+        s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+        jobs = []
+        for i, T in enumerate(Ts):
+            c, s = (ctx(), s1) if i % 2 == 0 else (c2, s2)
+            x_d = dev(synth.gen_x(cfg, 0, T))
+            nbytes = apw.moe_workspace(L.rw.table, L.layer, T, cfg.topk, cfg.shared)
+            ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device="cuda")
+            out = torch.full((T, cfg.hidden), float("nan"), dtype=torch.float16, device="cuda")
+            torch.cuda.synchronize()  # inputs ready before either stream starts
+            jobs.append((T, x_d, ws, out))
+        for i, (T, x_d, ws, out) in enumerate(jobs):
+            c, s = (ctx(), s1) if i % 2 == 0 else (c2, s2)
+            apw.moe_forward(c, L.rw.table, L.layer, x_d, L.wr_d, L.bias_d, T, cfg.topk, cfg.renormalize, ws,
+                            ws.numel(), out, s, n_shared=cfg.shared)
+        torch.cuda.synchronize()
+        for (T, _, _, out), ref in zip(jobs, refs):
+            np.testing.assert_array_equal(host(out).view(np.uint16), ref.view(np.uint16), err_msg=f"T={T}")
+    finally:
+        c2.close()
