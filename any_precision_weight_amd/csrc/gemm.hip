@@ -228,41 +228,46 @@ __device__ __attribute__((always_inline)) inline void stage_lut(const __amdgpu_b
             }
         }
     } else {
-        // 16-byte loads (8 entries of one row), lane -> row so that one wave touches 64 rows
-        constexpr int kLutU4 = (kRows << Q) / 8;
-        constexpr int kPer = (kLutU4 + kThreadsOf<KP> - 1) / kThreadsOf<KP>;
-        constexpr int kBatch = kPer < 4 ? kPer : 4;  // loads in flight per batch (register budget)
+        // 16-byte loads (8 entries of one row); thread -> (row il of both 32-row tiles,
+        // chunk ch), so the two tiles' entries of one code, which share a word, are one
+        // 32-bit store; the 32 lanes of each half of a wave take 32 consecutive rows
+        // (distinct banks)
+        constexpr int kItems = 32 * ((1 << Q) / 8);
+        constexpr int kPer = (kItems + kThreadsOf<KP> - 1) / kThreadsOf<KP>;
+        constexpr int kBatch = kPer < 4 ? kPer : 4;  // items (two loads each) in flight per batch
 #pragma unroll
         for (int j0 = 0; j0 < kPer; j0 += kBatch) {
-            u32x4 lv[kBatch];
+            u32x4 la[kBatch], lb[kBatch];
 #pragma unroll
             for (int jj = 0; jj < kBatch; ++jj) {
                 const int idx = tid + (j0 + jj) * kThreadsOf<KP>;
-                const int nl = idx % kRows, ch = idx / kRows;
-                const int n = (nl < 32 ? nA : nB) + (nl & 31);
-                const bool ok = idx < kLutU4 && n < N;
-                lv[jj] = ok ? __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                  rl, (int)((((uint32_t)n << Q) + 8u * ch) * 2u), 0, 0))
-                            : u32x4{0, 0, 0, 0};
+                const int il = idx % 32, ch = idx / 32;
+                const bool ok = idx < kItems;
+                la[jj] = ok && nA + il < N ? __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 rl, (int)((((uint32_t)(nA + il) << Q) + 8u * ch) * 2u), 0, 0))
+                                           : u32x4{0, 0, 0, 0};
+                lb[jj] = ok && nB + il < N ? __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 rl, (int)((((uint32_t)(nB + il) << Q) + 8u * ch) * 2u), 0, 0))
+                                           : u32x4{0, 0, 0, 0};
             }
             if (j0 == 0)
                 first_loads();
 #pragma unroll
             for (int jj = 0; jj < kBatch; ++jj) {
                 const int idx = tid + (j0 + jj) * kThreadsOf<KP>;
-                if (idx >= kLutU4)
+                if (idx >= kItems)
                     break;
-                const int nl = idx % kRows, ch = idx / kRows;
-                const int il = nl & 31, tl = nl >> 5;
+                const int il = idx % 32, ch = idx / 32;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const uint16_t v = (uint16_t)(lv[jj][e >> 1] >> (16 * (e & 1)));
+                    const uint32_t sh = 16 * (e & 1);
+                    const uint32_t w = ((la[jj][e >> 1] >> sh) & 0xFFFFu) | (((lb[jj][e >> 1] >> sh) & 0xFFFFu) << 16);
                     const uint32_t vp = bitrev((uint32_t)(8 * ch + e), Q);
                     if (Q < 8 || LUTB == kLargeLut) {
-                        *reinterpret_cast<uint16_t *>(smem + vp * 256 + 4 * il + 2 * tl) = v;
-                        *reinterpret_cast<uint16_t *>(smem + vp * 256 + 4 * (32 + il) + 2 * tl) = v;
+                        *reinterpret_cast<uint32_t *>(smem + vp * 256 + 4 * il) = w;
+                        *reinterpret_cast<uint32_t *>(smem + vp * 256 + 4 * (32 + il)) = w;
                     } else {
-                        *reinterpret_cast<uint16_t *>(smem + vp * 128 + 4 * il + 2 * tl) = v;
+                        *reinterpret_cast<uint32_t *>(smem + vp * 128 + 4 * il) = w;
                     }
                 }
             }
