@@ -103,31 +103,39 @@ __device__ __attribute__((always_inline)) inline void route_token(const uint16_t
         zsel[j] = bz;
         esel[j] = be;
     }
-    if (lane == 0) {
-        const double zmax = zsel[0];
-        double den = 0.0;
-        if (renormalize) {
-            for (int j = 0; j < topk; ++j)
-                den += exp(zsel[j] - zmax);
-        } else {
-            for (int e = 0; e < E; ++e)
-                den += exp(zs[e] - zmax);
+    // Softmax weights, one lane per term: lane j < topk takes choice j's exponential;
+    // the denominator is those (renormalize) or every expert's exponential, lane u
+    // summing experts u, u + 64, ..., reduced in a fixed tree and taken from lane 0.
+    const double zmax = zsel[0];
+    double zl = zsel[0];
+    int el = esel[0];
+#pragma unroll
+    for (int j = 1; j < APMOE_MAX_TOPK; ++j)
+        if (j < topk && j == lane) {
+            zl = zsel[j];
+            el = esel[j];
         }
-        const int kt = topk + n_shared;  // row: routed choices, then the shared experts (weight 1)
-        for (int j = 0; j < topk; ++j) {
-            if (COHERENT)  // read by the grouping workgroup, maybe on another XCD
-                __hip_atomic_store(ids + (size_t)t * kt + j, esel[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            else
-                ids[(size_t)t * kt + j] = esel[j];
-            wout[(size_t)t * kt + j] = (float)(exp(zsel[j] - zmax) / den);
-        }
-        for (int s = 0; s < n_shared; ++s) {
-            if (COHERENT)
-                __hip_atomic_store(ids + (size_t)t * kt + topk + s, E + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            else
-                ids[(size_t)t * kt + topk + s] = E + s;
-            wout[(size_t)t * kt + topk + s] = 1.0f;
-        }
+    const double ex = lane < topk ? exp(zl - zmax) : 0.0;
+    double term = 0.0;
+    if (renormalize) {
+        term = ex;
+    } else {
+        for (int e = lane; e < E; e += kWave)
+            term += exp(zs[e] - zmax);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        term += __shfl_xor(term, off, kWave);
+    const double den = __shfl(term, 0, kWave);  // lane 0's sum: the same value in every lane
+    const int kt = topk + n_shared;  // row: routed choices, then the shared experts (weight 1)
+    if (lane < kt) {
+        const bool routed = lane < topk;
+        const int id = routed ? el : E + (lane - topk);
+        if (COHERENT)  // read by the grouping workgroup, maybe on another XCD
+            __hip_atomic_store(ids + (size_t)t * kt + lane, id, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else
+            ids[(size_t)t * kt + lane] = id;
+        wout[(size_t)t * kt + lane] = routed ? (float)(ex / den) : 1.0f;
     }
 }
 
@@ -160,9 +168,12 @@ __device__ __attribute__((always_inline)) inline void sort_assignments(const int
     for (int e = tid; e < E; e += NT)
         cnt[e] = 0;
     __syncthreads();
-    auto id = [&](int a) {
+    auto load_id = [&](int a) {
         return COHERENT ? __hip_atomic_load(ids + a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : ids[a];
     };
+    // with at most NT assignments each thread reads its one id once for both passes
+    const int own = R <= NT && tid < R ? load_id(tid) : -1;
+    auto id = [&](int a) { return R <= NT ? own : load_id(a); };
     for (int a = tid; a < R; a += NT) {
         const int e = id(a);
         if (e >= 0 && e < E)
