@@ -390,7 +390,10 @@ apmoe_status apmoe_moe_workspace(const apmoe_table *tbl, int32_t layer, int32_t 
  * ws is caller-owned device memory of at least apmoe_moe_workspace bytes, 256-byte
  * aligned; it holds ids, weights, counts, offsets, perm, inv_perm, a and y.
  * out fp16 [T][H].  Every argument and size limit of the four steps is checked
- * before the first launch: a refused call enqueues nothing.
+ * before the first launch: a refused call enqueues nothing.  The call enqueues only
+ * kernel launches on `stream` (and an event fork and join with the context's side
+ * stream): it can be captured in a HIP graph and replayed, the counters being reset
+ * by the kernels.
  */
 apmoe_status apmoe_moe_forward(apmoe_ctx *ctx, const apmoe_table *tbl, int32_t layer, const uint16_t *x,
                                const uint16_t *w_router, const float *bias, int32_t T, int32_t topk,
