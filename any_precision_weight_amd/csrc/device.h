@@ -29,44 +29,6 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t by
 // The low q bits of c in reverse order.
 __device__ inline uint32_t bitrev(uint32_t c, int q) { return __builtin_bitreverse32(c) >> (32 - q); }
 
-// Exchange the bits of b under m with the bits of a under m << s.  BFI: two
-// bit-field inserts from the original pair (four instructions); otherwise the xor
-// form (five), which the compiler folds further when some words are known zero.
-template <bool BFI>
-__device__ inline void swap_bits(uint32_t &a, uint32_t &b, int s, uint32_t m)
-{
-    if constexpr (BFI) {
-        const uint32_t nb = (m & (a >> s)) | (~m & b);
-        const uint32_t na = ((m << s) & (b << s)) | (~(m << s) & a);
-        a = na;
-        b = nb;
-    } else {
-        const uint32_t t = ((a >> s) ^ b) & m;
-        b ^= t;
-        a ^= t << s;
-    }
-}
-
-// In-place transpose of 4 independent 8x8 bit blocks (the delta-swap method of
-// Hacker's Delight, section 7-3): on input d[p] byte b bit j is plane p, column
-// 8b+j; on output d[j] byte b bit p holds the same bit.
-template <bool BFI>
-__device__ inline void transpose8x8(uint32_t (&d)[8])
-{
-    swap_bits<BFI>(d[0], d[4], 4, 0x0F0F0F0Fu);
-    swap_bits<BFI>(d[1], d[5], 4, 0x0F0F0F0Fu);
-    swap_bits<BFI>(d[2], d[6], 4, 0x0F0F0F0Fu);
-    swap_bits<BFI>(d[3], d[7], 4, 0x0F0F0F0Fu);
-    swap_bits<BFI>(d[0], d[2], 2, 0x33333333u);
-    swap_bits<BFI>(d[1], d[3], 2, 0x33333333u);
-    swap_bits<BFI>(d[4], d[6], 2, 0x33333333u);
-    swap_bits<BFI>(d[5], d[7], 2, 0x33333333u);
-    swap_bits<BFI>(d[0], d[1], 1, 0x55555555u);
-    swap_bits<BFI>(d[2], d[3], 1, 0x55555555u);
-    swap_bits<BFI>(d[4], d[5], 1, 0x55555555u);
-    swap_bits<BFI>(d[6], d[7], 1, 0x55555555u);
-}
-
 // (m & a) | (~m & b) in one v_bitop3_b32 (truth table 0xE4: the third operand
 // selects between the first two).
 __device__ inline uint32_t select_bits(uint32_t m, uint32_t a, uint32_t b)
@@ -74,10 +36,15 @@ __device__ inline uint32_t select_bits(uint32_t m, uint32_t a, uint32_t b)
     return __builtin_amdgcn_bitop3_b32(a, b, m, (unsigned char)0xE4);
 }
 
-// The same transpose for codes of Q bits: planes p >= Q are zero on input, and the
-// swaps whose words are known zero are folded at compile time.  Each remaining swap
-// is two shifts and two selects; a swap with a zero partner is a mask and a
-// shift-and-mask.  Q = 5..8: 45..48 instructions per 32 columns.
+// Transpose of 4 independent 8x8 bit blocks (the delta-swap method of Hacker's
+// Delight, section 7-3) for codes of Q bits: on input d[p] byte b bit j is plane p,
+// column 8b + j (planes p >= Q are zero); on output d[j] byte b bit p holds the same
+// bit.  Each stage exchanges one bit of the word index with the same bit of the bit
+// position (distance 1, 2, 4), so the three stages commute; the swaps whose words are
+// known zero are folded at compile time.  A remaining swap is two shifts and two
+// selects, a swap with a zero partner a mask and a shift-and-mask.  With the stages
+// in the order 1, 2, 4 the zero words are paired longest: Q = 3..8 take 27, 28, 41,
+// 42, 47, 48 instructions per 32 columns (39..48 in the order 4, 2, 1).
 template <int Q>
 __device__ inline void transpose_codes(uint32_t (&d)[8])
 {
@@ -106,13 +73,20 @@ __device__ inline void transpose_codes(uint32_t (&d)[8])
             }
         }
     };
+    // after a stage of distance J, words i and i + J may be nonzero if either input was
+    constexpr auto spread = [](uint32_t nz, int J) {
+        uint32_t out = nz;
+        for (int i = 0; i < 8; ++i)
+            if (!(i & J) && (((nz >> i) | (nz >> (i + J))) & 1u))
+                out |= (1u << i) | (1u << (i + J));
+        return out;
+    };
     constexpr uint32_t nz0 = (1u << Q) - 1u;
-    // after a stage, word i (and i + J) may be nonzero if either input was
-    constexpr uint32_t nz1 = nz0 | ((nz0 >> 4) | (nz0 << 4)) & 0xFFu;
-    constexpr uint32_t nz2 = nz1 | ((nz1 >> 2) & 0x33u) | ((nz1 << 2) & 0xCCu);
-    stage(std::integral_constant<int, 4>{}, 4, 0x0F0F0F0Fu, std::integral_constant<uint32_t, nz0>{});
+    constexpr uint32_t nz1 = spread(nz0, 1);
+    constexpr uint32_t nz2 = spread(nz1, 2);
+    stage(std::integral_constant<int, 1>{}, 1, 0x55555555u, std::integral_constant<uint32_t, nz0>{});
     stage(std::integral_constant<int, 2>{}, 2, 0x33333333u, std::integral_constant<uint32_t, nz1>{});
-    stage(std::integral_constant<int, 1>{}, 1, 0x55555555u, std::integral_constant<uint32_t, nz2>{});
+    stage(std::integral_constant<int, 4>{}, 4, 0x0F0F0F0Fu, std::integral_constant<uint32_t, nz2>{});
 }
 
 // LDS byte address of a pointer into a __shared__ array.

@@ -38,8 +38,10 @@
 // second copy fills the rest of each 256-byte row.  Gathers are conflict-free: the
 // LDS serves a wave in two halves of 32 lanes (lanes 0-31, 32-63), and within a half
 // the 32 rows i fall in 32 distinct banks.  With the small (32 KB) region q = 8 keeps
-// one copy at v*128 + 4*i + 2*t (two instructions per address); the large (64 KB)
-// region holds both copies at every q.
+// one copy at (v & 127)*256 + (v & 128) + 4*i + 2*t: bits 0-6 of v in the second
+// byte of the address, bit 7 in the first beside the lane's constant (< 128), so one
+// v_perm still forms each address from two words masked once per four codes; the
+// large (64 KB) region holds both copies at every q.
 //
 // Pair lookups (q = 3; q = 4 with the large region): one ds_read_b32 returns the
 // centroids of two adjacent columns, packed as the A operand needs them.  Two stages
@@ -171,16 +173,28 @@ __device__ inline void group_product(const u32x2 (&w)[Q], const uint32_t (&xaddr
     for (int p = 0; p < 8; ++p)
         d[p] = p < Q ? w[p < Q ? p : 0][W] : 0u;
     transpose_codes<Q>(d);
+    // q = 8 in the small region: bits 0-6 of each code byte go to the address's second
+    // byte, bit 7 to bit 7 of its first byte beside the lane's constant (replicated in
+    // every byte of lane_const): two masks per four codes, then one v_perm per address
+    constexpr bool kSplit = Q == 8 && LUTB == kSmallLut;
+    uint32_t lo[8];
+    if constexpr (kSplit) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            lo[j] = (d[j] & 0x80808080u) | lane_const;
+            d[j] &= 0x7F7F7F7Fu;
+        }
+    }
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
         half8 a;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             uint32_t addr;
-            if (Q < 8 || LUTB == kLargeLut)
-                addr = __builtin_amdgcn_perm(d[j], lane_const, 0x0C0C0000u | ((4u + b) << 8));
+            if constexpr (kSplit)
+                addr = __builtin_amdgcn_perm(d[j], lo[j], 0x0C0C0000u | ((4u + b) << 8) | (uint32_t)b);
             else
-                addr = (((d[j] >> (8 * b)) & 0xFFu) << 7) | lane_const;
+                addr = __builtin_amdgcn_perm(d[j], lane_const, 0x0C0C0000u | ((4u + b) << 8));
             a[j] = *reinterpret_cast<const __attribute__((address_space(3))) _Float16 *>((uintptr_t)(lut_base + addr));
         }
         acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, __builtin_bit_cast(half8, xg[b]), acc, 0, 0, 0);
@@ -267,7 +281,7 @@ __device__ __attribute__((always_inline)) inline void stage_lut(const __amdgpu_b
                         *reinterpret_cast<uint32_t *>(smem + vp * 256 + 4 * il) = w;
                         *reinterpret_cast<uint32_t *>(smem + vp * 256 + 4 * (32 + il)) = w;
                     } else {
-                        *reinterpret_cast<uint32_t *>(smem + vp * 128 + 4 * il) = w;
+                        *reinterpret_cast<uint32_t *>(smem + (vp & 0x7Fu) * 256 + (vp & 0x80u) + 4 * il) = w;
                     }
                 }
             }
@@ -381,7 +395,7 @@ __device__ void gemm_block(const GemmParams &P, const DevBlock &blk, int rb, int
     const uint32_t lds_base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char *)smem);
     const uint32_t lane_const = kPairs<Q, LUTB>             ? (uint32_t)(128 * t + 4 * i)
                                 : Q < 8 || LUTB == kLargeLut ? (uint32_t)(4 * (32 * g + i) + 2 * t)
-                                                             : (uint32_t)(4 * i + 2 * t);
+                                                             : (uint32_t)(4 * i + 2 * t) * 0x01010101u;
     char *xs = smem + LUTB;
     const uint32_t xs_base = lds_base + LUTB;
     float *red = reinterpret_cast<float *>(xs);  // used after the last token tile is read
