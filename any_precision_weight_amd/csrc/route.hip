@@ -150,8 +150,10 @@ __global__ void __launch_bounds__(kRouteThreads) route_topk_kernel(const uint16_
 }
 
 // Stable counting sort of the R = T*topk assignments by expert, in one
-// workgroup of NT threads: per NT-assignment chunk, every wave ranks its lanes inside
-// each expert with ballots, and waves are ordered by a prefix over per-wave counts.
+// workgroup of NT threads: per-expert counts, their prefix sums (one wave, 64 experts
+// per scan), then per NT-assignment chunk every wave ranks its lanes inside each
+// expert with one ballot per distinct expert in the wave, and waves are ordered by a
+// prefix over per-wave counts.
 template <int NT, bool COHERENT>
 __device__ __attribute__((always_inline)) inline void sort_assignments(const int32_t *__restrict__ ids, int R, int E,
                                                                        int32_t *__restrict__ counts,
@@ -180,10 +182,23 @@ __device__ __attribute__((always_inline)) inline void sort_assignments(const int
             atomicAdd(&cnt[e], 1);
     }
     __syncthreads();
-    if (tid == 0) {
-        off[0] = 0;
-        for (int e = 0; e < E; ++e)
-            off[e + 1] = off[e] + cnt[e];
+    if (wave == 0) {  // off[e + 1] = cnt[0] + ... + cnt[e]: inclusive scans of 64 experts
+        int carry = 0;
+        for (int c0 = 0; c0 < E; c0 += kWave) {
+            const int e = c0 + lane;
+            int x = e < E ? cnt[e] : 0;
+#pragma unroll
+            for (int d = 1; d < kWave; d <<= 1) {
+                const int y = __shfl_up(x, d, kWave);
+                if (lane >= d)
+                    x += y;
+            }
+            if (e < E)
+                off[e + 1] = carry + x;
+            carry += __shfl(x, kWave - 1, kWave);
+        }
+        if (lane == 0)
+            off[0] = 0;
     }
     __syncthreads();
     for (int e = tid; e <= E; e += NT) {
@@ -202,15 +217,20 @@ __device__ __attribute__((always_inline)) inline void sort_assignments(const int
         if (e < 0 || e >= E)
             e = -1;  // never produced by the router; keeps every index in range
         // rank among lower lanes of this wave with the same expert, and whether
-        // this lane is the last of its expert in the wave
-        int rank = 0, after = 0;
-        for (int l = 0; l < kWave; ++l) {
-            const int el = __shfl(e, l, kWave);
-            if (el == e) {
-                rank += l < lane;
-                after += l > lane;
-            }
+        // this lane is the last of its expert in the wave: one ballot per distinct
+        // expert (lanes without an assignment form one more group, unused)
+        uint64_t same = 0;
+        uint64_t todo = __ballot(1);
+        while (todo) {
+            const int u = __builtin_amdgcn_readlane(e, (int)__builtin_ctzll(todo));
+            const uint64_t m = __ballot(e == u);
+            if (e == u)
+                same = m;
+            todo &= ~m;
         }
+        const uint64_t below = (1ull << lane) - 1ull;
+        const int rank = (int)__builtin_popcountll(same & below);
+        const int after = (int)__builtin_popcountll(same & ~below) - 1;
         for (int i = lane; i < E; i += kWave)
             wcnt[wave][i] = 0;
         __syncthreads();
