@@ -89,6 +89,18 @@ __device__ inline void transpose_codes(uint32_t (&d)[8])
     stage(std::integral_constant<int, 4>{}, 4, 0x0F0F0F0Fu, std::integral_constant<uint32_t, nz2>{});
 }
 
+// Index of a pair of adjacent columns (codes ce of the even and co of the odd column)
+// in a pair table: bit 2p + s is plane p's bit of the column of parity s (code bits
+// with plane 0 most significant).
+template <int Q>
+__host__ __device__ constexpr uint32_t pair_index(int ce, int co)
+{
+    uint32_t v = 0;
+    for (int p = 0; p < Q; ++p)
+        v |= (uint32_t)((ce >> (Q - 1 - p)) & 1) << (2 * p) | (uint32_t)((co >> (Q - 1 - p)) & 1) << (2 * p + 1);
+    return v;
+}
+
 // LDS byte address of a pointer into a __shared__ array.
 __device__ inline uint32_t lds_addr(const void *p)
 {

@@ -101,16 +101,6 @@ __device__ inline void load_planes(u32x2 (&w)[Q], const __amdgpu_buffer_rsrc_t (
         w[p] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs[p], (int)(word * 4u), 0, kLoadNT));
 }
 
-// Pair lookups use the index of two adjacent columns (see the file header).
-template <int Q>
-constexpr uint32_t pair_index(int ce, int co)
-{
-    uint32_t v = 0;
-    for (int p = 0; p < Q; ++p)
-        v |= (uint32_t)((ce >> (Q - 1 - p)) & 1) << (2 * p) | (uint32_t)((co >> (Q - 1 - p)) & 1) << (2 * p + 1);
-    return v;
-}
-
 __device__ inline uint32_t bfi32(uint32_t m, uint32_t a, uint32_t b) { return (m & a) | (~m & b); }
 
 // 4 MFMAs over one 32-column word of each needed plane, q = 3 or 4, pair lookups:

@@ -26,7 +26,10 @@
 // LDS (160 KB, one workgroup per CU), in this order (Layout below):
 //   LUT_q of the tile's 128 rows, 2^q x 256 bytes (64 KB at q = 8): entry (row nl,
 //     code) at v*256 + 4*(nl % 64) + 2*(nl / 64), v = code with its q bits reversed
-//     (the transposed code byte), so a lookup address is one v_perm.
+//     (the transposed code byte), so a lookup address is one v_perm.  q = 3 instead
+//     holds a pair table (32 KB): entry (row nl, pair index v) at (nl / 64)*16 KB +
+//     v*256 + 4*(nl % 64) with the centroids of two adjacent columns, so one 32-bit
+//     gather returns a packed A word (pair_indices3).
 //   NXB token stages of 32 KB (three where the LUT leaves room, q <= 7; two at q = 8),
 //     each 256 rows x 64 columns fp16; row tr holds eight 16-byte chunks (chunk c =
 //     columns 64*(c/4) + 32*s + 8*(c%4) of the step, s the stage's word), stored at
@@ -52,6 +55,9 @@ constexpr int kLutBytes = 64 * 1024;
 constexpr int kStageBytes = kBM * 64 * 2;  // 32 KB token stage
 constexpr int kAStageBytes = 16 * 1024;     // A fragments of one stage
 constexpr int kLdsBytes = 160 * 1024;
+// q = 3: pair table, two 16 KB regions (the tile's two 64-row halves) of 64 pair
+// indices x 256 bytes
+constexpr int kPairLutBytes = 32 * 1024;
 
 // LDS layout for bitwidth Q: LUT_Q (2^Q x 256 bytes), then NXB token buffers, then
 // two A buffers.  NXB = 3 where the LUT leaves room (Q <= 7), else 2.  A token stage
@@ -59,7 +65,8 @@ constexpr int kLdsBytes = 160 * 1024;
 // being read, one is landing).
 template <int Q>
 struct Layout {
-    static constexpr int kLut = (1 << Q) * 256;
+    static constexpr int kLut = Q == 3 ? kPairLutBytes : (1 << Q) * 256;
+    static_assert(kLut <= kLutBytes, "LUT region");
     static constexpr int kNxb = kLut <= 32 * 1024 ? 3 : 2;
     static constexpr int kD = kNxb - 2;
     static constexpr int kX = kLut;
@@ -217,6 +224,24 @@ __device__ inline uint32_t lookup1(uint32_t dj, int b, uint32_t lane_const, uint
     return *(const __attribute__((address_space(3))) uint16_t *)(uintptr_t)(lut_base + addr);
 }
 
+// q = 3, pair lookups: the three plane words of the lane's 32 columns -> 16 pair
+// indices, one per byte (two stages of bit-field inserts: 2-bit digits of planes 0
+// and 1 into nibbles, then plane 2's digits beside them): bit 2p + s of an index is
+// plane p's bit of column 2m + s (m the pair), and p[r] byte b indexes the columns
+// 8b + 2r, 8b + 2r + 1.  `hsel` (bit 6 of every byte) selects the table region of
+// the lane's 64-row half.
+__device__ inline void pair_indices3(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t hsel, uint32_t (&p)[4])
+{
+    const uint32_t a0 = select_bits(0x33333333u, w0, w1 << 2);
+    const uint32_t a1 = select_bits(0x33333333u, w0 >> 2, w1);
+    const uint32_t h0 = w2 & 0x33333333u;
+    const uint32_t h1 = (w2 >> 2) & 0x33333333u;
+    p[0] = select_bits(0x0F0F0F0Fu, a0, h0 << 4) | hsel;
+    p[1] = select_bits(0x0F0F0F0Fu, a1, h1 << 4) | hsel;
+    p[2] = select_bits(0x0F0F0F0Fu, a0 >> 4, h0) | hsel;
+    p[3] = select_bits(0x0F0F0F0Fu, a1 >> 4, h1) | hsel;
+}
+
 // Producer side of one stage: the lane's 32 weights of word W of `wc` -> four fp16 A
 // fragments in the A buffer.  The 32 lookups land in registers of their own and are
 // paired only after the last one is requested, so the wave waits for the LDS once;
@@ -225,6 +250,33 @@ template <int Q, int W, class Issue>
 __device__ inline void produce_a(const u32x2 (&wc)[Q], uint32_t lane_const, uint32_t lut_base, uint32_t a_dst,
                                  Issue &&issue)
 {
+    if constexpr (Q == 3) {
+        // 16 gathers of packed pairs; byte 0 of lane_const is the lane's row slot,
+        // bit 6 of its byte 1 the region (see pair_indices3)
+        uint32_t p[4];
+        pair_indices3(wc[0][W], wc[1][W], wc[Q == 3 ? 2 : 0][W], (lane_const >> 8) * 0x01010101u, p);
+        const uint32_t slot = lane_const & 0xFFu;
+        uint32_t v[4][4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+#pragma unroll
+                for (int r = 2 * h; r < 2 * h + 2; ++r) {
+                    const uint32_t addr = __builtin_amdgcn_perm(p[r], slot, 0x0C0C0000u | ((4u + b) << 8));
+                    v[b][r] = *(const __attribute__((address_space(3))) uint32_t *)(uintptr_t)(lut_base + addr);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                issue(2 * b + h);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        issue(8);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+            lds_store_b128(a_dst + 1024u * b, u32x4{v[b][0], v[b][1], v[b][2], v[b][3]});
+        return;
+    }
     uint32_t d[8];
     word_codes<Q, W>(wc, d);
     uint32_t v[4][8];
@@ -318,7 +370,28 @@ __device__ __attribute__((always_inline)) void tile_block(const TileParams &P, c
 
     // ---- LUT level Q of the tile's rows -> LDS (row pairs nl, nl+64 share a word;
     //      lane -> row pair, so the writes of a wave hit distinct banks) ----------------
-    {
+    if constexpr (Q == 3) {
+        // pair table: entry (row pr of half h, index v(ce, co)) at h * 16 KB + v * 256 +
+        // 4 * pr holds LUT[ce] | LUT[co] << 16.  Thread -> (row pr, half h, odd-column
+        // codes 2k, 2k + 1): one 16-byte load of the row's 8 centroids, 16 stores, 64
+        // consecutive rows per store instruction.
+        const __amdgpu_buffer_rsrc_t rl = make_rsrc(blk.lut, (uint32_t)N << (Q + 1));
+        const int pr = tid % 64, h = (tid / 64) % 2, k = tid / 128;
+        const int n = (h ? rowB0 : rowA0) + pr;
+        const u32x4 l = n < N ? __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                       rl, (int)(((uint32_t)n << Q) * 2u), 0, 0))
+                              : u32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int co = 2 * k; co < 2 * k + 2; ++co) {
+            const uint32_t hi = (l[co >> 1] >> (16 * (co & 1))) << 16;
+#pragma unroll
+            for (int ce = 0; ce < 8; ++ce) {
+                const uint32_t lo = (l[ce >> 1] >> (16 * (ce & 1))) & 0xFFFFu;
+                *(__attribute__((address_space(3))) uint32_t *)(uintptr_t)(base + (uint32_t)h * 16384u +
+                                                                           pair_index<3>(ce, co) * 256u + 4u * pr) = lo | hi;
+            }
+        }
+    } else {
         const __amdgpu_buffer_rsrc_t rl = make_rsrc(blk.lut, (uint32_t)N << (Q + 1));
         constexpr int kChunksPerRow = (1 << Q) / 8;  // 16-byte chunks of one row
         constexpr int kPairChunks = 64 * kChunksPerRow;
@@ -376,7 +449,8 @@ __device__ __attribute__((always_inline)) void tile_block(const TileParams &P, c
                 X.off[u] = (uint32_t)src * (uint32_t)K * 2u + col_off[u & 1];
             }
         }
-        const uint32_t lane_const = (uint32_t)(4 * (32 * (pw & 1) + i) + 2 * (pw >> 1));
+        const uint32_t lane_const = Q == 3 ? (uint32_t)(4 * (32 * (pw & 1) + i)) | ((uint32_t)(pw >> 1) << 14)
+                                           : (uint32_t)(4 * (32 * (pw & 1) + i) + 2 * (pw >> 1));
         const uint32_t a_dst = base + Layout<Q>::kA + (uint32_t)(pw * 4 * 1024 + lane * 16);
         using L = Layout<Q>;
         constexpr int D = L::kD;
