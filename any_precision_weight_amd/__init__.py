@@ -24,7 +24,7 @@ F16, F32 = 0, 1
 MIN_BITS, MAX_BITS, PLANES = 3, 8, 8
 
 EXPORTED = [
-    "apmoe_status_string", "apmoe_last_error", "apmoe_version", "apmoe_create", "apmoe_destroy",
+    "apmoe_status_string", "apmoe_last_error", "apmoe_version", "apmoe_create", "apmoe_destroy", "apmoe_ctx_faults",
     "apmoe_block_bytes", "apmoe_table_create", "apmoe_table_destroy", "apmoe_table_set_block",
     "apmoe_table_set_bits", "apmoe_table_set_plane", "apmoe_table_validate", "apmoe_table_committed_bits",
     "apmoe_table_commit", "apmoe_lut_build", "apmoe_tiled_plane_words", "apmoe_tile_planes", "apmoe_pack_planes", "apmoe_route", "apmoe_route_workspace", "apmoe_route_stats", "apmoe_gemm",
@@ -92,6 +92,7 @@ def _declare(L):
         "apmoe_version": (I32, []),
         "apmoe_create": (S, [ctypes.POINTER(P), ctypes.c_int]),
         "apmoe_destroy": (S, [P]),
+        "apmoe_ctx_faults": (S, [P, ctypes.POINTER(I32)]),
         "apmoe_block_bytes": (I64, [I32, I32, I32]),
         "apmoe_table_create": (S, [I32, I32, ctypes.POINTER(P)]),
         "apmoe_table_destroy": (S, [P]),
@@ -159,7 +160,8 @@ class Context:
     counters of the fused launches: calls on one context that may run at the same time
     must be ordered by the caller (or use a context each).  APMOE_UNFUSED=1 in the
     environment when the context is created gives one that runs every layer step in
-    its own launches."""
+    its own launches; APMOE_LAYER_KERNEL=1 one that runs a small batch's gate_up and
+    down in one launch (the one-launch decode layer) instead of two."""
 
     def __init__(self, device: int = 0, library: ctypes.CDLL | None = None):
         self.L = lib() if library is None else library
@@ -167,6 +169,12 @@ class Context:
         _check(self.L.apmoe_create(ctypes.byref(h), device), "apmoe_create", self.L)
         self.handle = h.value
         self.device = device
+
+    def faults(self) -> int:
+        """apmoe_ctx_faults: the context's sticky fault flags (0 = none; synchronises)."""
+        v = ctypes.c_int32()
+        _check(self.L.apmoe_ctx_faults(self.handle, ctypes.byref(v)), "apmoe_ctx_faults", self.L)
+        return v.value
 
     def close(self):
         if self.handle:

@@ -55,13 +55,19 @@ struct apmoe_ctx {
     apmoe::SideStream side;  // runs a short tile launch beside the decode and mid launches
     void *scratch = nullptr;  // this device's copy of the static scratch array (allocation-free entry point)
     // Completion counters of the fused launches, zero between calls (each launch sets
-    // the ones it counted on back to zero): [0] the route, then kCombineCounters for
-    // the output accumulation fused into the down product.
+    // the ones it counted on back to zero): [0] the route, [16, 16 + kLsWords) the
+    // one-launch decode layer's work list, then kCombineCounters for the output
+    // accumulation fused into the down product.
     int32_t *sync = nullptr;
     bool fuse = true;  // APMOE_UNFUSED=1 at apmoe_create: every layer step in its own launches
+    // APMOE_LAYER_KERNEL=1 at apmoe_create: gate_up and down of a small batch in one
+    // launch (the one-launch decode layer) instead of two
+    bool layer_kernel = false;
 };
 
 static constexpr int kRouteCounter = 0;
+static constexpr int kLayerSync = 16;
+static_assert(kLayerSync + apmoe::kLsWords <= 64, "layer counters below the combine counters");
 static constexpr int kCombineCounter0 = 64;
 static constexpr int kCombineCounters = 32 * 1024;  // tokens x 64-column blocks of one fused down call
 static constexpr size_t kSyncBytes = (size_t)(kCombineCounter0 + kCombineCounters) * sizeof(int32_t);
@@ -244,6 +250,8 @@ apmoe_status apmoe_create(apmoe_ctx **out, int device)
         e = hipMemset(c->sync, 0, kSyncBytes);
     const char *unfused = getenv("APMOE_UNFUSED");
     c->fuse = !(unfused && unfused[0] == '1');
+    const char *one = getenv("APMOE_LAYER_KERNEL");
+    c->layer_kernel = c->fuse && one && one[0] == '1';
     if (cur >= 0 && cur != device)
         hipSetDevice(cur);
     if (e != hipSuccess) {
@@ -268,6 +276,23 @@ apmoe_status apmoe_destroy(apmoe_ctx *ctx)
             hipFree(ctx->sync);
     }
     delete ctx;
+    return ok();
+}
+
+apmoe_status apmoe_ctx_faults(apmoe_ctx *ctx, int32_t *flags)
+{
+    apmoe_status s = check_ctx(ctx);
+    if (s != APMOE_OK)
+        return s;
+    if (!flags)
+        return fail(APMOE_INVALID_ARG, "flags is NULL");
+    hipError_t e = hipDeviceSynchronize();
+    int32_t v = 0;
+    if (e == hipSuccess)
+        e = hipMemcpy(&v, ctx->sync + kLayerSync + apmoe::kLsFault, sizeof(v), hipMemcpyDeviceToHost);
+    if (e != hipSuccess)
+        return hip_fail(e, "reading the fault flags");
+    *flags = v ? APMOE_FAULT_LAYER_WAIT : 0;
     return ok();
 }
 
@@ -1014,21 +1039,28 @@ apmoe_status apmoe_moe_forward(apmoe_ctx *ctx, const apmoe_table *tbl, int32_t l
                     offsets, perm, inv, stream);
     if (s != APMOE_OK || T == 0)
         return s;
+    // With at most kDecodeMaxRows tokens every expert takes the decode product, and the
+    // output accumulation runs in the down product's epilogue (same bits as the separate
+    // launch); where the shapes allow, gate_up and down then run as one launch (same bits).
+    const int nb = (H + 63) / 64;
+    const bool fuse_comb = ctx->fuse && T <= apmoe::kDecodeMaxRows && (int64_t)T * nb <= kCombineCounters;
+    apmoe::CombineArgs comb;
+    comb.w = tw;
+    comb.inv_perm = inv;
+    comb.out = out;
+    comb.cnt = ctx->sync + kCombineCounter0;
+    if (fuse_comb && ctx->layer_kernel && apmoe::layer_launch_fits(tbl->E, H, F, T)) {
+        const DevBlock *slice = tbl->d_table + tbl->index(layer, 0, 0);
+        hipError_t e = apmoe::launch_layer(slice, tbl->E, H, F, x, perm, offsets, kt, T, a, y, comb,
+                                           ctx->sync + kLayerSync, reinterpret_cast<hipStream_t>(stream));
+        return e == hipSuccess ? ok() : hip_fail(e, "layer launch");
+    }
     // gate_up with SiLU(gate) * up in its epilogue (F = K of down is a multiple of 128)
     s = apmoe_gemm_act(ctx, tbl, layer, x, 1, perm, offsets, T, kt, a, stream);
     if (s != APMOE_OK)
         return s;
-    // With at most kDecodeMaxRows tokens every expert takes the decode product, and the
-    // output accumulation runs in its epilogue (same bits as the separate launch).
-    const int nb = (H + 63) / 64;
-    if (ctx->fuse && T <= apmoe::kDecodeMaxRows && (int64_t)T * nb <= kCombineCounters) {
-        apmoe::CombineArgs comb;
-        comb.w = tw;
-        comb.inv_perm = inv;
-        comb.out = out;
-        comb.cnt = ctx->sync + kCombineCounter0;
+    if (fuse_comb)
         return gemm_common(ctx, tbl, layer, APMOE_DOWN, a, 0, perm, offsets, T, kt, y, APMOE_F32, 0, stream, &comb);
-    }
     s = apmoe_gemm(ctx, tbl, layer, APMOE_DOWN, a, 0, perm, offsets, T, kt, y, APMOE_F32, stream);
     if (s != APMOE_OK)
         return s;

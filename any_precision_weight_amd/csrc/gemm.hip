@@ -51,6 +51,8 @@
 // and holds LUT_q[code of the even column] in its low half and the odd column's in
 // its high half; its address is again one v_perm.  This replaces the three-stage
 // 8x8 transpose, the per-weight address and the packing of two 16-bit gathers.
+#include <algorithm>
+
 #include "device.h"
 
 namespace apmoe {
@@ -86,6 +88,18 @@ struct GemmParams {
     uint32_t plane_bytes;  // bytes of one tiled plane
     uint8_t order[APMOE_MAX_EXPERTS];  // experts by committed q, highest first (launches with E > 16)
 };
+
+// Work list of the one-launch decode layer (layer_kernel): both products' parameters
+// and its counters in the context (LayerSync offsets in internal.h).
+struct LayerParams {
+    // [APMOE_GATE_UP]: gate_up with the activation fused (act = 1), out = a;
+    // [APMOE_DOWN]: down with the output accumulation fused (comb.out set), in = a
+    GemmParams p[2];
+    int32_t *sync;
+    int items_gu, items_dn;
+};
+
+constexpr int max_i(int a, int b) { return a > b ? a : b; }
 
 // Plane bases are wave-uniform (scalar registers); the per-lane part is a 32-bit
 // word offset into the tiled plane, so each load is one buffer_load_dwordx2 with a
@@ -343,12 +357,28 @@ __device__ __attribute__((always_inline)) inline void combine_epilogue(const Gem
         __hip_atomic_store(P.comb.cnt + (size_t)fin[1 + tid] * NB + rb, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int Q, int TOKL, int KP, int LUTB>
+// Where a block's waves sit in their workgroup and its LDS.  HALVES = 1: a workgroup
+// of its own.  HALVES = 2: half HALF of a paired workgroup that runs two 64-row blocks
+// of one expert in lockstep (the same steps, token passes and barriers): each half
+// stages its own LUT at HALF * LUTB and keeps its own part-sum slots, and the two
+// share the token buffers after both LUTs, copied by all of the workgroup's waves.
+// COH: the activation epilogue stores `a` device-coherently (sc1), for a later work
+// item of the same launch that reads it, maybe on another XCD.
+template <int HALVES, int HALF, bool COH>
+struct Seat {
+    static constexpr int kHalves = HALVES, kHalf = HALF;
+    static constexpr bool kCoherent = COH;
+};
+using Alone = Seat<1, 0, false>;
+
+template <int Q, int TOKL, int KP, int LUTB, typename S = Alone>
 __device__ void gemm_block(const GemmParams &P, const DevBlock &blk, int rb, int r0, int Me, char *smem)
 {
-    const int tid = threadIdx.x;
+    const int gtid = threadIdx.x;
+    const int tid = gtid - S::kHalf * kThreadsOf<KP>;  // thread of this block
     const int lane = tid % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform (scalar)
+    const int gwave = __builtin_amdgcn_readfirstlane(gtid / kWave);  // wave of the workgroup
     const int t = wave & 1, part = wave >> 1;  // row tile, column part
     const int i = lane & 31, g = lane >> 5;
     const int N = P.N, K = P.K;
@@ -378,31 +408,35 @@ __device__ void gemm_block(const GemmParams &P, const DevBlock &blk, int rb, int
     // buffer (zeros, no memory traffic), and it still takes part in the barriers
     const uint32_t first_word = has_steps ? lane_word : kNoWord;
     u32x2 wc[Q];
-    stage_lut<Q, KP, LUTB>(rl, nA, nB, N, tid, smem, [&] { load_planes<Q>(wc, rs, first_word); });
+    stage_lut<Q, KP, LUTB>(rl, nA, nB, N, tid, smem + S::kHalf * LUTB, [&] { load_planes<Q>(wc, rs, first_word); });
     __syncthreads();
 
     // LDS byte addresses (compile-time constants for the static array)
-    const uint32_t lds_base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char *)smem);
+    const uint32_t lds_base = lds_addr(smem) + S::kHalf * LUTB;  // this block's LUT
     const uint32_t lane_const = kPairs<Q, LUTB>             ? (uint32_t)(128 * t + 4 * i)
                                 : Q < 8 || LUTB == kLargeLut ? (uint32_t)(4 * (32 * g + i) + 2 * t)
                                                              : (uint32_t)(4 * i + 2 * t) * 0x01010101u;
-    char *xs = smem + LUTB;
-    const uint32_t xs_base = lds_base + LUTB;
-    float *red = reinterpret_cast<float *>(xs);  // used after the last token tile is read
+    char *xs = smem + S::kHalves * LUTB;
+    const uint32_t xs_base = lds_addr(smem) + S::kHalves * LUTB;
+    // part-sum slots of this block, used after the last token tile is read
+    float *red = reinterpret_cast<float *>(xs) + S::kHalf * (kRedBytesOf<KP> / (int)sizeof(float));
     constexpr int kXBuf = KP * TOKL * kXRowBytes;  // one token buffer: KP parts x TOKL rows
-    constexpr int kDma = TOKL / 8;                 // token copies per wave and workgroup step
+    constexpr int kCopies = KP * TOKL / 4;         // copy instructions per buffer (4 token rows each)
+    constexpr int kNW = S::kHalves * 2 * KP;       // the waves that share them
+    constexpr int kDma = (kCopies + kNW - 1) / kNW;  // token copies per wave and workgroup step
     const int nws = (nsteps + KP - 1) / KP;         // workgroup steps: part p takes step KP s + p
 
     for (int tp = 0; tp < Me; tp += TOKL) {
         const int j = lane & 31;  // token column of this lane in the B operand and in D
         const bool tok_ok = j < TOKL && tp + j < Me;
-        // token copies: instruction u = wave + 2 KP k fills rows 4u .. 4u+3 of a buffer; lane L
-        // writes 16-byte position L % 16 of row 4u + L / 16 (part row / TOKL, token row
-        // % TOKL) and fetches the chunk stored there, chunk = position ^ token row
+        // token copies: instruction u = gwave + kNW k < kCopies fills rows 4u .. 4u+3 of a
+        // buffer; lane L writes 16-byte position L % 16 of row 4u + L / 16 (part row / TOKL,
+        // token row % TOKL) and fetches the chunk stored there, chunk = position ^ token row
         uint32_t doff[kDma];
 #pragma unroll
         for (int k = 0; k < kDma; ++k) {
-            const int row = 4 * (wave + 2 * KP * k) + (lane >> 4);
+            // (an instruction number past kCopies is not issued; its row is never used)
+            const int row = 4 * (kDma * kNW == kCopies ? gwave + kNW * k : (gwave + kNW * k) % kCopies) + (lane >> 4);
             const int pu = row / TOKL, jj = row % TOKL;
             const int c = (lane & 15) ^ jj;
             const int tok = tp + jj;
@@ -415,9 +449,10 @@ __device__ void gemm_block(const GemmParams &P, const DevBlock &blk, int rb, int
         auto copy_tokens = [&](int s, int b) {
 #pragma unroll
             for (int k = 0; k < kDma; ++k)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rx, (__attribute__((address_space(3))) void *)(xs + b * kXBuf + 1024 * (wave + 2 * KP * k)),
-                    16, doff[k] + (uint32_t)s * (uint32_t)(KP * kStepCols * 2), 0, 0, 0);
+                if (kDma * kNW == kCopies || gwave + kNW * k < kCopies)  // wave-uniform
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        rx, (__attribute__((address_space(3))) void *)(xs + b * kXBuf + 1024 * (gwave + kNW * k)),
+                        16, doff[k] + (uint32_t)s * (uint32_t)(KP * kStepCols * 2), 0, 0, 0);
         };
         // B-operand addresses in buffer 0: fragment f of word W is chunk 8g + 4W + f of this
         // lane's token row in its part; lanes of token columns >= TOKL repeat a row (their
@@ -526,10 +561,23 @@ __device__ void gemm_block(const GemmParams &P, const DevBlock &blk, int rb, int
                 // rows f = nA + 4g + 8(v/4) + v%4 < F of token row r0 + tp + j
                 _Float16 *oa = reinterpret_cast<_Float16 *>(P.out) + (size_t)(r0 + tp + j) * (size_t)(N >> 1) +
                                (size_t)(nA + 4 * g);
+                if constexpr (S::kCoherent) {
+                    // the four rows 8(v/4) .. +3 in one 8-byte device-coherent store
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const _Float16 up = (_Float16)red[slot(1, 1, v)];
-                    oa[8 * (v >> 2) + (v & 3)] = silu_mul((_Float16)acc[v], up);
+                    for (int v4 = 0; v4 < 4; ++v4) {
+                        half4 h;
+#pragma unroll
+                        for (int u = 0; u < 4; ++u)
+                            h[u] = silu_mul((_Float16)acc[4 * v4 + u], (_Float16)red[slot(1, 1, 4 * v4 + u)]);
+                        __hip_atomic_store(reinterpret_cast<uint64_t *>(oa + 8 * v4), __builtin_bit_cast(uint64_t, h),
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    }
+                } else {
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const _Float16 up = (_Float16)red[slot(1, 1, v)];
+                        oa[8 * (v >> 2) + (v & 3)] = silu_mul((_Float16)acc[v], up);
+                    }
                 }
             }
         }
@@ -539,17 +587,17 @@ __device__ void gemm_block(const GemmParams &P, const DevBlock &blk, int rb, int
         combine_epilogue(P, rb, r0, Me, smem);
 }
 
-template <int TOKL, int KP, int LUTB>
+template <int TOKL, int KP, int LUTB, typename S = Alone>
 __device__ __attribute__((always_inline)) inline void dispatch_q(const GemmParams &P, const DevBlock &blk, int rb,
                                                                  int r0, int Me, char *smem)
 {
     switch (blk.q) {
-    case 3: gemm_block<3, TOKL, KP, LUTB>(P, blk, rb, r0, Me, smem); break;
-    case 4: gemm_block<4, TOKL, KP, LUTB>(P, blk, rb, r0, Me, smem); break;
-    case 5: gemm_block<5, TOKL, KP, LUTB>(P, blk, rb, r0, Me, smem); break;
-    case 6: gemm_block<6, TOKL, KP, LUTB>(P, blk, rb, r0, Me, smem); break;
-    case 7: gemm_block<7, TOKL, KP, LUTB>(P, blk, rb, r0, Me, smem); break;
-    case 8: gemm_block<8, TOKL, KP, LUTB>(P, blk, rb, r0, Me, smem); break;
+    case 3: gemm_block<3, TOKL, KP, LUTB, S>(P, blk, rb, r0, Me, smem); break;
+    case 4: gemm_block<4, TOKL, KP, LUTB, S>(P, blk, rb, r0, Me, smem); break;
+    case 5: gemm_block<5, TOKL, KP, LUTB, S>(P, blk, rb, r0, Me, smem); break;
+    case 6: gemm_block<6, TOKL, KP, LUTB, S>(P, blk, rb, r0, Me, smem); break;
+    case 7: gemm_block<7, TOKL, KP, LUTB, S>(P, blk, rb, r0, Me, smem); break;
+    case 8: gemm_block<8, TOKL, KP, LUTB, S>(P, blk, rb, r0, Me, smem); break;
     default: break;  // unreachable: commit validates q
     }
 }
@@ -571,16 +619,12 @@ constexpr int kLdsBytes = LUTB + (kRedBytesOf<KP> > 2 * KP * TOKL * kXRowBytes ?
 // (0 when this launch does not serve it), then the lower index: lane u holds expert
 // u's key and every wave computes the ranks.  Above 16 experts the host's order of
 // the committed q map is used.  Returns false for grid padding.
+// The expert of rank j (0 = longest key first, lower index on ties): with at most 16
+// experts lane u holds key_of(u) and every wave computes the ranks; above 16 the host's
+// order of the committed q map.  Wave-uniform.
 template <typename KeyOf>
-__device__ __attribute__((always_inline)) inline bool work_item(const GemmParams &P, const KeyOf &key_of, int &e,
-                                                                int &rb)
+__device__ __attribute__((always_inline)) inline int expert_of_rank(const GemmParams &P, const KeyOf &key_of, int j)
 {
-    const int r8 = (P.row_blocks + kXcds - 1) / kXcds;
-    const int l = (int)(blockIdx.x / kXcds);
-    const int j = l / r8;  // rank of the expert
-    rb = (int)(blockIdx.x % kXcds) * r8 + l % r8;
-    if (j >= P.E || rb >= P.row_blocks)
-        return false;
     if (P.E <= kLptExperts) {
         const int lane = (int)(threadIdx.x % kWave);
         const int key = lane < P.E ? key_of(lane) : 0;
@@ -591,10 +635,22 @@ __device__ __attribute__((always_inline)) inline bool work_item(const GemmParams
             rank += v < P.E && (kv > key || (kv == key && v < lane));
         }
         const uint64_t hit = __ballot(lane < P.E && rank == j);  // exactly one lane: ranks are distinct
-        e = __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(hit));
-    } else {
-        e = P.order[j];
+        return __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(hit));
     }
+    return P.order[j];
+}
+
+template <typename KeyOf>
+__device__ __attribute__((always_inline)) inline bool work_item(const GemmParams &P, const KeyOf &key_of, int &e,
+                                                                int &rb)
+{
+    const int r8 = (P.row_blocks + kXcds - 1) / kXcds;
+    const int l = (int)(blockIdx.x / kXcds);
+    const int j = l / r8;  // rank of the expert
+    rb = (int)(blockIdx.x % kXcds) * r8 + l % r8;
+    if (j >= P.E || rb >= P.row_blocks)
+        return false;
+    e = expert_of_rank(P, key_of, j);
     return true;
 }
 
@@ -974,6 +1030,110 @@ __attribute__((amdgpu_waves_per_eu(MODE == kMidLow ? 4 : 2, MODE == kMidLow ? 4 
 constexpr int kDecodeLut = APMOE_DECODE_LUTB;
 static_assert(kDecodeLut == kSmallLut || kDecodeLut == kLargeLut, "LUT region");
 
+// ---------------------------------------------------------------------------
+// One-launch decode layer (PagedWeight, Section 3.3: routing, expert activation, down
+// projection and output accumulation in one fused kernel; here the launch after the
+// one-launch route): the gate_up product with its activation epilogue, then the down
+// product with the output accumulation in its epilogue, for batches whose experts all
+// take the decode product.  Each 8-wave workgroup takes a ticket from a device counter
+// when it starts and runs work item `ticket`:
+//   [0, G)      gate_up: expert rank j = i / P2, row-block pair i % P2 (P2 = F / 64).
+//               The workgroup's two halves run the pair's two 64-row blocks in
+//               lockstep, each as the 4-wave decode workgroup (KP = 2, its own LUT,
+//               the token buffers shared), store a device-coherently and count the
+//               pair on done[e];
+//   [G, G + D)  down: expert rank j = i' / NB, row block i' % NB (NB = H / 64): the
+//               8-wave decode workgroup (KP = 4) with the output accumulation, once
+//               done[e] = P2 (every row of a the expert reads is stored).
+// So the down blocks fill the slots that the last gate_up blocks leave, with no
+// launch boundary between the products.  A workgroup waits only for gate_up items,
+// which never wait, and a down ticket is drawn only after every gate_up ticket has
+// gone to a workgroup that is running, so every wait ends, in whatever order the
+// hardware starts the workgroups.  (A bound on the wait far above any item's length
+// turns a broken count into a fault flag instead of a hang.)  Rows of a are read only
+// after the wait, by plain loads: the launch starts with no line of a in any cache,
+// and each 128-byte line of a is written by one workgroup (a pair covers 128 bytes of
+// each token row).  The last workgroup to finish sets the counters back to zero.  Each
+// block does the arithmetic of the separate gate_up (KP = 2) and down (KP = 4)
+// launches, so the bits are theirs.
+// ---------------------------------------------------------------------------
+template <int TOKL>
+constexpr int kLayerLds = max_i(2 * kDecodeLut + max_i(2 * kRedBytesOf<2>, 2 * 2 * TOKL * kXRowBytes),
+                                kLdsBytes<TOKL, 4, kDecodeLut>);
+constexpr int kLayerSpin = 1 << 24;  // s_sleep rounds before a wait gives up (about a second)
+
+template <int TOKL>
+__global__ void __launch_bounds__(kThreadsOf<4>) __attribute__((amdgpu_waves_per_eu(4)))
+layer_kernel(LayerParams L)
+{
+    __shared__ __attribute__((aligned(16))) char smem[kLayerLds<TOKL>];
+    // the item number, read by every wave before the item's first barrier: the last 16
+    // bytes of the region, which an item first writes after that barrier (token buffers)
+    // or not at all
+    int *item = reinterpret_cast<int *>(smem + kLayerLds<TOKL> - 16);
+    if (threadIdx.x == 0)
+        *item = __hip_atomic_fetch_add(L.sync + kLsNext, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int it = __builtin_amdgcn_readfirstlane(*item);
+    const int pairs = L.p[APMOE_GATE_UP].row_blocks / 2;
+    const int kind = it < L.items_gu ? APMOE_GATE_UP : APMOE_DOWN;
+    // the item's parameters, indexed by a kind the compiler cannot see through: one set of
+    // scalar registers holds the fields of whichever product the item is
+    int ko = __builtin_amdgcn_readfirstlane(kind);
+    asm volatile("" : "+s"(ko));
+    const GemmParams &P = L.p[ko];
+    const int i2 = kind == APMOE_GATE_UP ? it : it - L.items_gu;
+    const int nb = kind == APMOE_GATE_UP ? pairs : P.row_blocks;  // work items per expert
+    const auto key_of = [&](int u) {
+        const int mu = P.offsets[u + 1] - P.offsets[u];
+        return mu > 0 && mu <= P.max_rows ? (mu + TOKL - 1) / TOKL * (2 * P.table[2 * u + P.kind].q + 7) : 0;
+    };
+    if (i2 < P.E * nb) {
+        const int e = expert_of_rank(P, key_of, i2 / nb);
+        const int rb = i2 % nb;
+        const int r0 = P.offsets[e];
+        const int Me = P.offsets[e + 1] - r0;
+        const DevBlock blk = P.table[2 * e + P.kind];
+        if (Me <= 0 || Me > P.max_rows) {
+            // no rows: no work, and no down item of this expert waits
+        } else if (kind == APMOE_GATE_UP) {
+            if (threadIdx.x < kThreadsOf<2>)
+                dispatch_q<TOKL, 2, kDecodeLut, Seat<2, 0, true>>(P, blk, 2 * rb, r0, Me, smem);
+            else
+                dispatch_q<TOKL, 2, kDecodeLut, Seat<2, 1, true>>(P, blk, 2 * rb + 1, r0, Me, smem);
+            __builtin_amdgcn_s_waitcnt(wait_vm<0>());  // this wave's rows of a are stored (device-coherent)
+            __syncthreads();
+            if (threadIdx.x == 0)
+                __hip_atomic_fetch_add(L.sync + kLsDone + e, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+            if (threadIdx.x == 0) {
+                int n = 0;
+                while (__hip_atomic_load(L.sync + kLsDone + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < pairs) {
+                    __builtin_amdgcn_s_sleep(2);
+                    if (++n >= kLayerSpin) {
+                        __hip_atomic_store(L.sync + kLsFault, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        break;
+                    }
+                }
+            }
+            __syncthreads();
+            dispatch_q<TOKL, 4, kDecodeLut>(P, blk, rb, r0, Me, smem);
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const int old = __hip_atomic_fetch_add(L.sync + kLsExit, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (old == (int)gridDim.x - 1) {  // every other workgroup is done
+            for (int u = 0; u < L.p[APMOE_GATE_UP].E; ++u)
+                __hip_atomic_store(L.sync + kLsDone + u, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(L.sync + kLsNext, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(L.sync + kLsExit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
+
+
 template <int KIND, int KP>
 void launch_kind(const GemmParams &P, hipStream_t s)
 {
@@ -988,10 +1148,10 @@ void launch_kind(const GemmParams &P, hipStream_t s)
 
 static hipError_t launch_mid(const GemmParams &P, int max_q, int act, int N, int E, hipStream_t s);
 
-hipError_t launch_gemm(const DevBlock *table, int kind, int E, int N, int K, int max_q, const uint8_t *order,
-                       const uint16_t *in, size_t in_bytes, int gather, const int32_t *perm, const int32_t *offsets,
-                       int topk, int R, void *out, int out_f32, int act, const CombineArgs *comb, hipStream_t s,
-                       int cus, const SideStream &side)
+static GemmParams gemm_params(const DevBlock *table, int kind, int E, int N, int K, const uint8_t *order,
+                              const uint16_t *in, size_t in_bytes, int gather, const int32_t *perm,
+                              const int32_t *offsets, int topk, void *out, int out_f32, int act,
+                              const CombineArgs *comb)
 {
     GemmParams P;
     P.comb = comb ? *comb : CombineArgs{};
@@ -1013,7 +1173,55 @@ hipError_t launch_gemm(const DevBlock *table, int kind, int E, int N, int K, int
     P.in_bytes = (uint32_t)in_bytes;
     P.plane_bytes = (uint32_t)(tiled_plane_words(N, K) * 4);
     for (int u = 0; u < E; ++u)
-        P.order[u] = order[u];
+        P.order[u] = order ? order[u] : (uint8_t)u;
+    P.max_rows = kDecodeMaxRows;
+    P.min_rows = 0;
+    return P;
+}
+
+// Token rows per pass of the decode product's LDS buffers for a batch of `tokens`.
+static int decode_tokl(int tokens, int E) { return tokens <= 16 || (E > kLptExperts && tokens <= 64) ? 8 : 16; }
+
+// Four column parts (8-wave workgroups) when the launch has few row blocks.
+static bool decode_wide(int row_blocks, int E) { return (long)row_blocks * E <= 4 * 256; }
+
+bool layer_launch_fits(int E, int H, int F, int T)
+{
+    return T >= 1 && T <= kDecodeMaxRows && E >= 1 && E <= kLptExperts && F % 64 == 0 && !decode_wide(F / 32, E) &&
+           decode_wide((H + kRows - 1) / kRows, E);
+}
+
+hipError_t launch_layer(const DevBlock *table, int E, int H, int F, const uint16_t *x, const int32_t *perm,
+                        const int32_t *offsets, int topk, int T, uint16_t *a, float *y, const CombineArgs &comb,
+                        int32_t *sync, hipStream_t s)
+{
+    if (!layer_launch_fits(E, H, F, T) || !comb.out)
+        return hipErrorInvalidValue;
+    const int R = T * topk;
+    LayerParams L;
+    GemmParams &gu = L.p[APMOE_GATE_UP], &dn = L.p[APMOE_DOWN];
+    gu = gemm_params(table, APMOE_GATE_UP, E, 2 * F, H, nullptr, x, (size_t)T * H * 2, 1, perm, offsets, topk, a, 0, 1,
+                     nullptr);
+    dn = gemm_params(table, APMOE_DOWN, E, H, F, nullptr, a, (size_t)R * F * 2, 0, perm, offsets, topk, y, 1, 0, &comb);
+    gu.tokl = dn.tokl = decode_tokl(T, E);
+    L.sync = sync;
+    L.items_gu = E * (gu.row_blocks / 2);
+    L.items_dn = E * dn.row_blocks;
+    const int grid = L.items_gu + L.items_dn;  // one item per workgroup, in the order they start
+    if (gu.tokl == 8)
+        hipLaunchKernelGGL(layer_kernel<8>, dim3(grid), dim3(kThreadsOf<4>), 0, s, L);
+    else
+        hipLaunchKernelGGL(layer_kernel<16>, dim3(grid), dim3(kThreadsOf<4>), 0, s, L);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm(const DevBlock *table, int kind, int E, int N, int K, int max_q, const uint8_t *order,
+                       const uint16_t *in, size_t in_bytes, int gather, const int32_t *perm, const int32_t *offsets,
+                       int topk, int R, void *out, int out_f32, int act, const CombineArgs *comb, hipStream_t s,
+                       int cus, const SideStream &side)
+{
+    GemmParams P = gemm_params(table, kind, E, N, K, order, in, in_bytes, gather, perm, offsets, topk, out, out_f32,
+                               act, comb);
     // A token is routed to an expert at most once, so no expert has more rows than the
     // batch has tokens (R / topk; a shared expert has exactly that many).  The token
     // buffers hold 8 rows up to 16 tokens (40 KB of LDS: four workgroups per CU; with 16
@@ -1031,9 +1239,7 @@ hipError_t launch_gemm(const DevBlock *table, int kind, int E, int N, int K, int
     const int tokens = topk > 0 ? R / topk : R;
     if (P.comb.out && (kind != APMOE_DOWN || !out_f32 || act || tokens > kDecodeMaxRows))
         return hipErrorInvalidValue;  // the fused accumulation needs every expert on the decode product
-    P.tokl = tokens <= 16 || (E > kLptExperts && tokens <= 64) ? 8 : 16;
-    P.max_rows = kDecodeMaxRows;
-    P.min_rows = 0;
+    P.tokl = decode_tokl(tokens, E);
     // A tile launch of at most two tiles per CU (by its bound) cannot fill the GPU for
     // long, and each of its tiles is long: it runs on the context's side stream beside
     // the decode and mid launches (they serve other experts and write other rows),
@@ -1056,7 +1262,7 @@ hipError_t launch_gemm(const DevBlock *table, int kind, int E, int N, int K, int
     }
     // Few workgroups (the down product's N / 64 row blocks) leave two per CU: four
     // column parts then give each CU four waves per SIMD instead of two.
-    const bool wide = (long)P.row_blocks * E <= 4 * 256;
+    const bool wide = decode_wide(P.row_blocks, E);
     if (kind == APMOE_GATE_UP)
         wide ? launch_kind<APMOE_GATE_UP, 4>(P, s) : launch_kind<APMOE_GATE_UP, 2>(P, s);
     else

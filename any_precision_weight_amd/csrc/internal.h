@@ -86,6 +86,19 @@ hipError_t launch_gemm(const DevBlock *table, int kind, int E, int N, int K, int
                        const uint16_t *in, size_t in_bytes, int gather, const int32_t *perm, const int32_t *offsets,
                        int topk, int R, void *out, int out_f32, int act, const CombineArgs *comb, hipStream_t s,
                        int cus, const SideStream &side);
+// The one-launch decode layer: gate_up with the activation and down with the output
+// accumulation in one persistent launch (gemm.hip, layer_kernel), for batches of at most
+// kDecodeMaxRows tokens over at most 16 experts whose separate launches would take two
+// column parts for gate_up and four for down (the same bits).  Its counters, at `sync`
+// (int32, zero before the first launch; every launch leaves them zero except the fault
+// flag): the next work item, the workgroups that have finished, a sticky flag set when a
+// wait gave up (a broken count; never expected), and per expert the gate_up pairs done.
+constexpr int kLsNext = 0, kLsExit = 1, kLsFault = 2, kLsDone = 8;
+constexpr int kLsWords = kLsDone + 16;
+bool layer_launch_fits(int E, int H, int F, int T);
+hipError_t launch_layer(const DevBlock *table, int E, int H, int F, const uint16_t *x, const int32_t *perm,
+                        const int32_t *offsets, int topk, int T, uint16_t *a, float *y, const CombineArgs &comb,
+                        int32_t *sync, hipStream_t s);
 hipError_t launch_gemm_tile(const DevBlock *table, int kind, int E, int N, int K, const uint16_t *in, size_t in_bytes,
                             int gather, const int32_t *perm, const int32_t *offsets, int topk, void *out, int out_f32,
                             int act, int R, hipStream_t s);

@@ -564,6 +564,8 @@ def main() -> int:
     ap.add_argument("--settle-max-s", type=float, default=8.0, help="warm-up seconds at most")
     ap.add_argument("--copies", type=int, default=2, help="resident weight copies of a single-layer decode workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--layer-kernel", action="store_true",
+                    help="small decode batches: gate_up and down in one launch (APMOE_LAYER_KERNEL=1)")
     ap.add_argument("--uniform-q", type=int, default=0, metavar="Q",
                     help="single-layer workload: every block at bitwidth Q (per-q study)")
     ap.add_argument("--workload", default="suite",
@@ -576,6 +578,8 @@ def main() -> int:
         print(f"bench.py: this build measures one GPU only (--gpus {args.gpus} requested); "
               "the layer's multi-GPU sharding is a design, not a measured path.", file=sys.stderr)
         return 2
+    if args.layer_kernel:
+        os.environ["APMOE_LAYER_KERNEL"] = "1"  # read when the contexts are created
 
     import torch
 

@@ -121,6 +121,15 @@ int32_t apmoe_version(void);
 apmoe_status apmoe_create(apmoe_ctx **out, int device);
 apmoe_status apmoe_destroy(apmoe_ctx *ctx);
 
+/* Sticky fault flags of the context's fused launches, 0 when none was raised.
+ * APMOE_FAULT_LAYER_WAIT: a work item of the one-launch decode layer (apmoe_moe_forward)
+ * gave up waiting for the gate_up blocks of its expert after about a second -- a broken
+ * completion count, which the design rules out; the bound only keeps such a bug from
+ * hanging the GPU, and that launch's output is then not to be trusted.  The flag stays
+ * set for the context's life.  Synchronises the device (a diagnostic, not for hot loops). */
+#define APMOE_FAULT_LAYER_WAIT 1
+apmoe_status apmoe_ctx_faults(apmoe_ctx *ctx, int32_t *flags);
+
 /*
  * Eq. 3 (Section 3.1): M_i^b, the GPU bytes of an n x k block at b bits,
  * n * b * k / 8 plane bytes plus n * 2^b * 2 LUT bytes.  The memory released by
@@ -382,7 +391,12 @@ apmoe_status apmoe_moe_workspace(const apmoe_table *tbl, int32_t layer, int32_t 
  * down product's epilogue -- the workgroup that finishes a token's last contribution
  * to a 64-column block sums it, with the arithmetic of apmoe_combine -- so the
  * small-batch layer is three launches (with the one-launch route); the same bits as
- * the four steps.  The completion counters of these fused launches belong to the
+ * the four steps.  A context created with APMOE_LAYER_KERNEL=1 runs gate_up and down
+ * of such a batch as one launch, on layers of at most 16 experts whose gate_up has
+ * more than 1024 and down at most 1024 64-row blocks in all (the Mixtral shapes): its
+ * workgroups take the gate_up blocks first and start an expert's down blocks once its
+ * gate_up blocks are stored (the same bits; measured slower than the two launches, so
+ * not the default).  The completion counters of these fused launches belong to the
  * context: calls on one context that may run at the same time must be ordered by the
  * caller.  APMOE_UNFUSED=1 at apmoe_create: every step in its own launches.
  * The table's experts of the layer are the routed ones (w_router rows) followed by

@@ -169,3 +169,73 @@ def test_two_contexts_on_two_streams():
             np.testing.assert_array_equal(host(out).view(np.uint16), ref.view(np.uint16), err_msg=f"T={T}")
     finally:
         c2.close()
+
+
+
+def _env_ctx(var: str) -> apw.Context:
+    old = os.environ.get(var)
+    os.environ[var] = "1"
+    try:
+        return apw.Context(0)
+    finally:
+        if old is None:
+            del os.environ[var]
+        else:
+            os.environ[var] = old
+
+
+_ONE = None
+
+
+def layer_kernel_ctx() -> apw.Context:
+    """A context that runs a small batch's gate_up and down in one launch."""
+    global _ONE
+    if _ONE is None:
+        _ONE = _env_ctx("APMOE_LAYER_KERNEL")
+    return _ONE
+
+
+def test_layer_kernel_matches_two_launches():
+    """The one-launch decode layer (gate_up and down in one launch, the down blocks of an
+    expert started once its gate_up blocks are stored) against gate_up and down as two
+    launches: identical bits call after call (the launch leaves its counters at zero),
+    with one and two tokens (experts without rows), and no fault flag."""
+    name = "mixtral8x7b_decode_t16"
+    L = _layer(name)
+    for T in [32, 16, 1, 2, 32, 9, 31, 17, 16]:
+        ref = _forward(ctx(), L, T)
+        got = _forward(layer_kernel_ctx(), L, T)
+        assert not np.isnan(got.astype(np.float32)).any(), f"T={T}: an output left unwritten"
+        np.testing.assert_array_equal(got.view(np.uint16), ref.view(np.uint16), err_msg=f"{name} T={T}")
+    assert layer_kernel_ctx().faults() == 0
+
+
+def test_layer_kernel_two_contexts_on_two_streams():
+    """Two one-launch layers at once on two streams (each context its own work list and
+    counters; each launch gets only part of the GPU, so its down blocks wait for gate_up
+    blocks that start late): the bits of the separate launches, no fault flag."""
+    L = _layer("mixtral8x7b_decode_t16")
+    cfg = L.cfg
+    Ts = [32, 32, 16, 32, 24, 1]
+    refs = [_forward(ctx(), L, T) for T in Ts]
+    c2 = _env_ctx("APMOE_LAYER_KERNEL")
+    try:
+        s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+        jobs = []
+        for T in Ts:
+            x_d = dev(synth.gen_x(cfg, 0, T))
+            nbytes = apw.moe_workspace(L.rw.table, L.layer, T, cfg.topk, cfg.shared)
+            ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device="cuda")
+            out = torch.full((T, cfg.hidden), float("nan"), dtype=torch.float16, device="cuda")
+            jobs.append((T, x_d, ws, out))
+        torch.cuda.synchronize()  # inputs ready before either stream starts
+        for i, (T, x_d, ws, out) in enumerate(jobs):
+            c, s = (layer_kernel_ctx(), s1) if i % 2 == 0 else (c2, s2)
+            apw.moe_forward(c, L.rw.table, L.layer, x_d, L.wr_d, L.bias_d, T, cfg.topk, cfg.renormalize, ws,
+                            ws.numel(), out, s, n_shared=cfg.shared)
+        torch.cuda.synchronize()
+        for (T, _, _, out), ref in zip(jobs, refs):
+            np.testing.assert_array_equal(host(out).view(np.uint16), ref.view(np.uint16), err_msg=f"T={T}")
+        assert layer_kernel_ctx().faults() == 0 and c2.faults() == 0
+    finally:
+        c2.close()
