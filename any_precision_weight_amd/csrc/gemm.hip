@@ -1146,7 +1146,7 @@ void launch_kind(const GemmParams &P, hipStream_t s)
 
 }  // namespace
 
-static hipError_t launch_mid(const GemmParams &P, int max_q, int act, int N, int E, hipStream_t s);
+static hipError_t launch_mid(const GemmParams &P, int max_q, int act, int N, int E, bool beside, hipStream_t s);
 
 static GemmParams gemm_params(const DevBlock *table, int kind, int E, int N, int K, const uint8_t *order,
                               const uint16_t *in, size_t in_bytes, int gather, const int32_t *perm,
@@ -1269,7 +1269,7 @@ hipError_t launch_gemm(const DevBlock *table, int kind, int E, int N, int K, int
         wide ? launch_kind<APMOE_DOWN, 4>(P, s) : launch_kind<APMOE_DOWN, 2>(P, s);
     err = hipGetLastError();
     if (err == hipSuccess && tokens > P.max_rows)
-        err = launch_mid(P, max_q, act, N, E, s);
+        err = launch_mid(P, max_q, act, N, E, beside, s);
     if (err != hipSuccess || !tile)
         return err;
     if (beside)
@@ -1278,7 +1278,7 @@ hipError_t launch_gemm(const DevBlock *table, int kind, int E, int N, int K, int
 }
 
 // The mid product's launch(es) for the experts with kDecodeMaxRows + 1 .. kMidMaxRows rows.
-static hipError_t launch_mid(const GemmParams &P, int max_q, int act, int N, int E, hipStream_t s)
+static hipError_t launch_mid(const GemmParams &P, int max_q, int act, int N, int E, bool beside, hipStream_t s)
 {
     hipError_t err = hipSuccess;
     const int kind = P.kind;
@@ -1287,11 +1287,14 @@ static hipError_t launch_mid(const GemmParams &P, int max_q, int act, int N, int
     M.row_blocks = act ? (N / 2) / 64 : (N + kMidRows - 1) / kMidRows;
     const dim3 mgrid(kXcds * E * ((M.row_blocks + kXcds - 1) / kXcds));
     // Two workgroups per CU pay where an expert alone has many row blocks (the 8x22B
-    // gate_up: 256); with few (its down: 48) they measured slower than one.  The q = 8
-    // launch always follows: q is read from the device table when the kernels run, and
-    // its workgroups exit at once when no expert of 33..64 rows is at q = 8.
+    // gate_up: 256), and where a tile launch beside this one holds part of the CUs (the
+    // 8x22B down: 48 row blocks per expert on the CUs the tile launch leaves, one round
+    // instead of two); with few row blocks on the whole GPU they measured slower than
+    // one.  The q = 8 launch always follows: q is read from the device table when the
+    // kernels run, and its workgroups exit at once when no expert of 33..64 rows is at
+    // q = 8.
     (void)max_q;
-    if (M.row_blocks >= 128) {
+    if (M.row_blocks >= 128 || beside) {
         if (kind == APMOE_GATE_UP)
             hipLaunchKernelGGL((gemm_mid_kernel<APMOE_GATE_UP, kMidLow>), mgrid, dim3(kMidThreads), 0, s, M);
         else
