@@ -57,7 +57,8 @@ struct apmoe_ctx {
     // Completion counters of the fused launches, zero between calls (each launch sets
     // the ones it counted on back to zero): [0] the route, [16, 16 + kLsWords) the
     // one-launch decode layer's work list, then kCombineCounters for the output
-    // accumulation fused into the down product.
+    // accumulation fused into the down product, then the one-launch layer's 16
+    // per-expert counts.
     int32_t *sync = nullptr;
     bool fuse = true;  // APMOE_UNFUSED=1 at apmoe_create: every layer step in its own launches
     // APMOE_LAYER_KERNEL=1 at apmoe_create: gate_up and down of a small batch in one
@@ -70,7 +71,10 @@ static constexpr int kLayerSync = 16;
 static_assert(kLayerSync + apmoe::kLsWords <= 64, "layer counters below the combine counters");
 static constexpr int kCombineCounter0 = 64;
 static constexpr int kCombineCounters = 32 * 1024;  // tokens x 64-column blocks of one fused down call
-static constexpr size_t kSyncBytes = (size_t)(kCombineCounter0 + kCombineCounters) * sizeof(int32_t);
+// the one-launch layer's per-expert counts, 4 KB apart, after the combine counters
+static constexpr int kLayerDone = (kCombineCounter0 + kCombineCounters + 1023) / 1024 * 1024;
+static constexpr size_t kSyncBytes =
+    (size_t)(kLayerDone + 16 * apmoe::kLsDoneStride) * sizeof(int32_t);
 // Largest assignment count (T * (topk + n_shared)) routed in one fused launch: the last
 // workgroup groups them with 256 threads, one chunk.  (At 512 assignments, two chunks,
 // the fused launch took 21.6 us against 17.7 us for the two launches; at 64, 13.5
@@ -1052,7 +1056,8 @@ apmoe_status apmoe_moe_forward(apmoe_ctx *ctx, const apmoe_table *tbl, int32_t l
     if (fuse_comb && ctx->layer_kernel && apmoe::layer_launch_fits(tbl->E, H, F, T)) {
         const DevBlock *slice = tbl->d_table + tbl->index(layer, 0, 0);
         hipError_t e = apmoe::launch_layer(slice, tbl->E, H, F, x, perm, offsets, kt, T, a, y, comb,
-                                           ctx->sync + kLayerSync, reinterpret_cast<hipStream_t>(stream));
+                                           ctx->sync + kLayerSync, ctx->sync + kLayerDone,
+                                           reinterpret_cast<hipStream_t>(stream));
         return e == hipSuccess ? ok() : hip_fail(e, "layer launch");
     }
     // gate_up with SiLU(gate) * up in its epilogue (F = K of down is a multiple of 128)

@@ -96,6 +96,7 @@ struct LayerParams {
     // [APMOE_DOWN]: down with the output accumulation fused (comb.out set), in = a
     GemmParams p[2];
     int32_t *sync;
+    int32_t *done;  // per expert the gate_up pairs done, kLsDoneStride words apart
     int items_gu, items_dn;
 };
 
@@ -1060,7 +1061,7 @@ static_assert(kDecodeLut == kSmallLut || kDecodeLut == kLargeLut, "LUT region");
 template <int TOKL>
 constexpr int kLayerLds = max_i(2 * kDecodeLut + max_i(2 * kRedBytesOf<2>, 2 * 2 * TOKL * kXRowBytes),
                                 kLdsBytes<TOKL, 4, kDecodeLut>);
-constexpr int kLayerSpin = 1 << 24;  // s_sleep rounds before a wait gives up (about a second)
+constexpr int kLayerSpin = 1 << 21;  // polls before a wait gives up (about a second)
 
 template <int TOKL>
 __global__ void __launch_bounds__(kThreadsOf<4>) __attribute__((amdgpu_waves_per_eu(4)))
@@ -1104,12 +1105,18 @@ layer_kernel(LayerParams L)
             __builtin_amdgcn_s_waitcnt(wait_vm<0>());  // this wave's rows of a are stored (device-coherent)
             __syncthreads();
             if (threadIdx.x == 0)
-                __hip_atomic_fetch_add(L.sync + kLsDone + e, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_fetch_add(L.done + kLsDoneStride * e, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         } else {
             if (threadIdx.x == 0) {
-                int n = 0;
-                while (__hip_atomic_load(L.sync + kLsDone + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < pairs) {
-                    __builtin_amdgcn_s_sleep(2);
+                // many down workgroups may wait at once: polls back off to one per ~2 k clk,
+                // and each expert's count sits on its own 4 KB, so they do not crowd the
+                // memory requests of the gate_up workgroups still running
+                int n = 0, nap = 1;
+                while (__hip_atomic_load(L.done + kLsDoneStride * e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
+                       pairs) {
+                    for (int i = 0; i < nap; ++i)
+                        __builtin_amdgcn_s_sleep(8);
+                    nap = nap < 4 ? 2 * nap : 4;
                     if (++n >= kLayerSpin) {
                         __hip_atomic_store(L.sync + kLsFault, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                         break;
@@ -1125,7 +1132,7 @@ layer_kernel(LayerParams L)
         const int old = __hip_atomic_fetch_add(L.sync + kLsExit, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (old == (int)gridDim.x - 1) {  // every other workgroup is done
             for (int u = 0; u < L.p[APMOE_GATE_UP].E; ++u)
-                __hip_atomic_store(L.sync + kLsDone + u, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(L.done + kLsDoneStride * u, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(L.sync + kLsNext, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(L.sync + kLsExit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
@@ -1193,7 +1200,7 @@ bool layer_launch_fits(int E, int H, int F, int T)
 
 hipError_t launch_layer(const DevBlock *table, int E, int H, int F, const uint16_t *x, const int32_t *perm,
                         const int32_t *offsets, int topk, int T, uint16_t *a, float *y, const CombineArgs &comb,
-                        int32_t *sync, hipStream_t s)
+                        int32_t *sync, int32_t *done, hipStream_t s)
 {
     if (!layer_launch_fits(E, H, F, T) || !comb.out)
         return hipErrorInvalidValue;
@@ -1205,6 +1212,7 @@ hipError_t launch_layer(const DevBlock *table, int E, int H, int F, const uint16
     dn = gemm_params(table, APMOE_DOWN, E, H, F, nullptr, a, (size_t)R * F * 2, 0, perm, offsets, topk, y, 1, 0, &comb);
     gu.tokl = dn.tokl = decode_tokl(T, E);
     L.sync = sync;
+    L.done = done;
     L.items_gu = E * (gu.row_blocks / 2);
     L.items_dn = E * dn.row_blocks;
     const int grid = L.items_gu + L.items_dn;  // one item per workgroup, in the order they start

@@ -91,14 +91,15 @@ hipError_t launch_gemm(const DevBlock *table, int kind, int E, int N, int K, int
 // kDecodeMaxRows tokens over at most 16 experts whose separate launches would take two
 // column parts for gate_up and four for down (the same bits).  Its counters, at `sync`
 // (int32, zero before the first launch; every launch leaves them zero except the fault
-// flag): the next work item, the workgroups that have finished, a sticky flag set when a
-// wait gave up (a broken count; never expected), and per expert the gate_up pairs done.
-constexpr int kLsNext = 0, kLsExit = 1, kLsFault = 2, kLsDone = 8;
-constexpr int kLsWords = kLsDone + 16;
+// flag): the next work item, the workgroups that have finished, and a sticky flag set
+// when a wait gave up (a broken count; never expected); at `done`, per expert the
+// gate_up pairs done, kLsDoneStride words (4 KB) apart, zero between launches.
+constexpr int kLsNext = 0, kLsExit = 1, kLsFault = 2, kLsWords = 4;
+constexpr int kLsDoneStride = 1024;
 bool layer_launch_fits(int E, int H, int F, int T);
 hipError_t launch_layer(const DevBlock *table, int E, int H, int F, const uint16_t *x, const int32_t *perm,
                         const int32_t *offsets, int topk, int T, uint16_t *a, float *y, const CombineArgs &comb,
-                        int32_t *sync, hipStream_t s);
+                        int32_t *sync, int32_t *done, hipStream_t s);
 hipError_t launch_gemm_tile(const DevBlock *table, int kind, int E, int N, int K, const uint16_t *in, size_t in_bytes,
                             int gather, const int32_t *perm, const int32_t *offsets, int topk, void *out, int out_f32,
                             int act, int R, hipStream_t s);

@@ -114,7 +114,7 @@ int32_t apmoe_version(void);
 
 /* Bind a context to HIP device `device`.  Fails with APMOE_UNSUPPORTED on a
  * device that is not gfx950.  The context owns one stream of its own (default
- * priority), two events and about 128 KB of device memory for the completion counters of
+ * priority), two events and about 200 KB of device memory for the completion counters of
  * the fused launches (zeroed here, on `device`), released by apmoe_destroy;
  * APMOE_HIP_ERROR if they cannot be created.  APMOE_UNFUSED=1 in the environment at
  * this call gives a context whose layer steps always run as separate launches. */
