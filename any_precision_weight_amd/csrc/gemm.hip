@@ -1298,13 +1298,14 @@ hipError_t launch_gemm(const DevBlock *table, int kind, int E, int N, int K, int
     // Few workgroups (the down product's N / 64 row blocks) leave two per CU: four
     // column parts then give each CU four waves per SIMD instead of two.
     const bool wide = decode_wide(P.row_blocks, E);
-    // gate_up of 17..32 tokens (16-row token buffers): two 64-row blocks per 8-wave
+    // gate_up with 16-row token buffers (above 16 tokens): two 64-row blocks per 8-wave
     // workgroup sharing the token buffers -- four waves per SIMD instead of three and
     // half the token copies per weight, which pays more than the halves' lockstep costs
-    // (32-layer step, map A -1.0%, map B -1.3%); with 8-row buffers (up to 16 tokens,
-    // already four waves per SIMD) it measured 8% slower
-    const bool pairs = kind == APMOE_GATE_UP && act && !wide && P.tokl == 16 && tokens <= kDecodeMaxRows &&
-                       P.row_blocks % 2 == 0 && E <= kLptExperts;
+    // (32-layer step, map A -1.0%, map B -1.3%; the 8x22B layer's decode experts
+    // -1.8% of its gate_up); with 8-row buffers (up to 16 tokens, already four waves
+    // per SIMD) it measured 8% slower
+    const bool pairs = kind == APMOE_GATE_UP && act && !wide && P.tokl == 16 && P.row_blocks % 2 == 0 &&
+                       E <= kLptExperts;
     if (pairs) {
         GemmParams Q = P;
         Q.row_blocks = P.row_blocks / 2;
